@@ -1,0 +1,268 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU reference for the FP8 block-scaled GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the library path may call, link or load this file;
+ * only the test suite, the smoke check and the CPU-baseline leg of the benchmark use it.
+ * It shares no code, header, table or constant with the HIP implementation.
+ *
+ * Sources (cited by page title and section):
+ *   [P1] "DeepSeek開源第三彈：V3/R1訓練推理關鍵秘籍，核心代碼僅300行"
+ *        - section 深入了解DeepGEMM: FP8 GEMM with fine-grained scaling (a design taken from
+ *          DeepSeek V3); FP8 tensor-core accumulation is imprecise, so partial results are
+ *          promoted and accumulated a second time at higher precision (two-level accumulation).
+ *        - section 如何使用？: the three entry points gemm_fp8_fp8_bf16_nt (NT: left operand not
+ *          transposed, right operand transposed), m_grouped_gemm_fp8_fp8_bf16_nt_contiguous and
+ *          m_grouped_gemm_fp8_fp8_bf16_nt_masked; FP8 inputs, BF16 output.
+ *   [P3] "DeepGEMM：AI計算の経済性を変えるオープンソースライブラリ"
+ *        - section DeepGEMMが重要な理由, item 4: contiguous grouped GEMM (token sequences grouped
+ *          per expert) and masked grouped GEMM (sparse expert activation).
+ *
+ * The pages say "fine-grained scaling" only.  The reading taken here (listed with every other
+ * reading in the design notes): A carries one fp32 scale per 1x128 block of a row (sa[M][K/128]),
+ * B one fp32 scale per 128x128 block (sb[ceil(N/128)][K/128]); FP8 is OCP E4M3 (e4m3fn).
+ *
+ * What is computed is the plain definition of the dequantised product, rounded once:
+ *
+ *   D[m][n] = bf16_rne( sum_kb  sa[m][kb] * sb[n/128][kb] * sum_{k in block kb} e4m3(A[m][k]) * e4m3(B[n][k]) )
+ *
+ * The inner block sum is exact in fp64 in any order: every e4m3 value is an integer multiple of
+ * 2^-9 of magnitude below 2^18 * 2^-9, so each product is a multiple of 2^-18 below 2^36 * 2^-18
+ * and 128 of them stay below 2^43 * 2^-18, inside fp64's 53-bit significand.  The scale product
+ * sa*sb of two fp32 values is exact in fp64 (48-bit significand).  The sum over K-blocks is done
+ * with fp64 fused multiply-add, then rounded once, fp64 -> bf16, round to nearest even.
+ *
+ * Parity pins (tests/test_oracle_pins.py): e4m3 decode against the OCP table anchors and an
+ * independent library decoder; bf16 rounding against exact rational rounding; whole products
+ * against exact rational brute force on tiny shapes, integer closed forms, power-of-two scale
+ * closed forms, a library fp64 matmul of the dequantised operands, and the grouping/permutation/
+ * padding invariants.  No function below is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_API __attribute__((visibility("default")))
+
+/* ---- element formats --------------------------------------------------------------------- */
+
+/* OCP 8-bit floating point, E4M3 ("e4m3fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits.
+ * Exponent field 0 is subnormal (f * 2^-9); S.1111.111 is NaN; there is no infinity, so the
+ * largest finite value is S.1111.110 = 1.75 * 2^8 = 448. */
+ORACLE_API double oracle_e4m3_value(uint8_t code) {
+    int sign = code >> 7;
+    int e = (code >> 3) & 0xF;
+    int f = code & 0x7;
+    double v;
+    if (e == 0xF && f == 0x7) return NAN;
+    if (e == 0)
+        v = ldexp((double)f, -9);                 /* f/8 * 2^(1-7) */
+    else
+        v = ldexp(1.0 + (double)f / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* Round an fp64 value to bfloat16 (1 sign, 8 exponent bits with bias 127, 7 stored mantissa
+ * bits), round to nearest, ties to even, in a single step.  Result: the 16-bit pattern. */
+ORACLE_API uint16_t oracle_bf16_bits(double x) {
+    if (isnan(x)) return 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double ax = fabs(x);
+    if (ax == 0.0) return sign;
+    int e2;
+    frexp(ax, &e2);                       /* ax in [2^(e2-1), 2^e2) */
+    int unit_exp = e2 - 1 - 7;            /* weight of the last kept bit for a normal bf16 */
+    if (e2 - 1 < -126) unit_exp = -126 - 7; /* subnormal range: fixed quantum 2^-133 */
+    double q = ldexp(nearbyint(ldexp(ax, -unit_exp)), unit_exp); /* default mode is RNE */
+    if (q >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80);  /* overflow -> inf */
+    float qf = (float)q;                  /* exact: q has <= 8 significant bits in range */
+    uint32_t bits;
+    memcpy(&bits, &qf, sizeof bits);
+    return (uint16_t)(sign | (uint16_t)((bits >> 16) & 0x7FFF));
+}
+
+/* ---- one output element ------------------------------------------------------------------ */
+
+/* Two-level sum for one output: per 128-wide K block an exact fp64 dot product of the decoded
+ * codes, then scaled by sa*sb and accumulated across blocks (fp64 fused multiply-add).
+ * a_row/b_row: K codes each; sa_row/sb_row: ceil(K/128) scales each. */
+static double element(const double* a_row, const float* sa_row, const double* b_row,
+                      const float* sb_row, int64_t K) {
+    int64_t nkb = (K + 127) / 128;
+    double acc = 0.0;
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+        int64_t k0 = kb * 128, k1 = k0 + 128 < K ? k0 + 128 : K;
+        double block = 0.0;
+        for (int64_t k = k0; k < k1; ++k) block += a_row[k] * b_row[k];
+        double s = (double)sa_row[kb] * (double)sb_row[kb];
+        acc = fma(s, block, acc);
+    }
+    return acc;
+}
+
+static void decode_rows(const uint8_t* codes, int64_t rows, int64_t K, double* out) {
+    double table[256];
+    for (int c = 0; c < 256; ++c) table[c] = oracle_e4m3_value((uint8_t)c);
+    for (int64_t i = 0; i < rows * K; ++i) out[i] = table[codes[i]];
+}
+
+static int pick_threads(int nthreads) {
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+ORACLE_API int oracle_num_threads(int nthreads) { return pick_threads(nthreads); }
+
+/* ---- dense NT ---------------------------------------------------------------------------- */
+
+/* D[M][N] (bf16 bits) = A[M][K] . B[N][K]^T with sa[M][ceil(K/128)], sb[ceil(N/128)][ceil(K/128)].
+ * acc (optional, may be NULL): the fp64 value before the final rounding.  Returns 0, or -1 when
+ * out of memory. */
+ORACLE_API int oracle_gemm_nt(const uint8_t* A, const float* sa, const uint8_t* B, const float* sb,
+                              int64_t M, int64_t N, int64_t K, uint16_t* D, double* acc,
+                              int nthreads) {
+    int64_t nkb = (K + 127) / 128;
+    double* Ad = (double*)malloc(sizeof(double) * (size_t)(M * K + 1));
+    double* Bd = (double*)malloc(sizeof(double) * (size_t)(N * K + 1));
+    if (!Ad || !Bd) { free(Ad); free(Bd); return -1; }
+    decode_rows(A, M, K, Ad);
+    decode_rows(B, N, K, Bd);
+    int nt = pick_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double v = element(Ad + m * K, sa + m * nkb, Bd + n * K, sb + (n / 128) * nkb, K);
+            D[m * N + n] = oracle_bf16_bits(v);
+            if (acc) acc[m * N + n] = v;
+        }
+    }
+    free(Ad);
+    free(Bd);
+    return 0;
+}
+
+/* ---- M-grouped, contiguous layout --------------------------------------------------------- */
+
+/* Rows of all groups are concatenated along M.  Row r belongs to group g = m_indices[r] and is
+ * multiplied by B[g] (B is [G][N][K], sb is [G][ceil(N/128)][ceil(K/128)]).  m_indices[r] == -1
+ * marks a padding row: it has no defined output (valid[r] = 0, its D row is set to 0).  An index
+ * outside [-1, G) is treated as padding too. */
+ORACLE_API int oracle_grouped_contiguous(const uint8_t* A, const float* sa, const uint8_t* B,
+                                         const float* sb, const int32_t* m_indices, int64_t M,
+                                         int64_t N, int64_t K, int32_t G, uint16_t* D,
+                                         uint8_t* valid, double* acc, int nthreads) {
+    int64_t nkb = (K + 127) / 128, nnb = (N + 127) / 128;
+    double* Ad = (double*)malloc(sizeof(double) * (size_t)(M * K + 1));
+    double* Bd = (double*)malloc(sizeof(double) * (size_t)((int64_t)G * N * K + 1));
+    if (!Ad || !Bd) { free(Ad); free(Bd); return -1; }
+    decode_rows(A, M, K, Ad);
+    decode_rows(B, (int64_t)G * N, K, Bd);
+    int nt = pick_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t r = 0; r < M; ++r) {
+        int32_t g = m_indices[r];
+        int ok = g >= 0 && g < G;
+        if (valid) valid[r] = (uint8_t)ok;
+        for (int64_t n = 0; n < N; ++n) {
+            double v = 0.0;
+            if (ok)
+                v = element(Ad + r * K, sa + r * nkb, Bd + ((int64_t)g * N + n) * K,
+                            sb + ((int64_t)g * nnb + n / 128) * nkb, K);
+            D[r * N + n] = ok ? oracle_bf16_bits(v) : 0;
+            if (acc) acc[r * N + n] = v;
+        }
+    }
+    free(Ad);
+    free(Bd);
+    return 0;
+}
+
+/* ---- M-grouped, masked layout ------------------------------------------------------------- */
+
+/* Group g owns a fixed block of M_max rows: A[g][M_max][K], sa[g][M_max][ceil(K/128)],
+ * D[g][M_max][N].  Only rows r < min(masked_m[g], M_max) are valid; the others have no defined
+ * output (valid = 0, D set to 0).  A negative masked_m counts as 0. */
+ORACLE_API int oracle_grouped_masked(const uint8_t* A, const float* sa, const uint8_t* B,
+                                     const float* sb, const int32_t* masked_m, int32_t G,
+                                     int64_t M_max, int64_t N, int64_t K, uint16_t* D,
+                                     uint8_t* valid, double* acc, int nthreads) {
+    int64_t nkb = (K + 127) / 128, nnb = (N + 127) / 128;
+    int64_t rows = (int64_t)G * M_max;
+    double* Ad = (double*)malloc(sizeof(double) * (size_t)(rows * K + 1));
+    double* Bd = (double*)malloc(sizeof(double) * (size_t)((int64_t)G * N * K + 1));
+    if (!Ad || !Bd) { free(Ad); free(Bd); return -1; }
+    decode_rows(A, rows, K, Ad);
+    decode_rows(B, (int64_t)G * N, K, Bd);
+    int nt = pick_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t gr = 0; gr < rows; ++gr) {
+        int64_t g = gr / (M_max > 0 ? M_max : 1), r = gr % (M_max > 0 ? M_max : 1);
+        int64_t count = masked_m[g] < 0 ? 0 : (masked_m[g] > M_max ? M_max : masked_m[g]);
+        int ok = r < count;
+        if (valid) valid[gr] = (uint8_t)ok;
+        for (int64_t n = 0; n < N; ++n) {
+            double v = 0.0;
+            if (ok)
+                v = element(Ad + gr * K, sa + gr * nkb, Bd + (g * N + n) * K,
+                            sb + (g * nnb + n / 128) * nkb, K);
+            D[gr * N + n] = ok ? oracle_bf16_bits(v) : 0;
+            if (acc) acc[gr * N + n] = v;
+        }
+    }
+    free(Ad);
+    free(Bd);
+    return 0;
+}
+
+/* ---- selected elements ------------------------------------------------------------------- */
+
+/* The same element computation for `count` chosen outputs, for full-size problems where the
+ * whole product is too slow on a CPU.  For sample i: the A row is a_rows[i] (row of A and of sa,
+ * flattened over groups), the B row is b_rows[i] (row of B flattened over groups, i.e.
+ * g*N + n) and the B scale row is sb_rows[i] (g*ceil(N/128) + n/128).  Out: bf16 bits and the
+ * fp64 value (optional). */
+ORACLE_API int oracle_elements(const uint8_t* A, const float* sa, const uint8_t* B,
+                               const float* sb, int64_t K, const int64_t* a_rows,
+                               const int64_t* b_rows, const int64_t* sb_rows, int64_t count,
+                               uint16_t* out, double* acc, int nthreads) {
+    int64_t nkb = (K + 127) / 128;
+    int nt = pick_threads(nthreads);
+    (void)nt;
+    double table[256];
+    for (int c = 0; c < 256; ++c) table[c] = oracle_e4m3_value((uint8_t)c);
+    int failed = 0;
+#pragma omp parallel num_threads(nt)
+    {
+        double* a = (double*)malloc(sizeof(double) * (size_t)(K + 1));
+        double* b = (double*)malloc(sizeof(double) * (size_t)(K + 1));
+        int mine_ok = a && b;
+        if (!mine_ok) {
+#pragma omp atomic write
+            failed = 1;
+        }
+        /* every thread reaches the work-sharing loop; one without buffers does nothing */
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t i = 0; i < count; ++i) {
+            if (!mine_ok) continue;
+            const uint8_t* ar = A + a_rows[i] * K;
+            const uint8_t* br = B + b_rows[i] * K;
+            for (int64_t k = 0; k < K; ++k) { a[k] = table[ar[k]]; b[k] = table[br[k]]; }
+            double v = element(a, sa + a_rows[i] * nkb, b, sb + sb_rows[i] * nkb, K);
+            out[i] = oracle_bf16_bits(v);
+            if (acc) acc[i] = v;
+        }
+        free(a);
+        free(b);
+    }
+    return failed ? -1 : 0;
+}

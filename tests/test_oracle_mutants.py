@@ -1,0 +1,38 @@
+"""Sensitivity of the oracle's pins: each case plants one plausible mistake in a temporary copy of
+oracle.c (on the CPU), builds it, and runs the pin suite against it, which must fail."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "decode_sign_dropped": ("return sign ? -v : v;", "return v;"),
+    "subnormal_quantum": ("v = ldexp((double)f, -9);", "v = ldexp((double)f, -10);"),
+    "rounding_truncates": ("nearbyint(ldexp(ax, -unit_exp))", "trunc(ldexp(ax, -unit_exp))"),
+    "bf16_no_subnormal_range": ("if (e2 - 1 < -126) unit_exp = -126 - 7;", ""),
+    "block_sum_drops_last_term": ("k1 = k0 + 128 < K ? k0 + 128 : K;", "k1 = (k0 + 128 < K ? k0 + 128 : K) - 1;"),
+    "sa_index_fixed_block": ("double s = (double)sa_row[kb] * (double)sb_row[kb];",
+                             "double s = (double)sa_row[0] * (double)sb_row[kb];"),
+    "sb_block_from_k_not_n": ("sb + (n / 128) * nkb, K);", "sb + 0 * nkb, K);"),
+    "fp32_accumulation": ("acc = fma(s, block, acc);", "acc = (float)(acc + (float)(s * block));"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    assert src.count(old) >= 1, name
+    mutated = src.replace(old, new)
+    c = tmp_path / "oracle_mutant.c"
+    so = tmp_path / "liboracle_mutant.so"
+    c.write_text(mutated)
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", str(so), str(c), "-lm"])
+    env = dict(os.environ, ORACLE_LIB_OVERRIDE=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "planted mistake %s was not caught:\n%s" % (name, r.stdout[-2000:])
