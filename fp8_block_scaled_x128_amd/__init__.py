@@ -1,0 +1,225 @@
+"""MI355X (gfx950) FP8 GEMM with fine-grained block scaling: Python binding of libfp8gemm.so.
+
+Argument marshalling only -- every step of the computation runs in the HIP kernels behind the
+C ABI declared in include/fp8gemm.h.  torch supplies device memory and the current stream.
+
+    D = gemm_nt(A, sa, B, sb)                              # dense NT, bf16 out
+    D = grouped_contiguous(A, sa, B, sb, m_indices)        # MoE, groups concatenated along M
+    D = grouped_masked(A, sa, B, sb, masked_m, expected_m) # MoE, fixed per-group capacity
+
+A and B are E4M3 codes (torch.float8_e4m3fn or uint8), sa one fp32 scale per 1x128 block of a
+row of A, sb one per 128x128 block of B (page "DeepSeek開源第三彈：V3/R1訓練推理關鍵秘籍，核心代碼僅
+300行", sections 深入了解DeepGEMM and 如何使用？).  There is no CPU fallback: without the built
+library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["gemm_nt", "grouped_contiguous", "grouped_masked", "init", "set_num_cus",
+           "last_config", "read_device_error", "status_string", "lib", "library_path",
+           "Fp8GemmError", "STATUS", "DEVERR_BAD_INDEX", "DEVERR_BAD_COUNT"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfp8gemm.so")
+_lib = None
+
+STATUS = {0: "FP8GEMM_OK", 1: "FP8GEMM_ERR_NULL_PTR", 2: "FP8GEMM_ERR_BAD_SHAPE",
+          3: "FP8GEMM_ERR_MISALIGNED", 4: "FP8GEMM_ERR_UNSUPPORTED", 5: "FP8GEMM_ERR_LAUNCH",
+          6: "FP8GEMM_ERR_HIP"}
+DEVERR_BAD_INDEX = 1
+DEVERR_BAD_COUNT = 2
+
+#: exported C symbols and their ctypes signatures (restype, argtypes)
+_P, _I64, _I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+SIGNATURES = {
+    "fp8gemm_nt": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "fp8gemm_grouped_contiguous": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P]),
+    "fp8gemm_grouped_masked": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _P]),
+    "fp8gemm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fp8gemm_init": (ctypes.c_int, []),
+    "fp8gemm_set_num_cus": (ctypes.c_int, [ctypes.c_int]),
+    "fp8gemm_last_config": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_int]),
+    "fp8gemm_read_device_error": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32)]),
+}
+
+
+class Fp8GemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, status_string(status), STATUS.get(status, status)))
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libfp8gemm.so is not built (python -m fp8_block_scaled_x128_amd.build)")
+        l = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fp8gemm_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise Fp8GemmError(status, where)
+
+
+def init() -> None:
+    _check(lib().fp8gemm_init(), "fp8gemm_init")
+
+
+def set_num_cus(n: int) -> None:
+    _check(lib().fp8gemm_set_num_cus(int(n)), "fp8gemm_set_num_cus")
+
+
+def last_config() -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().fp8gemm_last_config(buf, 256), "fp8gemm_last_config")
+    return buf.value.decode()
+
+
+# ---- tensor front end -------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def read_device_error(stream=None) -> int:
+    """Synchronise the stream and return (and clear) the device error word."""
+    torch = _torch()
+    dev = torch.cuda.current_device()
+    v = ctypes.c_int32(0)
+    _check(lib().fp8gemm_read_device_error(_stream(stream, dev), ctypes.byref(v)),
+           "fp8gemm_read_device_error")
+    return v.value
+
+
+def _codes(t, name):
+    torch = _torch()
+    if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise TypeError("%s must be float8_e4m3fn or uint8 codes, got %s" % (name, t.dtype))
+    return _dev_contig(t, name)
+
+
+def _dev_contig(t, name):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _f32(t, name):
+    torch = _torch()
+    if t.dtype != torch.float32:
+        raise TypeError("%s must be float32, got %s" % (name, t.dtype))
+    return _dev_contig(t, name)
+
+
+def _i32(t, name):
+    torch = _torch()
+    if t.dtype != torch.int32:
+        raise TypeError("%s must be int32, got %s" % (name, t.dtype))
+    return _dev_contig(t, name)
+
+
+def _out(out, shape, device):
+    torch = _torch()
+    if out is None:
+        return torch.empty(shape, dtype=torch.bfloat16, device=device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(shape):
+        raise ValueError("out must be bfloat16 of shape %s" % (tuple(shape),))
+    return _dev_contig(out, "out")
+
+
+def _shape_check(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def gemm_nt(A, sa, B, sb, out=None, stream=None):
+    """D[M,N] (bf16) = A[M,K] . B[N,K]^T with sa [M, K/128] and sb [ceil(N/128), K/128]."""
+    torch = _torch()
+    A, B = _codes(A, "A"), _codes(B, "B")
+    sa, sb = _f32(sa, "sa"), _f32(sb, "sb")
+    _shape_check(A.dim() == 2 and B.dim() == 2 and A.shape[1] == B.shape[1], "A [M,K] and B [N,K]")
+    M, K = A.shape
+    N = B.shape[0]
+    _shape_check(tuple(sa.shape) == (M, K // 128) and tuple(sb.shape) == ((N + 127) // 128, K // 128),
+                 "sa [M,K/128], sb [ceil(N/128),K/128]")
+    D = _out(out, (M, N), A.device)
+    with torch.cuda.device(A.device):
+        st = lib().fp8gemm_nt(A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(), D.data_ptr(),
+                              M, N, K, _stream(stream, A.device))
+    _check(st, "fp8gemm_nt")
+    return D
+
+
+def grouped_contiguous(A, sa, B, sb, m_indices, out=None, stream=None):
+    """MoE contiguous layout: A [M_total,K], B [G,N,K], m_indices int32 [M_total] (-1 = padding).
+    Padding rows of ``out`` are left untouched (zeros when ``out`` is allocated here)."""
+    torch = _torch()
+    A, B = _codes(A, "A"), _codes(B, "B")
+    sa, sb = _f32(sa, "sa"), _f32(sb, "sb")
+    m_indices = _i32(m_indices, "m_indices")
+    _shape_check(A.dim() == 2 and B.dim() == 3 and A.shape[1] == B.shape[2], "A [M,K] and B [G,N,K]")
+    M, K = A.shape
+    G, N = B.shape[0], B.shape[1]
+    _shape_check(tuple(sa.shape) == (M, K // 128) and tuple(sb.shape) == (G, (N + 127) // 128, K // 128)
+                 and tuple(m_indices.shape) == (M,), "sa [M,K/128], sb [G,ceil(N/128),K/128], m_indices [M]")
+    if out is None:
+        out = torch.zeros((M, N), dtype=torch.bfloat16, device=A.device)
+    D = _out(out, (M, N), A.device)
+    with torch.cuda.device(A.device):
+        st = lib().fp8gemm_grouped_contiguous(A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(),
+                                              m_indices.data_ptr(), D.data_ptr(), M, N, K, G,
+                                              _stream(stream, A.device))
+    _check(st, "fp8gemm_grouped_contiguous")
+    return D
+
+
+def grouped_masked(A, sa, B, sb, masked_m, expected_m: int, out=None, stream=None):
+    """MoE masked layout: A [G,M_max,K], B [G,N,K], masked_m int32 [G]; rows past masked_m[g] of
+    ``out`` are left untouched (zeros when ``out`` is allocated here)."""
+    torch = _torch()
+    A, B = _codes(A, "A"), _codes(B, "B")
+    sa, sb = _f32(sa, "sa"), _f32(sb, "sb")
+    masked_m = _i32(masked_m, "masked_m")
+    _shape_check(A.dim() == 3 and B.dim() == 3 and A.shape[0] == B.shape[0] and A.shape[2] == B.shape[2],
+                 "A [G,M_max,K] and B [G,N,K]")
+    G, M_max, K = A.shape
+    N = B.shape[1]
+    _shape_check(tuple(sa.shape) == (G, M_max, K // 128) and tuple(sb.shape) == (G, (N + 127) // 128, K // 128)
+                 and tuple(masked_m.shape) == (G,), "sa [G,M_max,K/128], sb [G,ceil(N/128),K/128], masked_m [G]")
+    if out is None:
+        out = torch.zeros((G, M_max, N), dtype=torch.bfloat16, device=A.device)
+    D = _out(out, (G, M_max, N), A.device)
+    with torch.cuda.device(A.device):
+        st = lib().fp8gemm_grouped_masked(A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(),
+                                          masked_m.data_ptr(), D.data_ptr(), G, M_max, N, K,
+                                          int(expected_m), _stream(stream, A.device))
+    _check(st, "fp8gemm_grouped_masked")
+    return D

@@ -1,0 +1,378 @@
+// fp8gemm_api.cpp -- C ABI of libfp8gemm.so: argument validation, launch-shape selection,
+// split-K workspace management and kernel launch (host code).
+//
+// Entry points and their meaning: include/fp8gemm.h (the dense NT GEMM and the two M-grouped
+// MoE layouts of page "DeepSeek開源第三彈：V3/R1訓練推理關鍵秘籍，核心代碼僅300行", section
+// 如何使用？).  The launch shape is chosen per call from the problem size (the pages' per-shape
+// block-size choice, section 如何使用？, JIT design item; here an ahead-of-time table).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+#include <vector>
+
+#include "fp8gemm.h"
+#include "fp8gemm_internal.h"
+
+using namespace fp8gemm;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct Workspace {
+    float* partials = nullptr;
+    size_t partial_bytes = 0;
+    int32_t* counters = nullptr;
+    size_t counter_count = 0;
+};
+
+struct DeviceState {
+    std::mutex mu;
+    bool ready = false;
+    int cus = 0;
+    int32_t* err = nullptr;                              // device error word
+    std::vector<int> occupancy;                          // per kernel-table entry
+    std::unordered_map<hipStream_t, Workspace> ws;       // split-K workspace per stream
+};
+
+DeviceState g_dev[kMaxDevices];
+std::atomic<int> g_cu_cap{0};
+thread_local char g_last_config[256] = "";
+
+// Query the device once: CU count, occupancy of every kernel, device error word.
+int device_state(DeviceState** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8GEMM_ERR_HIP;
+    DeviceState& d = g_dev[dev];
+    std::lock_guard<std::mutex> lock(d.mu);
+    if (!d.ready) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8GEMM_ERR_HIP;
+        d.cus = prop.multiProcessorCount;
+        int n = 0;
+        const KernelEntry* tab = kernel_table(&n);
+        d.occupancy.assign(n, 1);
+        for (int i = 0; i < n; ++i) {
+            int blocks = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, tab[i].func, tab[i].threads, 0) ==
+                    hipSuccess && blocks > 0)
+                d.occupancy[i] = blocks;
+        }
+        void* e = nullptr;
+        if (hipMalloc(&e, 256) != hipSuccess) return FP8GEMM_ERR_HIP;
+        if (hipMemset(e, 0, 256) != hipSuccess) return FP8GEMM_ERR_HIP;
+        d.err = static_cast<int32_t*>(e);
+        d.ready = true;
+    }
+    *out = &d;
+    return FP8GEMM_OK;
+}
+
+// The split-K workspace of `stream`, grown to at least the given sizes.  Counters start at zero
+// and every launch leaves them at zero.
+int workspace(DeviceState* d, hipStream_t stream, size_t partial_bytes, size_t counters,
+              Workspace** out) {
+    std::lock_guard<std::mutex> lock(d->mu);
+    Workspace& w = d->ws[stream];
+    if (w.partial_bytes < partial_bytes) {
+        if (w.partials) {
+            if (hipStreamSynchronize(stream) != hipSuccess) return FP8GEMM_ERR_HIP;
+            hipFree(w.partials);
+        }
+        w.partials = nullptr;
+        w.partial_bytes = 0;
+        size_t bytes = std::max(partial_bytes, (size_t)1 << 22);
+        if (hipMalloc(&w.partials, bytes) != hipSuccess) return FP8GEMM_ERR_HIP;
+        w.partial_bytes = bytes;
+    }
+    if (w.counter_count < counters) {
+        if (w.counters) {
+            if (hipStreamSynchronize(stream) != hipSuccess) return FP8GEMM_ERR_HIP;
+            hipFree(w.counters);
+        }
+        w.counters = nullptr;
+        w.counter_count = 0;
+        size_t n = std::max(counters, (size_t)4096);
+        if (hipMalloc(&w.counters, n * sizeof(int32_t)) != hipSuccess) return FP8GEMM_ERR_HIP;
+        if (hipMemset(w.counters, 0, n * sizeof(int32_t)) != hipSuccess) return FP8GEMM_ERR_HIP;
+        w.counter_count = n;
+    }
+    *out = &w;
+    return FP8GEMM_OK;
+}
+
+int find_entry(int layout, int bm, int bn, int wm, int wn, int stages) {
+    int n = 0;
+    const KernelEntry* tab = kernel_table(&n);
+    for (int i = 0; i < n; ++i)
+        if (tab[i].layout == layout && tab[i].bm == bm && tab[i].bn == bn && tab[i].waves_m == wm &&
+            tab[i].waves_n == wn && tab[i].stages == stages)
+            return i;
+    return -1;
+}
+
+// Optional override for experiments: FP8GEMM_FORCE_CONFIG=BMxBN:WMxWN:STAGES:SPLIT
+bool forced_config(int layout, int* idx, int* split) {
+    const char* s = std::getenv("FP8GEMM_FORCE_CONFIG");
+    if (!s || !*s) return false;
+    int bm, bn, wm, wn, st, sp;
+    if (std::sscanf(s, "%dx%d:%dx%d:%d:%d", &bm, &bn, &wm, &wn, &st, &sp) != 6) return false;
+    int i = find_entry(layout, bm, bn, wm, wn, st);
+    if (i < 0) return false;
+    *idx = i;
+    *split = std::max(1, sp);
+    return true;
+}
+
+struct Choice {
+    int entry;
+    int split;
+};
+
+int pick_split(int64_t tiles, int nkb, int target_units) {
+    if (tiles >= target_units) return 1;
+    int64_t s = (target_units + tiles - 1) / tiles;
+    s = std::min<int64_t>(s, std::max(1, nkb / 2));       // keep >= 2 slices per split
+    return (int)std::max<int64_t>(1, s);
+}
+
+// Launch-shape table (see the design notes for the measurements behind each row).
+Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_rows, int G, int cus) {
+    Choice c{-1, 1};
+    int forced = -1, fsplit = 1;
+    if (forced_config(layout, &forced, &fsplit)) return Choice{forced, fsplit};
+    if (layout == kDense) {
+        if (rows <= 64) c.entry = find_entry(kDense, 64, 64, 1, 4, 8);
+        else if (rows <= 128) c.entry = find_entry(kDense, 128, 64, 1, 4, 6);
+        else if (rows >= 1024 && N >= 256) c.entry = find_entry(kDense, 256, 256, 4, 2, 2);
+        else c.entry = find_entry(kDense, 128, 128, 2, 2, 4);
+    } else if (layout == kContiguous) {
+        if (rows >= 2048 && N >= 256) c.entry = find_entry(kContiguous, 128, 256, 2, 4, 2);
+        else c.entry = find_entry(kContiguous, 128, 128, 2, 2, 4);
+    } else {
+        if (expected_rows <= 64) c.entry = find_entry(kMasked, 64, 64, 1, 4, 8);
+        else c.entry = find_entry(kMasked, 128, 64, 1, 4, 6);
+    }
+    int n = 0;
+    const KernelEntry* tab = kernel_table(&n);
+    const KernelEntry& e = tab[c.entry];
+    int64_t tiles_n = (N + e.bn - 1) / e.bn;
+    int64_t active_tiles;
+    if (layout == kMasked) {
+        int64_t per_group = std::max<int64_t>(1, (std::min(expected_rows, rows) + e.bm - 1) / e.bm);
+        active_tiles = (int64_t)G * per_group * tiles_n;
+    } else {
+        active_tiles = ((rows + e.bm - 1) / e.bm) * tiles_n;
+    }
+    c.split = pick_split(active_tiles, nkb, cus);
+    return c;
+}
+
+int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream) {
+    DeviceState* d = nullptr;
+    int st = device_state(&d);
+    if (st != FP8GEMM_OK) return st;
+    int cap = g_cu_cap.load();
+    int cus = (cap > 0 && cap < d->cus) ? cap : d->cus;
+    Choice c = choose(layout, a.rows, a.N, a.nkb, expected_rows, a.G, cus);
+    if (c.entry < 0) return FP8GEMM_ERR_UNSUPPORTED;
+    int n = 0;
+    const KernelEntry* tab = kernel_table(&n);
+    const KernelEntry& e = tab[c.entry];
+
+    a.tiles_m = (int32_t)((a.rows + e.bm - 1) / e.bm);
+    a.tiles_n = (int32_t)((a.N + e.bn - 1) / e.bn);
+    int split = e.splitk ? std::min(c.split, a.nkb) : 1;
+    a.kb_per_split = (a.nkb + split - 1) / split;
+    a.splits = (a.nkb + a.kb_per_split - 1) / a.kb_per_split;
+    const int64_t groups = (layout == kMasked) ? a.G : 1;
+    a.units = groups * a.tiles_m * a.tiles_n * a.splits;
+    a.group_m = (layout != kMasked && a.tiles_m >= 8) ? (layout == kDense ? 4 : 8) : 1;
+    a.err = d->err;
+    a.ws = nullptr;
+    a.counters = nullptr;
+    if (a.splits > 1) {
+        const int64_t tiles = a.units / a.splits;
+        Workspace* w = nullptr;
+        st = workspace(d, stream, (size_t)a.units * e.bm * e.bn * sizeof(float), (size_t)tiles, &w);
+        if (st != FP8GEMM_OK) return st;
+        a.ws = w->partials;
+        a.counters = w->counters;
+    }
+    int64_t slots = (int64_t)cus * d->occupancy[c.entry];
+    int64_t grid = std::min<int64_t>(a.units, slots);
+    if (grid <= 0) return FP8GEMM_OK;
+    std::snprintf(g_last_config, sizeof g_last_config,
+                  "%s tile=%dx%d waves=%dx%d stages=%d split=%d kb_per_split=%d units=%lld grid=%lld",
+                  layout == kDense ? "nt" : (layout == kContiguous ? "contiguous" : "masked"), e.bm,
+                  e.bn, e.waves_m, e.waves_n, e.stages, a.splits, a.kb_per_split,
+                  (long long)a.units, (long long)grid);
+    if (std::getenv("FP8GEMM_LOG")) std::fprintf(stderr, "[fp8gemm] %s\n", g_last_config);
+    e.launch(dim3((unsigned)grid), a, stream);
+    if (hipGetLastError() != hipSuccess) return FP8GEMM_ERR_LAUNCH;
+    return FP8GEMM_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shared checks of the operand pointers (non-null, aligned).
+int check_ptrs(const void* A, const float* sa, const void* B, const float* sb, const void* D) {
+    if (!A || !sa || !B || !sb || !D) return FP8GEMM_ERR_NULL_PTR;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || !aligned(sa, 4) || !aligned(sb, 4))
+        return FP8GEMM_ERR_MISALIGNED;
+    return FP8GEMM_OK;
+}
+
+// Sizes the kernels index with 32-bit per-lane offsets: a tile row offset r*K (r < 256) must fit.
+constexpr int64_t kMaxK = int64_t(1) << 24;
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxBytes = int64_t(1) << 40;
+
+int check_k(int64_t K) {
+    if (K <= 0 || K % 128 != 0) return FP8GEMM_ERR_BAD_SHAPE;
+    if (K > kMaxK) return FP8GEMM_ERR_UNSUPPORTED;
+    return FP8GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8gemm_nt(const void* A, const float* sa, const void* B, const float* sb, void* D, int64_t M,
+               int64_t N, int64_t K, void* stream) {
+    if (M < 0 || N < 0) return FP8GEMM_ERR_BAD_SHAPE;
+    int st = check_k(K);
+    if (st != FP8GEMM_OK) return st;
+    if (M > kMaxRows || N > kMaxRows || M * K >= kMaxBytes || N * K >= kMaxBytes)
+        return FP8GEMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return FP8GEMM_OK;
+    st = check_ptrs(A, sa, B, sb, D);
+    if (st != FP8GEMM_OK) return st;
+    KernelArgs a{};
+    a.A = static_cast<const uint8_t*>(A);
+    a.sa = sa;
+    a.B = static_cast<const uint8_t*>(B);
+    a.sb = sb;
+    a.D = static_cast<uint16_t*>(D);
+    a.rows = M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.G = 1;
+    a.nkb = (int32_t)(K / 128);
+    a.nnb = (int32_t)((N + 127) / 128);
+    return launch(kDense, a, M, static_cast<hipStream_t>(stream));
+}
+
+int fp8gemm_grouped_contiguous(const void* A, const float* sa, const void* B, const float* sb,
+                               const int32_t* m_indices, void* D, int64_t M_total, int64_t N,
+                               int64_t K, int32_t G, void* stream) {
+    if (M_total < 0 || N < 0 || G <= 0) return FP8GEMM_ERR_BAD_SHAPE;
+    int st = check_k(K);
+    if (st != FP8GEMM_OK) return st;
+    if (M_total > kMaxRows || N > kMaxRows || M_total * K >= kMaxBytes || (int64_t)G * N * K >= kMaxBytes)
+        return FP8GEMM_ERR_UNSUPPORTED;
+    if (M_total == 0 || N == 0) return FP8GEMM_OK;
+    st = check_ptrs(A, sa, B, sb, D);
+    if (st != FP8GEMM_OK) return st;
+    if (!m_indices) return FP8GEMM_ERR_NULL_PTR;
+    if (!aligned(m_indices, 4)) return FP8GEMM_ERR_MISALIGNED;
+    KernelArgs a{};
+    a.A = static_cast<const uint8_t*>(A);
+    a.sa = sa;
+    a.B = static_cast<const uint8_t*>(B);
+    a.sb = sb;
+    a.D = static_cast<uint16_t*>(D);
+    a.m_indices = m_indices;
+    a.rows = M_total;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.G = G;
+    a.nkb = (int32_t)(K / 128);
+    a.nnb = (int32_t)((N + 127) / 128);
+    return launch(kContiguous, a, M_total, static_cast<hipStream_t>(stream));
+}
+
+int fp8gemm_grouped_masked(const void* A, const float* sa, const void* B, const float* sb,
+                           const int32_t* masked_m, void* D, int32_t G, int64_t M_max, int64_t N,
+                           int64_t K, int64_t expected_m, void* stream) {
+    if (G <= 0 || M_max < 0 || N < 0 || expected_m < 0) return FP8GEMM_ERR_BAD_SHAPE;
+    int st = check_k(K);
+    if (st != FP8GEMM_OK) return st;
+    if ((int64_t)G * M_max > kMaxRows || N > kMaxRows || (int64_t)G * M_max * K >= kMaxBytes ||
+        (int64_t)G * N * K >= kMaxBytes)
+        return FP8GEMM_ERR_UNSUPPORTED;
+    if (M_max == 0 || N == 0) return FP8GEMM_OK;
+    st = check_ptrs(A, sa, B, sb, D);
+    if (st != FP8GEMM_OK) return st;
+    if (!masked_m) return FP8GEMM_ERR_NULL_PTR;
+    if (!aligned(masked_m, 4)) return FP8GEMM_ERR_MISALIGNED;
+    KernelArgs a{};
+    a.A = static_cast<const uint8_t*>(A);
+    a.sa = sa;
+    a.B = static_cast<const uint8_t*>(B);
+    a.sb = sb;
+    a.D = static_cast<uint16_t*>(D);
+    a.masked_m = masked_m;
+    a.rows = M_max;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.G = G;
+    a.nkb = (int32_t)(K / 128);
+    a.nnb = (int32_t)((N + 127) / 128);
+    int64_t hint = expected_m > 0 ? std::min(expected_m, M_max) : M_max;
+    return launch(kMasked, a, hint, static_cast<hipStream_t>(stream));
+}
+
+const char* fp8gemm_status_string(int status) {
+    switch (status) {
+        case FP8GEMM_OK: return "ok";
+        case FP8GEMM_ERR_NULL_PTR: return "null pointer";
+        case FP8GEMM_ERR_BAD_SHAPE: return "bad shape";
+        case FP8GEMM_ERR_MISALIGNED: return "misaligned pointer";
+        case FP8GEMM_ERR_UNSUPPORTED: return "unsupported size";
+        case FP8GEMM_ERR_LAUNCH: return "kernel launch failed";
+        case FP8GEMM_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int fp8gemm_init(void) {
+    DeviceState* d = nullptr;
+    return device_state(&d);
+}
+
+int fp8gemm_set_num_cus(int n) {
+    if (n < 0) return FP8GEMM_ERR_BAD_SHAPE;
+    g_cu_cap.store(n);
+    return FP8GEMM_OK;
+}
+
+int fp8gemm_last_config(char* buf, int len) {
+    if (!buf || len <= 0) return FP8GEMM_ERR_NULL_PTR;
+    std::snprintf(buf, (size_t)len, "%s", g_last_config);
+    return FP8GEMM_OK;
+}
+
+int fp8gemm_read_device_error(void* stream, int32_t* err) {
+    if (!err) return FP8GEMM_ERR_NULL_PTR;
+    DeviceState* d = nullptr;
+    int st = device_state(&d);
+    if (st != FP8GEMM_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipStreamSynchronize(s) != hipSuccess) return FP8GEMM_ERR_HIP;
+    int32_t v = 0;
+    if (hipMemcpy(&v, d->err, sizeof v, hipMemcpyDeviceToHost) != hipSuccess) return FP8GEMM_ERR_HIP;
+    if (hipMemset(d->err, 0, sizeof v) != hipSuccess) return FP8GEMM_ERR_HIP;
+    *err = v;
+    return FP8GEMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,529 @@
+// fp8gemm_kernels.hip -- gfx950 (MI355X) kernels of the FP8 block-scaled GEMM.
+//
+// One kernel body serves the dense NT GEMM and the two M-grouped MoE layouts (page
+// "DeepSeek開源第三彈：V3/R1訓練推理關鍵秘籍，核心代碼僅300行", sections 深入了解DeepGEMM and
+// 如何使用？: a single core kernel, fine-grained scaling, two-level accumulation; NT layout;
+// contiguous and masked grouped variants).
+//
+// Per work unit (an output tile, for one K range) a workgroup
+//   1. streams 128-wide K slices of the B tile, the A tile and their scales from HBM into an
+//      LDS ring with direct-to-LDS DMA loads (global_load_lds_dword[x4]), STAGES slices ahead;
+//   2. per slice and per 16x16 sub-tile issues ONE v_mfma_f32_16x16x128_f8f6f4 with a zero
+//      accumulator input, so the matrix core returns the fresh fp32 partial of exactly that
+//      128-wide block (the FP8 matrix-core sum is not exact fp32, so the partial is kept short);
+//   3. promotes the partial: acc += partial * (sa[m][kb] * sb[n/128][kb]) with VALU FMAs in
+//      fp32 -- the pages' two-level accumulation, re-derived for MFMA;
+//   4. rounds acc once to bf16 (round to nearest even) and stores D, or, when the K range is
+//      split across workgroups, writes its fp32 partial tile to a workspace; the last workgroup
+//      of the tile to arrive sums all partials in split order and stores D.
+//
+// MFMA orientation: the matrix core computes C[i][j] = sum_k X[i][k] Y[j][k] with lane l
+// holding X row (l % 16), Y row (l % 16) and output column (l % 16), rows 4*(l/16)..+3.  The
+// kernel feeds B rows as X and A rows as Y, so every lane owns 4 consecutive n of one m: the
+// promotion scale sa[m]*sb[n/128] is one value per lane per sub-tile and the bf16 results of a
+// lane are contiguous in D.  Both operands give lane l the K bytes [32*(l/16), +32) of the
+// slice, in the same order (the hardware pairs equal positions of X and Y).
+//
+// LDS layout of one slice: rows of 128 bytes, 16-byte chunk c of row r stored at chunk
+// position c ^ ((r >> 1) & 7), so the 16 lanes of a ds_read_b128 phase (rows r..r+15, one
+// chunk) hit 16 distinct 16-byte bank groups of the 64-bank (256 B) LDS.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8gemm_internal.h"
+
+namespace fp8gemm {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------------------------------
+// device helpers
+// ------------------------------------------------------------------------------------------
+
+// Direct-to-LDS loads.  Lane i of the wave moves 16 (x4) or 4 (x1) bytes from global address
+// sbase + voff (uniform 64-bit base, per-lane 32-bit offset) to LDS address lds_base + 16*i (4*i).  Written as inline asm so that the compiler does
+// not insert a full vmcnt wait before every later LDS read (it cannot tell the ring's stages
+// apart); the kernel waits for these loads itself with s_waitcnt vmcnt.  They have no register
+// outputs.  M0 is written here and used by nothing else in these kernels (checked on the built
+// code object by the build script).
+__device__ __forceinline__ void dma_x4(uint32_t lds_base, const void* sbase, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds_base), "v"(voff), "s"(sbase) : "memory");
+}
+__device__ __forceinline__ void dma_x1(uint32_t lds_base, const void* sbase, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(lds_base), "v"(voff), "s"(sbase) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Wait until at most `per * k` of this wave's DMA loads are in flight, 0 <= k <= KMAX.
+template <int PER, int KMAX>
+__device__ __forceinline__ void wait_slices(int k) {
+    if constexpr (KMAX == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (k >= KMAX) wait_vmcnt<PER * KMAX>();
+        else wait_slices<PER, KMAX - 1>(k);
+    }
+}
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// Values that are the same in every lane but not provably so to the compiler (results of
+// cross-lane reductions, pointers derived from them) are moved to scalar registers explicitly.
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+__device__ __forceinline__ v4f mfma16x16x128(const v8i& x, const v8i& y) {
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    // format code 0 = E4M3 for both operands; scale operands 0 select the unscaled form
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, zero, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even (v_cvt_pk_bf16_f32)
+    uint16_t ua, ub;
+    __builtin_memcpy(&ua, &a, 2);
+    __builtin_memcpy(&ub, &b, 2);
+    return (uint32_t)ua | ((uint32_t)ub << 16);
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// ------------------------------------------------------------------------------------------
+// the kernel
+// ------------------------------------------------------------------------------------------
+
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT>
+struct Tile {
+    static constexpr int NW = WMW * WNW;            // waves per workgroup
+    static constexpr int NT = 64 * NW;
+    static constexpr int WM = BM / WMW;             // rows of M per wave
+    static constexpr int WN = BN / WNW;             // rows of N per wave
+    static constexpr int JM = WM / 16;              // 16-wide M sub-tiles per wave
+    static constexpr int IN = WN / 16;              // 16-wide N sub-tiles per wave
+    static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
+    static_assert(BN % (8 * NW) == 0 && BM % (8 * NW) == 0, "each wave moves whole 8-row groups");
+    static_assert(BM % 64 == 0, "scale rows of A are moved 64 at a time");
+    static constexpr int B_OFF = 0;
+    static constexpr int A_OFF = BN * 128;
+    static constexpr int SA_OFF = (BN + BM) * 128;
+    static constexpr int SB_OFF = SA_OFF + BM * 4;
+    static constexpr int STAGE_BYTES = SB_OFF + 256;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static constexpr int B_DMA = BN / (8 * NW);     // x4 loads per wave per slice for B
+    static constexpr int A_DMA = BM / (8 * NW);
+    static constexpr int AUX = (BM / 64 + 1 + NW - 1) / NW;  // x1 loads per wave: sa chunks + sb
+    static constexpr int NDMA = B_DMA + A_DMA + AUX;
+    static_assert(NDMA * (STAGES - 1) < 64, "vmcnt range");
+    // every wave's N range lies inside one 128-row block of B scales
+    static constexpr bool NB_UNIFORM = (BN % 128 == 0) && (128 % WN == 0);
+    // split-K partial reduction is compiled for tiles small enough to need it (decode shapes)
+    static constexpr bool SPLITK = BM * BN <= 128 * 256;
+};
+
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT>
+__global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArgs args) {
+    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
+    __shared__ int s_flag;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WMW;              // wave position along M
+    const int wn = wave / WMW;              // wave position along N
+    const int row16 = lane & 15;
+    const int grp = lane >> 4;
+
+    const int K = args.K;
+    const int N = args.N;
+    const int nkb = args.nkb;
+    const int nnb = args.nnb;
+    const uint32_t smem_base = lds_addr(smem);
+
+    // XCD-aware order: workgroups are dealt to the 8 XCDs round robin, so give the workgroups
+    // of one XCD a contiguous range of logical ids (consecutive units share operand panels).
+    const int P = gridDim.x;
+    int logical = blockIdx.x;
+    if ((P & 7) == 0) logical = (blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3);
+
+    for (int64_t unit = logical; unit < args.units; unit += P) {
+        // ---- decode the unit: split s fastest, then M tile, N tile, group -------------------
+        int64_t u = unit;
+        const int split = (int)(u % args.splits); u /= args.splits;
+        int tm, tn;
+        if (args.group_m > 1) {
+            // bands of group_m M tiles; inside a band the M tile varies fastest
+            const int64_t per_group_units = (int64_t)args.tiles_m * args.tiles_n;
+            const int64_t grp_i = u / per_group_units;
+            int64_t v = u % per_group_units;
+            const int band_units = args.group_m * args.tiles_n;
+            const int band = (int)(v / band_units);
+            const int inb = (int)(v % band_units);
+            const int band_m0 = band * args.group_m;
+            const int band_h = min(args.group_m, args.tiles_m - band_m0);
+            tm = band_m0 + inb % band_h;
+            tn = inb / band_h;
+            u = grp_i;
+        } else {
+            tm = (int)(u % args.tiles_m); u /= args.tiles_m;
+            tn = (int)(u % args.tiles_n); u /= args.tiles_n;
+        }
+        const int gidx = (int)u;                       // group (masked layout), else 0
+        const int m0 = tm * BM;                        // first row of the tile (within group)
+        const int n0 = tn * BN;
+        const int kb0 = split * args.kb_per_split;
+        const int kb1 = min(nkb, kb0 + args.kb_per_split);
+        const int nks = kb1 - kb0;
+
+        // ---- rows of A, group of B ---------------------------------------------------------
+        int64_t arow0;        // first row of A / sa / D for this tile
+        int row_limit;        // rows [0, row_limit) of the tile are in range of the A array
+        int valid_rows;       // rows [0, valid_rows) may be valid (contiguous: further masked)
+        int g = 0;
+        if constexpr (LAYOUT == kMasked) {
+            g = gidx;
+            int cnt = args.masked_m[g];
+            if (cnt < 0 || cnt > args.rows) {
+                if (tm == 0 && tn == 0 && split == 0 && tid == 0)
+                    atomicOr(args.err, kDevErrBadCount);
+                cnt = cnt < 0 ? 0 : (int)args.rows;
+            }
+            if (m0 >= cnt) continue;                   // uniform: whole workgroup skips
+            arow0 = (int64_t)g * args.rows + m0;
+            row_limit = (int)min((int64_t)BM, args.rows - m0);
+            valid_rows = min(BM, cnt - m0);
+        } else if constexpr (LAYOUT == kContiguous) {
+            arow0 = m0;
+            row_limit = (int)min((int64_t)BM, args.rows - m0);
+            // the group of this tile's 128-row block: the largest id among its rows
+            int gmax = -1, bad = 0;
+            for (int r = lane; r < row_limit; r += 64) {
+                int id = args.m_indices[arow0 + r];
+                if (id < -1 || id >= args.G) bad = 1;
+                else gmax = max(gmax, id);
+            }
+            gmax = __builtin_amdgcn_readfirstlane(wave_max(gmax));
+            // any row whose id is neither -1 nor the block's group breaks the precondition
+            int off = 0;
+            for (int r = lane; r < row_limit; r += 64) {
+                int id = args.m_indices[arow0 + r];
+                if (id >= 0 && id < args.G && id != gmax) off = 1;
+            }
+            bad = __builtin_amdgcn_readfirstlane(wave_max(bad | off));
+            if (bad && wave == 0 && lane == 0 && split == 0 && tn == 0) atomicOr(args.err, kDevErrBadIndex);
+            if (gmax < 0) continue;                    // padding only: nothing to compute
+            g = gmax;
+            valid_rows = row_limit;
+        } else {
+            arow0 = m0;
+            row_limit = (int)min((int64_t)BM, args.rows - m0);
+            valid_rows = row_limit;
+        }
+        (void)valid_rows;
+        const uint8_t* Ag = args.A + arow0 * K;
+        const float* sag = args.sa + arow0 * nkb;
+        const uint8_t* Bg = args.B + (int64_t)g * N * K;
+        const float* sbg = args.sb + (int64_t)g * nnb * nkb;
+        const int nb_first = n0 >> 7;
+        const int nb_count = min(nnb, (n0 + BN + 127) >> 7) - nb_first;
+
+        // ---- per-lane DMA source offsets (32-bit, relative to uniform per-slice bases) -------
+        // B and A: x4 load e of the workgroup covers tile rows 8e..8e+7; lane -> (row, chunk).
+        uint32_t b_off[T::B_DMA];
+#pragma unroll
+        for (int q = 0; q < T::B_DMA; ++q) {
+            const int r = 8 * (wave * T::B_DMA + q) + (lane >> 3);
+            const int c = (lane & 7) ^ swz(r);
+            const int n = min(r, N - 1 - n0);          // clamp the N tail to a real row
+            b_off[q] = (uint32_t)n * (uint32_t)K + (uint32_t)(c * 16);
+        }
+        uint32_t a_off[T::A_DMA];
+#pragma unroll
+        for (int q = 0; q < T::A_DMA; ++q) {
+            const int r = 8 * (wave * T::A_DMA + q) + (lane >> 3);
+            const int c = (lane & 7) ^ swz(r);
+            const int rr = min(r, row_limit - 1);
+            a_off[q] = (uint32_t)rr * (uint32_t)K + (uint32_t)(c * 16);
+        }
+        // aux x1 loads: chunk x < BM/64 moves sa rows 64x..64x+63, chunk BM/64 moves sb
+        uint32_t aux_off[T::AUX];
+#pragma unroll
+        for (int t = 0; t < T::AUX; ++t) {
+            const int x = wave + T::NW * t;
+            if (x < BM / 64) {
+                const int r = min(64 * x + lane, row_limit - 1);
+                aux_off[t] = (uint32_t)r * (uint32_t)nkb * 4u;
+            } else {
+                const int nb = nb_first + min(lane, nb_count - 1);
+                aux_off[t] = (uint32_t)nb * (uint32_t)nkb * 4u;
+            }
+        }
+        const uint8_t* Bt = uniform_ptr(Bg + (int64_t)n0 * K + (int64_t)kb0 * 128);  // slice-0 bases
+        const uint8_t* At = uniform_ptr(Ag + (int64_t)kb0 * 128);
+        const float* sat = uniform_ptr(sag + kb0);
+        const float* sbt = uniform_ptr(sbg + kb0);
+
+        auto issue_slice = [&](int i) {
+            const uint32_t st = smem_base + (uint32_t)((i % STAGES) * T::STAGE_BYTES);
+            const uint8_t* bs = uniform_ptr(Bt + (int64_t)i * 128);
+            const uint8_t* as = uniform_ptr(At + (int64_t)i * 128);
+#pragma unroll
+            for (int q = 0; q < T::B_DMA; ++q)
+                dma_x4(st + T::B_OFF + 8 * (wave * T::B_DMA + q) * 128, bs, b_off[q]);
+#pragma unroll
+            for (int q = 0; q < T::A_DMA; ++q)
+                dma_x4(st + T::A_OFF + 8 * (wave * T::A_DMA + q) * 128, as, a_off[q]);
+#pragma unroll
+            for (int t = 0; t < T::AUX; ++t) {
+                const int x = wave + T::NW * t;
+                if (x < BM / 64) dma_x1(st + T::SA_OFF + 256 * x, uniform_ptr(sat + i), aux_off[t]);
+                else dma_x1(st + T::SB_OFF, uniform_ptr(sbt + i), aux_off[t]);
+            }
+        };
+
+        // ---- accumulators -------------------------------------------------------------------
+        v4f acc[T::IN][T::JM];
+#pragma unroll
+        for (int i = 0; i < T::IN; ++i)
+#pragma unroll
+            for (int j = 0; j < T::JM; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+        // ---- pipeline prologue --------------------------------------------------------------
+#pragma unroll
+        for (int i = 0; i < STAGES - 1; ++i)
+            if (i < nks) issue_slice(i);
+
+        // ---- main loop over 128-wide K slices -----------------------------------------------
+        for (int i = 0; i < nks; ++i) {
+            // slice i landed (this wave's loads), then every wave's loads
+            wait_slices<T::NDMA, STAGES - 2>(min(STAGES - 2, nks - 1 - i));
+            __syncthreads();
+            if (i + STAGES - 1 < nks) issue_slice(i + STAGES - 1);
+
+            const uint8_t* st = smem + (i % STAGES) * T::STAGE_BYTES;
+            const float* sa_l = reinterpret_cast<const float*>(st + T::SA_OFF);
+            const float* sb_l = reinterpret_cast<const float*>(st + T::SB_OFF);
+
+            // A fragments (Y operand) and their scales for this wave's JM sub-tiles
+            v8i af[T::JM];
+            float sav[T::JM];
+#pragma unroll
+            for (int j = 0; j < T::JM; ++j) {
+                const int r = wm * T::WM + 16 * j + row16;
+                const uint8_t* rp = st + T::A_OFF + r * 128;
+                const v4i lo = *reinterpret_cast<const v4i*>(rp + (((2 * grp) ^ swz(r)) << 4));
+                const v4i hi = *reinterpret_cast<const v4i*>(rp + (((2 * grp + 1) ^ swz(r)) << 4));
+                af[j] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                sav[j] = sa_l[r];
+            }
+            float sw[T::JM];
+            if constexpr (T::NB_UNIFORM) {
+                const float sbw = sb_l[((n0 + wn * T::WN) >> 7) - nb_first];
+#pragma unroll
+                for (int j = 0; j < T::JM; ++j) sw[j] = sav[j] * sbw;
+            }
+            // Software pipeline over the N sub-tiles: the MFMAs of sub-tile i2 are issued before
+            // the promotion FMAs of sub-tile i2-1, so the matrix core and the VALU overlap and
+            // only one sub-tile row of partials is live.
+            auto load_bf = [&](int i2) {
+                const int r = wn * T::WN + 16 * i2 + row16;
+                const uint8_t* rp = st + T::B_OFF + r * 128;
+                const v4i lo = *reinterpret_cast<const v4i*>(rp + (((2 * grp) ^ swz(r)) << 4));
+                const v4i hi = *reinterpret_cast<const v4i*>(rp + (((2 * grp + 1) ^ swz(r)) << 4));
+                return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            };
+            auto promote = [&](int i2, const v4f (&p)[T::JM]) {
+                float sbi = 0.f;
+                if constexpr (!T::NB_UNIFORM) sbi = sb_l[((n0 + wn * T::WN + 16 * i2) >> 7) - nb_first];
+#pragma unroll
+                for (int j = 0; j < T::JM; ++j) {
+                    float s;
+                    if constexpr (T::NB_UNIFORM) s = sw[j];
+                    else s = sav[j] * sbi;
+                    acc[i2][j] += p[j] * s;
+                }
+            };
+            v4f pprev[T::JM];
+            v8i bf = load_bf(0);
+#pragma unroll
+            for (int i2 = 0; i2 < T::IN; ++i2) {
+                v4f pcur[T::JM];
+#pragma unroll
+                for (int j = 0; j < T::JM; ++j) pcur[j] = mfma16x16x128(bf, af[j]);
+                if (i2 + 1 < T::IN) bf = load_bf(i2 + 1);
+                if (i2 > 0) promote(i2 - 1, pprev);
+#pragma unroll
+                for (int j = 0; j < T::JM; ++j) pprev[j] = pcur[j];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            promote(T::IN - 1, pprev);
+        }
+
+        // ---- epilogue -----------------------------------------------------------------------
+        bool store_direct = true;
+        if (T::SPLITK && args.splits > 1) {
+            // write this split's fp32 partial tile, lane-major (coalesced 16-byte stores)
+            const int64_t tile_id = unit / args.splits;
+            float* wsp = args.ws + (tile_id * args.splits + split) * (int64_t)(BM * BN)
+                         + (int64_t)wave * (T::WM * T::WN);
+#pragma unroll
+            for (int i2 = 0; i2 < T::IN; ++i2)
+#pragma unroll
+                for (int j = 0; j < T::JM; ++j)
+                    *reinterpret_cast<v4f*>(wsp + ((i2 * T::JM + j) * 64 + lane) * 4) = acc[i2][j];
+            __threadfence();
+            __syncthreads();
+            if (tid == 0) {
+                const int old = atomicAdd(args.counters + tile_id, 1);
+                const int last = (old == args.splits - 1);
+                if (last) args.counters[tile_id] = 0;     // ready for the next launch
+                s_flag = last;
+            }
+            __syncthreads();
+            store_direct = s_flag != 0;
+            if (store_direct) {
+                __threadfence();
+                // sum every split's partial (this one's included) from the workspace, in split
+                // order, so the result does not depend on which workgroup arrived last
+                const float* wsb = args.ws + tile_id * args.splits * (int64_t)(BM * BN)
+                                   + (int64_t)wave * (T::WM * T::WN);
+                for (int s2 = 0; s2 < args.splits; ++s2) {
+                    const float* p = wsb + (int64_t)s2 * (BM * BN);
+#pragma unroll
+                    for (int i2 = 0; i2 < T::IN; ++i2)
+#pragma unroll
+                        for (int j = 0; j < T::JM; ++j) {
+                            const v4f v = __builtin_nontemporal_load(
+                                reinterpret_cast<const v4f*>(p + ((i2 * T::JM + j) * 64 + lane) * 4));
+                            acc[i2][j] = (s2 == 0) ? v : acc[i2][j] + v;
+                        }
+                }
+            }
+        }
+        if (store_direct) {
+            // lane owns D[m][n..n+3] per sub-tile
+#pragma unroll
+            for (int j = 0; j < T::JM; ++j) {
+                const int rm = wm * T::WM + 16 * j + row16;     // row within the tile
+                bool ok = rm < valid_rows;
+                if constexpr (LAYOUT == kContiguous) {
+                    if (ok) ok = args.m_indices[arow0 + rm] == g;
+                }
+                if (!ok) continue;
+                uint16_t* drow = args.D + (arow0 + rm) * (int64_t)N;
+#pragma unroll
+                for (int i2 = 0; i2 < T::IN; ++i2) {
+                    const int n = n0 + wn * T::WN + 16 * i2 + 4 * grp;
+                    const v4f v = acc[i2][j];
+                    if (n + 3 < N && (N & 3) == 0) {
+                        uint2 pk;
+                        pk.x = pack_bf16x2(v.x, v.y);
+                        pk.y = pack_bf16x2(v.z, v.w);
+                        *reinterpret_cast<uint2*>(drow + n) = pk;
+                    } else {
+                        const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            if (n + r < N) {
+                                __bf16 h = (__bf16)e[r];
+                                uint16_t hb;
+                                __builtin_memcpy(&hb, &h, 2);
+                                drow[n + r] = hb;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        // the next unit's prologue rewrites stages other waves may still be reading
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// instantiation table
+// ------------------------------------------------------------------------------------------
+
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT>
+static void launch_impl(dim3 grid, const KernelArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT>), grid,
+                       dim3(WMW * WNW * 64), 0, s, a);
+}
+
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT>
+static KernelEntry entry(const char* name) {
+    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT>;
+    KernelEntry e;
+    e.name = name;
+    e.layout = LAYOUT;
+    e.bm = BM;
+    e.bn = BN;
+    e.waves_m = WMW;
+    e.waves_n = WNW;
+    e.stages = STAGES;
+    e.threads = T::NT;
+    e.splitk = T::SPLITK;
+    e.lds_bytes = T::LDS_BYTES;
+    e.func = reinterpret_cast<const void*>(&fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT>);
+    e.launch = &launch_impl<BM, BN, WMW, WNW, STAGES, LAYOUT>;
+    return e;
+}
+
+#define FP8GEMM_ENTRY(BM, BN, WMW, WNW, ST, L) \
+    entry<BM, BN, WMW, WNW, ST, L>(#L " " #BM "x" #BN " waves " #WMW "x" #WNW " stages " #ST)
+
+const KernelEntry* kernel_table(int* count) {
+    static const KernelEntry table[] = {
+        // large M: 256x256 tiles, 8 waves (4 along M x 2 along N), 2-slice ring
+        FP8GEMM_ENTRY(256, 256, 4, 2, 2, kDense),
+        // medium tiles
+        FP8GEMM_ENTRY(128, 128, 2, 2, 4, kDense),
+        FP8GEMM_ENTRY(128, 256, 2, 4, 2, kDense),
+        // decode (M <= 128): all rows in one tile, narrow N tiles, deep ring
+        FP8GEMM_ENTRY(64, 64, 1, 4, 8, kDense),
+        FP8GEMM_ENTRY(128, 64, 1, 4, 6, kDense),
+        FP8GEMM_ENTRY(64, 32, 1, 2, 8, kDense),
+        // contiguous grouped: tiles never cross a 128-row block
+        FP8GEMM_ENTRY(128, 256, 2, 4, 2, kContiguous),
+        FP8GEMM_ENTRY(128, 128, 2, 2, 4, kContiguous),
+        FP8GEMM_ENTRY(64, 64, 1, 4, 8, kContiguous),
+        // masked grouped
+        FP8GEMM_ENTRY(64, 64, 1, 4, 8, kMasked),
+        FP8GEMM_ENTRY(128, 64, 1, 4, 6, kMasked),
+        FP8GEMM_ENTRY(128, 128, 2, 2, 4, kMasked),
+        FP8GEMM_ENTRY(64, 32, 1, 2, 8, kMasked),
+    };
+    *count = (int)(sizeof(table) / sizeof(table[0]));
+    return table;
+}
+
+}  // namespace fp8gemm

@@ -1,0 +1,120 @@
+/*
+ * fp8gemm.h -- C ABI of the MI355X (gfx950) FP8 block-scaled GEMM library (libfp8gemm.so).
+ *
+ * Operation (page "DeepSeek開源第三彈：V3/R1訓練推理關鍵秘籍，核心代碼僅300行", sections
+ * 深入了解DeepGEMM and 如何使用？): FP8 GEMM with fine-grained scaling in NT layout (left operand
+ * not transposed, right operand transposed), BF16 output, plus the two M-grouped MoE layouts
+ * (contiguous and masked; also page "DeepGEMM：AI計算の経済性を変えるオープンソースライブラリ",
+ * section DeepGEMMが重要な理由, item 4):
+ *
+ *   D[m][n] = bf16( sum_kb sa[m][kb] * sb[n/128][kb] * sum_{k in [128kb, 128kb+128)} A[m][k] * B[n][k] )
+ *
+ * with A, B in OCP E4M3 ("e4m3fn"), sa one fp32 scale per 1x128 block of a row of A and sb one
+ * fp32 scale per 128x128 block of B.  The GPU forms each 128-wide K block's partial product on
+ * the matrix cores, then scales it by sa*sb and adds it into an fp32 accumulator (the pages'
+ * two-level accumulation), and rounds once to bf16 (round to nearest even).
+ *
+ * Conventions for every GEMM entry point:
+ *   - All matrix and scale pointers are DEVICE pointers; the caller owns every buffer.
+ *   - All arrays are dense row-major with the last index contiguous:
+ *       A  [rows][K] uint8 codes      sa [rows][K/128] float
+ *       B  [(G)][N][K] uint8 codes    sb [(G)][ceil(N/128)][K/128] float
+ *       D  [rows][N] bfloat16 (uint16 bit patterns)
+ *   - K must be a positive multiple of 128; M, N may be any non-negative size (N tails are
+ *     masked).  A, B and D must be 16-byte aligned; sa, sb and the index vectors 4-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls are asynchronous:
+ *     they validate on the host (no device access, no synchronisation), enqueue the kernel and
+ *     return.  An argument error is reported before anything is enqueued.
+ *   - Results are deterministic: the same inputs give the same bits, whatever the launch
+ *     configuration's timing (split-K partials are summed in a fixed order).
+ *   - Thread safety: calls may come from any host thread.  Calls on different streams may run
+ *     concurrently; each stream has its own library-owned split-K workspace, created on first
+ *     use of that stream (one hipMalloc; call fp8gemm_init() or make one call per stream before
+ *     any HIP graph capture).  fp8gemm_set_num_cus is a global knob, not synchronised with
+ *     calls in flight.
+ *
+ * Return value of every int function: a fp8gemm_status code.
+ */
+#ifndef FP8GEMM_H
+#define FP8GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8gemm_status {
+    FP8GEMM_OK = 0,
+    FP8GEMM_ERR_NULL_PTR = 1,    /* a required pointer is NULL */
+    FP8GEMM_ERR_BAD_SHAPE = 2,   /* negative size, K not a positive multiple of 128, G <= 0, expected_m < 0 */
+    FP8GEMM_ERR_MISALIGNED = 3,  /* A, B or D not 16-byte aligned, or a scale/index vector not 4-byte aligned */
+    FP8GEMM_ERR_UNSUPPORTED = 4, /* a size beyond the supported range (an operand of 2^40 bytes or more, K >= 2^31) */
+    FP8GEMM_ERR_LAUNCH = 5,      /* the HIP launch failed (hipGetLastError after the launch) */
+    FP8GEMM_ERR_HIP = 6          /* a HIP runtime call failed (device query, workspace allocation, copy) */
+} fp8gemm_status;
+
+/* Dense NT GEMM, gemm_fp8_fp8_bf16_nt (page "DeepSeek開源第三彈…", section 如何使用？).
+ *   A [M][K] e4m3, sa [M][K/128], B [N][K] e4m3, sb [ceil(N/128)][K/128], D [M][N] bf16.
+ *   M == 0 or N == 0 is a valid no-op. */
+int fp8gemm_nt(const void* A, const float* sa, const void* B, const float* sb, void* D,
+               int64_t M, int64_t N, int64_t K, void* stream);
+
+/* M-grouped GEMM, contiguous layout, m_grouped_gemm_fp8_fp8_bf16_nt_contiguous (same page and
+ * section; page "DeepGEMM：AI計算の経済性を…", section DeepGEMMが重要な理由: token sequences are
+ * grouped per expert).  The rows of all groups are concatenated along M:
+ *   A [M_total][K], sa [M_total][K/128], B [G][N][K], sb [G][ceil(N/128)][K/128],
+ *   m_indices [M_total] int32 (device): row r is multiplied by B[m_indices[r]];
+ *   m_indices[r] == -1 marks a padding row, whose D row is left untouched.
+ *   D [M_total][N].
+ * Precondition: within each aligned block of 128 rows all rows that are not -1 carry the same
+ * group id (groups are padded to multiples of 128 rows).  A row whose id is outside [-1, G), or
+ * differs from the id of its 128-row block, is treated as padding and flags
+ * FP8GEMM_DEVERR_BAD_INDEX in the device error word (see fp8gemm_read_device_error). */
+int fp8gemm_grouped_contiguous(const void* A, const float* sa, const void* B, const float* sb,
+                               const int32_t* m_indices, void* D, int64_t M_total, int64_t N,
+                               int64_t K, int32_t G, void* stream);
+
+/* M-grouped GEMM, masked layout, m_grouped_gemm_fp8_fp8_bf16_nt_masked (same page and section;
+ * page "DeepGEMM：AI計算の経済性を…", section DeepGEMMが重要な理由: sparse expert activation).
+ * Every group owns a fixed block of M_max rows:
+ *   A [G][M_max][K], sa [G][M_max][K/128], B [G][N][K], sb [G][ceil(N/128)][K/128],
+ *   masked_m [G] int32 (device): rows r < masked_m[g] of group g are valid; D rows at or past it
+ *   are left untouched.  A count above M_max is clamped to M_max and flags
+ *   FP8GEMM_DEVERR_BAD_COUNT; a negative count is taken as 0 and flags it too.
+ *   expected_m >= 0: a hint of the typical masked_m, used only to pick the launch shape;
+ *   it never changes results.  D [G][M_max][N]. */
+int fp8gemm_grouped_masked(const void* A, const float* sa, const void* B, const float* sb,
+                           const int32_t* masked_m, void* D, int32_t G, int64_t M_max, int64_t N,
+                           int64_t K, int64_t expected_m, void* stream);
+
+/* Device-side precondition flags (bits of the device error word). */
+#define FP8GEMM_DEVERR_BAD_INDEX 1 /* contiguous: an m_indices entry outside [-1, G) or off its block's group */
+#define FP8GEMM_DEVERR_BAD_COUNT 2 /* masked: a masked_m entry outside [0, M_max] */
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* fp8gemm_status_string(int status);
+
+/* Optional eager set-up on the current device: device query and the device error word.  The
+ * GEMM calls do it lazily otherwise.  Returns FP8GEMM_ERR_HIP when no device is usable. */
+int fp8gemm_init(void);
+
+/* Cap the number of compute units the launch shapes are sized for and the persistent grids
+ * occupy (the "set max SM count" utility of page "DeepSeek開源第三彈…", section 如何使用？).
+ * n == 0 restores all CUs; n < 0 is FP8GEMM_ERR_BAD_SHAPE. */
+int fp8gemm_set_num_cus(int n);
+
+/* The launch configuration chosen by the last GEMM call on the calling host thread, as text
+ * (e.g. "nt tile=256x256 waves=4x2 stages=2 split=1 grid=256"), NUL-terminated into buf[len].
+ * Returns FP8GEMM_ERR_NULL_PTR when buf is NULL or len <= 0. */
+int fp8gemm_last_config(char* buf, int len);
+
+/* Synchronise `stream`, then read and clear the current device's error word into *err
+ * (FP8GEMM_DEVERR_* bits; 0 when every index and count met the preconditions). */
+int fp8gemm_read_device_error(void* stream, int32_t* err);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8GEMM_H */

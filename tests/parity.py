@@ -1,0 +1,51 @@
+"""Comparison helpers for the GPU parity tests (oracle vs HIP library)."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+REL = 2.0 ** -7      # one bf16 ulp, relative
+ABS_RMS = 1e-3       # times rms(ref) over the call's valid outputs
+
+
+def bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return oracle.bf16_bits_to_float(bits).astype(np.float64)
+
+
+def gpu_bits(t) -> np.ndarray:
+    """bf16 device tensor -> uint16 bit patterns on the host."""
+    import torch
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def within_tolerance(got_bits: np.ndarray, ref_bits: np.ndarray, mask=None, rms_ref=None):
+    """|gpu - ref| <= 2^-7 |ref| + 1e-3 rms(ref), per element, over `mask` (all if None).
+    Returns (ok, report)."""
+    g = bits_to_f64(got_bits)
+    r = bits_to_f64(ref_bits)
+    if mask is not None:
+        g, r = g[mask], r[mask]
+    if rms_ref is None:
+        rms_ref = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    err = np.abs(g - r)
+    lim = REL * np.abs(r) + ABS_RMS * rms_ref
+    bad = ~(err <= lim)
+    eq = float(np.mean(g == r)) if r.size else 1.0
+    rep = dict(n=int(r.size), bad=int(bad.sum()), bit_equal=eq,
+               max_err_over_lim=float(np.max(err / np.maximum(lim, 1e-300))) if r.size else 0.0,
+               rms_ref=rms_ref)
+    return (not bad.any()), rep
+
+
+def assert_close(got_bits, ref_bits, mask=None, rms_ref=None, what=""):
+    ok, rep = within_tolerance(got_bits, ref_bits, mask, rms_ref)
+    assert ok, "%s: %s" % (what, rep)
+    return rep
+
+
+def assert_bit_exact(got_bits, ref_bits, mask=None, what=""):
+    g = got_bits if mask is None else got_bits[mask]
+    r = ref_bits if mask is None else ref_bits[mask]
+    neq = int(np.sum(g != r))
+    assert neq == 0, "%s: %d of %d outputs differ in bits" % (what, neq, r.size)

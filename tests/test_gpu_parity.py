@@ -1,0 +1,398 @@
+"""GPU parity: the HIP library (called through the C ABI) against the CPU oracle, element by
+element, on seeded inputs.  Floating-point cases: |gpu - ref| <= 2^-7 |ref| + 1e-3 rms(ref);
+integer-valued and power-of-two-scale cases: bit-exact."""
+import os
+import re
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from parity import assert_bit_exact, assert_close, gpu_bits
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU runs deselect these with -m "not gpu"
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import fp8_block_scaled_x128_amd as fg  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SENTINEL = 0x7FC1   # a NaN pattern the library never writes
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def run_dense(d, out=None):
+    D = fg.gemm_nt(dev(d.A), dev(d.sa), dev(d.B), dev(d.sb), out=out)
+    torch.cuda.synchronize()
+    return D
+
+
+def sentinel_tensor(shape):
+    t = torch.full(shape, SENTINEL, dtype=torch.int16, device="cuda")
+    return t.view(torch.bfloat16)
+
+
+def kernel_table():
+    src = open(os.path.join(ROOT, "fp8_block_scaled_x128_amd", "csrc", "fp8gemm_kernels.hip")).read()
+    return [(int(a), int(b), int(c), int(d), int(e), f) for a, b, c, d, e, f in
+            re.findall(r"FP8GEMM_ENTRY\((\d+), (\d+), (\d+), (\d+), (\d+), (k\w+)\)", src)]
+
+
+class forced:
+    """Force the launch configuration of the calls inside the block (FP8GEMM_FORCE_CONFIG)."""
+
+    def __init__(self, bm, bn, wm, wn, st, split):
+        self.v = "%dx%d:%dx%d:%d:%d" % (bm, bn, wm, wn, st, split)
+
+    def __enter__(self):
+        os.environ["FP8GEMM_FORCE_CONFIG"] = self.v
+
+    def __exit__(self, *exc):
+        os.environ.pop("FP8GEMM_FORCE_CONFIG", None)
+
+
+def int_codes(rng, shape, lo=-4, hi=4):
+    vals = rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+    return torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+# ------------------------------------------------------------------------------------------
+# dense
+# ------------------------------------------------------------------------------------------
+
+def test_config0_full_parity():
+    d = W.config0()
+    D = run_dense(d)
+    ref = oracle.gemm_nt(d.A, d.sa, d.B, d.sb)
+    rep = assert_close(gpu_bits(D), ref, what="config 0")
+    say("config0", fg.last_config(), rep)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (3, 17, 256), (64, 64, 128), (65, 300, 640),
+                                   (128, 2112, 1024), (130, 257, 384), (256, 512, 1024),
+                                   (1030, 520, 1152), (64, 2112, 7168)])
+def test_integer_inputs_bit_exact(M, N, K):
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    A, B = int_codes(rng, (M, K)), int_codes(rng, (N, K))
+    sa = np.ones((M, K // 128), np.float32)
+    sb = np.ones(((N + 127) // 128, K // 128), np.float32)
+    d = W.Dense(A, sa, B, sb)
+    D = run_dense(d)
+    assert_bit_exact(gpu_bits(D), oracle.gemm_nt(A, sa, B, sb), what="integer %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", [(70, 300, 640), (64, 2112, 1024), (257, 390, 1024), (2048, 384, 512)])
+def test_power_of_two_scales_bit_exact(M, N, K):
+    """Integer codes with power-of-two block scales: every term and sum is exact in fp32, so a
+    wrong K-block or N-block scale index (N=300/390/2112 straddle 128-blocks) changes bits."""
+    rng = np.random.default_rng(M + N + K)
+    A, B = int_codes(rng, (M, K)), int_codes(rng, (N, K))
+    sa = (2.0 ** rng.integers(-1, 2, size=(M, K // 128))).astype(np.float32)
+    sb = (2.0 ** rng.integers(-1, 2, size=((N + 127) // 128, K // 128))).astype(np.float32)
+    D = run_dense(W.Dense(A, sa, B, sb))
+    assert_bit_exact(gpu_bits(D), oracle.gemm_nt(A, sa, B, sb), what="pow2 %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 7, 128), (5, 130, 256), (17, 33, 384), (64, 64, 128),
+                                   (100, 300, 640), (129, 257, 256), (300, 520, 1152),
+                                   (1024, 512, 512), (1100, 384, 256), (2048, 640, 384)])
+def test_random_ragged_shapes(M, N, K):
+    d = W.dense(M, N, K, seed=M + 1000 * N + K)
+    D = run_dense(d)
+    rep = assert_close(gpu_bits(D), oracle.gemm_nt(d.A, d.sa, d.B, d.sb), what="%dx%dx%d" % (M, N, K))
+    say("ragged", M, N, K, fg.last_config(), rep["bit_equal"])
+
+
+@pytest.mark.parametrize("entry", [e for e in kernel_table() if e[5] == "kDense"],
+                         ids=lambda e: "%dx%d_w%dx%d_s%d" % e[:5])
+@pytest.mark.parametrize("split", [1, 3])
+def test_every_dense_kernel_config(entry, split):
+    bm, bn, wm, wn, st, _ = entry
+    M, N, K = 2 * bm + 5, 2 * bn + 17, 1152
+    d = W.dense(M, N, K, seed=bm * bn + split)
+    ref = oracle.gemm_nt(d.A, d.sa, d.B, d.sb)
+    with forced(bm, bn, wm, wn, st, split):
+        D = run_dense(d)
+        cfg = fg.last_config()
+    assert "tile=%dx%d" % (bm, bn) in cfg, cfg
+    assert_close(gpu_bits(D), ref, what=cfg)
+    # integer inputs through the same configuration are bit-exact
+    rng = np.random.default_rng(5)
+    A, B = int_codes(rng, (M, K)), int_codes(rng, (N, K))
+    sa = (2.0 ** rng.integers(-1, 2, size=(M, K // 128))).astype(np.float32)
+    sb = (2.0 ** rng.integers(-1, 2, size=((N + 127) // 128, K // 128))).astype(np.float32)
+    with forced(bm, bn, wm, wn, st, split):
+        D2 = run_dense(W.Dense(A, sa, B, sb))
+    assert_bit_exact(gpu_bits(D2), oracle.gemm_nt(A, sa, B, sb), what=cfg)
+
+
+def test_output_guard_band_and_determinism():
+    """No write outside D (canaries around it) and identical bits on repeated calls (split-K)."""
+    d = W.dense(64, 2112, 7168, seed=77)
+    M, N = 64, 2112
+    pad = 4096
+    buf = sentinel_tensor((M * N + 2 * pad,))
+    D = buf[pad:pad + M * N].view(M, N)
+    run_dense(d, out=D)
+    b = gpu_bits(buf)
+    assert np.all(b[:pad] == SENTINEL) and np.all(b[-pad:] == SENTINEL)
+    first = gpu_bits(D).copy()
+    for _ in range(3):
+        run_dense(d, out=D)
+        assert np.array_equal(gpu_bits(D), first)
+    say("determinism", fg.last_config())
+
+
+def test_cu_cap_and_side_stream():
+    """A CU cap shrinks the persistent grid (it may change the split-K choice, hence the order of
+    the fp32 partial sums: compared within tolerance); a side stream gives the same bits."""
+    d = W.dense(200, 700, 1024, seed=78)
+    ref_oracle = oracle.gemm_nt(d.A, d.sa, d.B, d.sb)
+    ref = gpu_bits(run_dense(d))
+    fg.set_num_cus(24)
+    try:
+        D = run_dense(d)
+        cfg = fg.last_config()
+    finally:
+        fg.set_num_cus(0)
+    assert_close(gpu_bits(D), ref_oracle, what=cfg)
+    assert "grid=" in cfg and int(cfg.split("grid=")[1]) <= 24
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        D2 = fg.gemm_nt(dev(d.A), dev(d.sa), dev(d.B), dev(d.sb))
+    s.synchronize()
+    assert np.array_equal(gpu_bits(D2), ref)
+
+
+# ------------------------------------------------------------------------------------------
+# grouped: contiguous
+# ------------------------------------------------------------------------------------------
+
+def run_contig(c, out=None):
+    D = fg.grouped_contiguous(dev(c.A), dev(c.sa), dev(c.B), dev(c.sb), dev(c.m_indices), out=out)
+    torch.cuda.synchronize()
+    return D
+
+
+@pytest.mark.parametrize("counts,N,K", [([100, 0, 257, 128, 3], 320, 512), ([128], 256, 256),
+                                        ([1, 1, 1], 64, 128), ([700, 300], 2112, 1024)])
+def test_contiguous_parity_and_padding_untouched(counts, N, K):
+    c = W.contiguous(counts, 0, N, K, seed=sum(counts) + N, packed=True)
+    M = c.A.shape[0]
+    out = sentinel_tensor((M, N))
+    D = run_contig(c, out=out)
+    ref, valid = oracle.grouped_contiguous(c.A, c.sa, c.B, c.sb, c.m_indices)
+    v = valid.astype(bool)
+    got = gpu_bits(D)
+    rep = assert_close(got, ref, mask=v[:, None].repeat(N, 1), what="contiguous %s" % counts)
+    assert np.all(got[~v] == SENTINEL), "padding rows were written"
+    # refill the padding rows with other data: valid outputs keep their bits
+    A2, sa2 = c.A.copy(), c.sa.copy()
+    rng = np.random.default_rng(3)
+    A2[~v] = W.random_codes(rng, (int((~v).sum()), K))
+    sa2[~v] = 1e3
+    D2 = run_contig(W.Contiguous(A2, sa2, c.B, c.sb, c.m_indices))
+    assert np.array_equal(gpu_bits(D2)[v], got[v])
+    assert fg.read_device_error() == 0
+    say("contiguous", counts, fg.last_config(), rep["bit_equal"])
+
+
+@pytest.mark.parametrize("entry", [e for e in kernel_table() if e[5] == "kContiguous"],
+                         ids=lambda e: "%dx%d_w%dx%d_s%d" % e[:5])
+@pytest.mark.parametrize("split", [1, 2])
+def test_every_contiguous_kernel_config(entry, split):
+    bm, bn, wm, wn, st, _ = entry
+    c = W.contiguous([130, 0, 250], 0, 2 * bn + 40, 640, seed=bm + bn + split, packed=True)
+    ref, valid = oracle.grouped_contiguous(c.A, c.sa, c.B, c.sb, c.m_indices)
+    with forced(bm, bn, wm, wn, st, split):
+        D = run_contig(c)
+        cfg = fg.last_config()
+    assert "tile=%dx%d" % (bm, bn) in cfg, cfg
+    v = valid.astype(bool)
+    assert_close(gpu_bits(D), ref, mask=v[:, None].repeat(D.shape[1], 1), what=cfg)
+
+
+def test_contiguous_equals_per_group_dense():
+    c = W.contiguous([256, 384], 0, 512, 1024, seed=91, packed=True)
+    D = gpu_bits(run_contig(c))
+    for g in range(2):
+        rows = np.nonzero(c.m_indices == g)[0]
+        Dg = run_dense(W.Dense(c.A[rows], c.sa[rows], c.B[g], c.sb[g]))
+        # the same rows through the dense entry point: equal within tolerance (launch shapes differ)
+        assert_close(D[rows], gpu_bits(Dg), what="group %d" % g)
+
+
+def test_contiguous_bad_index_flags_and_is_padding():
+    c = W.contiguous([128, 128], 0, 128, 256, seed=92, packed=True)
+    mi = c.m_indices.copy()
+    mi[5] = 7           # out of range
+    mi[200] = 0         # a group-0 row inside group 1's block
+    out = sentinel_tensor(c.A.shape[:1] + (128,))
+    D = fg.grouped_contiguous(dev(c.A), dev(c.sa), dev(c.B), dev(c.sb), dev(mi), out=out)
+    err = fg.read_device_error()
+    assert err & fg.DEVERR_BAD_INDEX
+    got = gpu_bits(D)
+    assert np.all(got[5] == SENTINEL) and np.all(got[200] == SENTINEL)
+    ref, valid = oracle.grouped_contiguous(c.A, c.sa, c.B, c.sb, c.m_indices)
+    keep = np.ones(256, bool)
+    keep[[5, 200]] = False
+    assert_close(got[keep], ref[keep], what="bad index rows excluded")
+    assert fg.read_device_error() == 0      # cleared by the read
+
+
+# ------------------------------------------------------------------------------------------
+# grouped: masked
+# ------------------------------------------------------------------------------------------
+
+def run_masked(w, expected_m, out=None):
+    D = fg.grouped_masked(dev(w.A), dev(w.sa), dev(w.B), dev(w.sb), dev(w.masked_m), expected_m, out=out)
+    torch.cuda.synchronize()
+    return D
+
+
+@pytest.mark.parametrize("mm,M_max,N,K", [([0, 1, 64, 200, 130], 200, 192, 384),
+                                          ([64, 64], 64, 4096, 256), ([3], 256, 100, 128)])
+def test_masked_parity_rows_past_count_untouched(mm, M_max, N, K):
+    w = W.masked(np.array(mm, np.int32), M_max, N, K, seed=sum(mm) + N)
+    G = len(mm)
+    ref, valid = oracle.grouped_masked(w.A, w.sa, w.B, w.sb, w.masked_m)
+    v = valid.astype(bool)
+    results = []
+    for em in (1, 64, M_max):
+        out = sentinel_tensor((G, M_max, N))
+        D = run_masked(w, em, out=out)
+        got = gpu_bits(D)
+        assert_close(got, ref, mask=np.broadcast_to(v[:, :, None], got.shape), what="masked em=%d" % em)
+        assert np.all(got[~v] == SENTINEL)
+        results.append(got)
+    assert fg.read_device_error() == 0
+    say("masked", mm, fg.last_config())
+
+
+@pytest.mark.parametrize("entry", [e for e in kernel_table() if e[5] == "kMasked"],
+                         ids=lambda e: "%dx%d_w%dx%d_s%d" % e[:5])
+@pytest.mark.parametrize("split", [1, 3])
+def test_every_masked_kernel_config(entry, split):
+    bm, bn, wm, wn, st, _ = entry
+    w = W.masked(np.array([bm + 3, 0, 17, 2 * bm], np.int32), 2 * bm, 2 * bn + 24, 768, seed=bm * 3 + split)
+    ref, valid = oracle.grouped_masked(w.A, w.sa, w.B, w.sb, w.masked_m)
+    with forced(bm, bn, wm, wn, st, split):
+        D = run_masked(w, 64)
+        cfg = fg.last_config()
+    assert "tile=%dx%d" % (bm, bn) in cfg, cfg
+    got = gpu_bits(D)
+    assert_close(got, ref, mask=np.broadcast_to(valid.astype(bool)[:, :, None], got.shape), what=cfg)
+
+
+def test_masked_count_out_of_range_clamps_and_flags():
+    w = W.masked(np.array([64, 10], np.int32), 64, 128, 256, seed=93)
+    mm = np.array([1000, -5], np.int32)
+    D = fg.grouped_masked(dev(w.A), dev(w.sa), dev(w.B), dev(w.sb), dev(mm), 64,
+                          out=sentinel_tensor((2, 64, 128)))
+    assert fg.read_device_error() & fg.DEVERR_BAD_COUNT
+    ref, valid = oracle.grouped_masked(w.A, w.sa, w.B, w.sb, mm)
+    got = gpu_bits(D)
+    assert np.all(got[1] == SENTINEL)
+    assert_close(got[0], ref[0], what="clamped count")
+
+
+# ------------------------------------------------------------------------------------------
+# full-size workloads: sampled outputs
+# ------------------------------------------------------------------------------------------
+
+def sample_positions(rng, rows, N, n_random=3000):
+    r = [0, rows - 1] + list(rng.integers(0, rows, 6))
+    rr, cc = [], []
+    for x in r:
+        cols = np.unique(np.concatenate([np.arange(min(64, N)), np.arange(max(0, N - 64), N),
+                                         rng.integers(0, N, 64)]))
+        rr.append(np.full(cols.size, x))
+        cc.append(cols)
+    rr.append(rng.integers(0, rows, n_random))
+    cc.append(rng.integers(0, N, n_random))
+    return np.concatenate(rr).astype(np.int64), np.concatenate(cc).astype(np.int64)
+
+
+def check_sampled_dense(d, D, seed):
+    M, N, K = d.shape
+    rng = np.random.default_rng(seed)
+    r, c = sample_positions(rng, M, N)
+    ref = oracle.elements(d.A, d.sa, d.B, d.sb, r, c, c // 128)
+    got = gpu_bits(D)
+    gs = got[r, c]
+    full = oracle.bf16_bits_to_float(got)
+    assert np.all(np.isfinite(full)), "non-finite outputs"
+    return assert_close(gs, ref, what="sampled %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("mi", range(len(W.SWEEP_M)))
+@pytest.mark.parametrize("nki", range(len(W.SWEEP_NK)))
+def test_sweep_full_size_sampled(mi, nki):
+    M, (N, K) = W.SWEEP_M[mi], W.SWEEP_NK[nki]
+    say("sweep case", M, N, K)
+    d = W.sweep_case(mi, nki)
+    D = run_dense(d)
+    rep = check_sampled_dense(d, D, seed=mi * 10 + nki)
+    say("sweep", M, N, K, fg.last_config(), rep["bit_equal"])
+
+
+def check_sampled_grouped(A, sa, B, sb, D_bits, rows_valid, rows_group, N, seed, what):
+    """rows_valid: flattened row ids (into A/sa/D) with their group rows_group."""
+    rng = np.random.default_rng(seed)
+    K = A.shape[-1]
+    nkb, nnb = K // 128, (N + 127) // 128
+    pick = rng.integers(0, rows_valid.size, 4000)
+    r = rows_valid[pick]
+    g = rows_group[pick]
+    c = rng.integers(0, N, pick.size)
+    ref = oracle.elements(A.reshape(-1, K), sa.reshape(-1, nkb), B.reshape(-1, K), sb.reshape(-1, nkb),
+                          r, g * N + c, g * nnb + c // 128)
+    return assert_close(D_bits.reshape(-1, N)[r, c], ref, what=what)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_contiguous_configs_full_size_sampled(cfg):
+    say("contiguous config", cfg)
+    c = W.config2() if cfg == 2 else W.config3()
+    N = c.B.shape[1]
+    out = sentinel_tensor((c.A.shape[0], N))
+    D = run_contig(c, out=out)
+    got = gpu_bits(D)
+    valid = c.m_indices >= 0
+    assert np.all(got[~valid] == SENTINEL)
+    rows = np.nonzero(valid)[0]
+    rep = check_sampled_grouped(c.A, c.sa, c.B, c.sb, got, rows, c.m_indices[rows], N, cfg,
+                                "config %d" % cfg)
+    assert fg.read_device_error() == 0
+    say("contiguous config", cfg, fg.last_config(), rep["bit_equal"])
+
+
+@pytest.mark.slow
+def test_masked_config4_full_size_sampled():
+    say("masked config 4")
+    w = W.config4()
+    G, M_max, K = w.A.shape
+    N = w.B.shape[1]
+    out = sentinel_tensor((G, M_max, N))
+    D = run_masked(w, w.expected_m, out=out)
+    got = gpu_bits(D)
+    valid = np.arange(M_max)[None, :] < w.masked_m[:, None]
+    assert np.all(got[~valid] == SENTINEL)
+    gi, ri = np.nonzero(valid)
+    rep = check_sampled_grouped(w.A, w.sa, w.B, w.sb, got, gi * M_max + ri, gi, N, 4, "config 4")
+    assert fg.read_device_error() == 0
+    say("masked config 4", fg.last_config(), rep["bit_equal"])
