@@ -74,7 +74,8 @@ def main():
                 b_cache[nki] = (torch.from_numpy(Bq).to(dev), torch.from_numpy(sbq).to(dev), Bq, sbq)
             Bd, sbd, Bq, sbq = b_cache[nki]
             Aq, saq = W._acts(np.random.default_rng(a_seed), M, K)
-            cases.append(dict(M=M, N=N, K=K, A=torch.from_numpy(Aq).to(dev), sa=torch.from_numpy(saq).to(dev),
+            cases.append(dict(M=M, N=N, K=K, A=torch.from_numpy(Aq).to(dev),
+                              sa=torch.from_numpy(np.ascontiguousarray(saq.T)).to(dev),
                               B=Bd, sb=sbd, D=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
                               hostA=Aq, hostsa=saq, hostB=Bq, hostsb=sbq))
     # interleave M values so that no two consecutive GEMMs share a weight matrix
@@ -186,7 +187,8 @@ def bench_grouped(fg, W, torch, dev, stream, reps=10):
                        ("masked_cfg4", W.config4)):
         t0 = time.time()
         w = make()
-        A, sa, B, sb = (torch.from_numpy(x).to(dev) for x in (w.A, w.sa, w.B, w.sb))
+        A, B, sb = (torch.from_numpy(x).to(dev) for x in (w.A, w.B, w.sb))
+        sa = torch.from_numpy(np.ascontiguousarray(np.swapaxes(w.sa, -1, -2))).to(dev)  # K-block-major
         N, K = w.B.shape[1], w.B.shape[2]
         if name.startswith("contiguous"):
             idx = torch.from_numpy(w.m_indices).to(dev)

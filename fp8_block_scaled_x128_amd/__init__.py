@@ -8,7 +8,7 @@ C ABI declared in include/fp8gemm.h.  torch supplies device memory and the curre
     D = grouped_masked(A, sa, B, sb, masked_m, expected_m) # MoE, fixed per-group capacity
 
 A and B are E4M3 codes (torch.float8_e4m3fn or uint8), sa one fp32 scale per 1x128 block of a
-row of A, sb one per 128x128 block of B (page "DeepSeek開源第三彈：V3/R1訓練推理關鍵秘籍，核心代碼僅
+row of A stored K-block-major (sa[kb, m], shape [K/128, M]), sb one per 128x128 block of B (page "DeepSeek開源第三彈：V3/R1訓練推理關鍵秘籍，核心代碼僅
 300行", sections 深入了解DeepGEMM and 如何使用？).  There is no CPU fallback: without the built
 library every call raises.
 """
@@ -161,15 +161,15 @@ def _shape_check(cond, msg):
 
 
 def gemm_nt(A, sa, B, sb, out=None, stream=None):
-    """D[M,N] (bf16) = A[M,K] . B[N,K]^T with sa [M, K/128] and sb [ceil(N/128), K/128]."""
+    """D[M,N] (bf16) = A[M,K] . B[N,K]^T with sa [K/128, M] and sb [ceil(N/128), K/128]."""
     torch = _torch()
     A, B = _codes(A, "A"), _codes(B, "B")
     sa, sb = _f32(sa, "sa"), _f32(sb, "sb")
     _shape_check(A.dim() == 2 and B.dim() == 2 and A.shape[1] == B.shape[1], "A [M,K] and B [N,K]")
     M, K = A.shape
     N = B.shape[0]
-    _shape_check(tuple(sa.shape) == (M, K // 128) and tuple(sb.shape) == ((N + 127) // 128, K // 128),
-                 "sa [M,K/128], sb [ceil(N/128),K/128]")
+    _shape_check(tuple(sa.shape) == (K // 128, M) and tuple(sb.shape) == ((N + 127) // 128, K // 128),
+                 "sa [K/128,M], sb [ceil(N/128),K/128]")
     D = _out(out, (M, N), A.device)
     with torch.cuda.device(A.device):
         st = lib().fp8gemm_nt(A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(), D.data_ptr(),
@@ -179,7 +179,8 @@ def gemm_nt(A, sa, B, sb, out=None, stream=None):
 
 
 def grouped_contiguous(A, sa, B, sb, m_indices, out=None, stream=None):
-    """MoE contiguous layout: A [M_total,K], B [G,N,K], m_indices int32 [M_total] (-1 = padding).
+    """MoE contiguous layout: A [M_total,K], sa [K/128,M_total], B [G,N,K], m_indices int32 [M_total]
+    (-1 = padding).
     Padding rows of ``out`` are left untouched (zeros when ``out`` is allocated here)."""
     torch = _torch()
     A, B = _codes(A, "A"), _codes(B, "B")
@@ -188,8 +189,8 @@ def grouped_contiguous(A, sa, B, sb, m_indices, out=None, stream=None):
     _shape_check(A.dim() == 2 and B.dim() == 3 and A.shape[1] == B.shape[2], "A [M,K] and B [G,N,K]")
     M, K = A.shape
     G, N = B.shape[0], B.shape[1]
-    _shape_check(tuple(sa.shape) == (M, K // 128) and tuple(sb.shape) == (G, (N + 127) // 128, K // 128)
-                 and tuple(m_indices.shape) == (M,), "sa [M,K/128], sb [G,ceil(N/128),K/128], m_indices [M]")
+    _shape_check(tuple(sa.shape) == (K // 128, M) and tuple(sb.shape) == (G, (N + 127) // 128, K // 128)
+                 and tuple(m_indices.shape) == (M,), "sa [K/128,M], sb [G,ceil(N/128),K/128], m_indices [M]")
     if out is None:
         out = torch.zeros((M, N), dtype=torch.bfloat16, device=A.device)
     D = _out(out, (M, N), A.device)
@@ -202,7 +203,7 @@ def grouped_contiguous(A, sa, B, sb, m_indices, out=None, stream=None):
 
 
 def grouped_masked(A, sa, B, sb, masked_m, expected_m: int, out=None, stream=None):
-    """MoE masked layout: A [G,M_max,K], B [G,N,K], masked_m int32 [G]; rows past masked_m[g] of
+    """MoE masked layout: A [G,M_max,K], sa [G,K/128,M_max], B [G,N,K], masked_m int32 [G]; rows past masked_m[g] of
     ``out`` are left untouched (zeros when ``out`` is allocated here)."""
     torch = _torch()
     A, B = _codes(A, "A"), _codes(B, "B")
@@ -212,8 +213,8 @@ def grouped_masked(A, sa, B, sb, masked_m, expected_m: int, out=None, stream=Non
                  "A [G,M_max,K] and B [G,N,K]")
     G, M_max, K = A.shape
     N = B.shape[1]
-    _shape_check(tuple(sa.shape) == (G, M_max, K // 128) and tuple(sb.shape) == (G, (N + 127) // 128, K // 128)
-                 and tuple(masked_m.shape) == (G,), "sa [G,M_max,K/128], sb [G,ceil(N/128),K/128], masked_m [G]")
+    _shape_check(tuple(sa.shape) == (G, K // 128, M_max) and tuple(sb.shape) == (G, (N + 127) // 128, K // 128)
+                 and tuple(masked_m.shape) == (G,), "sa [G,K/128,M_max], sb [G,ceil(N/128),K/128], masked_m [G]")
     if out is None:
         out = torch.zeros((G, M_max, N), dtype=torch.bfloat16, device=A.device)
     D = _out(out, (G, M_max, N), A.device)

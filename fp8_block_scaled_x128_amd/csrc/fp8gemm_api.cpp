@@ -137,42 +137,47 @@ struct Choice {
     int split;
 };
 
-int pick_split(int64_t tiles, int nkb, int target_units) {
-    if (tiles >= target_units) return 1;
-    int64_t s = (target_units + tiles - 1) / tiles;
-    s = std::min<int64_t>(s, std::max(1, nkb / 2));       // keep >= 2 slices per split
+// K splits so that tiles * splits is about one unit per CU, each split keeping >= 4 K slices.
+int pick_split(int64_t tiles, int nkb, int cus) {
+    if (tiles >= cus) return 1;
+    int64_t s = (cus + tiles / 2) / tiles;
+    s = std::min<int64_t>(s, std::max(1, nkb / 4));
     return (int)std::max<int64_t>(1, s);
 }
 
-// Launch-shape table (see the design notes for the measurements behind each row).
+// Launch-shape table.  Rows of A per tile decide the regime:
+//  - <= 128 rows (decode): HBM-bound stream of B.  Tiles span all rows of A (64, or 128 when A
+//    re-reads would cost as much as B: K >= 8192 or very wide N), N tiles of 64 or 128 so that
+//    about one unit per CU is in flight, and split-K to reach that count on narrow N.
+//  - >= 1024 rows (prefill): MFMA-bound; 256x256 tiles, 8 waves.
+//  - in between: 128x128 tiles.
 Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_rows, int G, int cus) {
     Choice c{-1, 1};
     int forced = -1, fsplit = 1;
     if (forced_config(layout, &forced, &fsplit)) return Choice{forced, fsplit};
-    if (layout == kDense) {
-        if (rows <= 64) c.entry = find_entry(kDense, 64, 64, 1, 4, 8);
-        else if (rows <= 128) c.entry = find_entry(kDense, 128, 64, 1, 4, 6);
-        else if (rows >= 1024 && N >= 256) c.entry = find_entry(kDense, 256, 256, 4, 2, 2);
-        else c.entry = find_entry(kDense, 128, 128, 2, 2, 4);
-    } else if (layout == kContiguous) {
-        if (rows >= 2048 && N >= 256) c.entry = find_entry(kContiguous, 128, 256, 2, 4, 2);
-        else c.entry = find_entry(kContiguous, 128, 128, 2, 2, 4);
+    const int64_t m = (layout == kMasked) ? std::max<int64_t>(1, std::min(expected_rows, rows)) : rows;
+    const int64_t groups = (layout == kMasked) ? G : 1;
+    const int64_t K = (int64_t)nkb * 128;
+    if (m <= 64) {
+        const int64_t t64 = groups * ((N + 63) / 64);
+        if (t64 * 2 >= 3 * cus) c.entry = find_entry(layout, 64, 128, 1, 4, 3);
+        else c.entry = find_entry(layout, 64, 64, 1, 4, 4);
+    } else if (m <= 128) {
+        if (N >= 16384 || K >= 8192) c.entry = find_entry(layout, 128, 128, 2, 4, 3);
+        else c.entry = find_entry(layout, 64, 64, 1, 4, 4);
+    } else if (m >= 1024 && N >= 256 && layout == kDense) {
+        c.entry = find_entry(layout, 256, 256, 4, 2, 2);
+    } else if (m >= 1024 && N >= 256 && layout == kContiguous) {
+        c.entry = find_entry(layout, 128, 256, 2, 4, 2);
     } else {
-        if (expected_rows <= 64) c.entry = find_entry(kMasked, 64, 64, 1, 4, 8);
-        else c.entry = find_entry(kMasked, 128, 64, 1, 4, 6);
+        c.entry = find_entry(layout, 128, 128, 2, 2, 4);
     }
+    if (c.entry < 0) return c;
     int n = 0;
     const KernelEntry* tab = kernel_table(&n);
     const KernelEntry& e = tab[c.entry];
-    int64_t tiles_n = (N + e.bn - 1) / e.bn;
-    int64_t active_tiles;
-    if (layout == kMasked) {
-        int64_t per_group = std::max<int64_t>(1, (std::min(expected_rows, rows) + e.bm - 1) / e.bm);
-        active_tiles = (int64_t)G * per_group * tiles_n;
-    } else {
-        active_tiles = ((rows + e.bm - 1) / e.bm) * tiles_n;
-    }
-    c.split = pick_split(active_tiles, nkb, cus);
+    const int64_t tiles = groups * ((m + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
+    c.split = pick_split(tiles, nkb, cus);
     return c;
 }
 

@@ -77,6 +77,11 @@ __device__ __forceinline__ void wait_slices(int k) {
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
+// Buffer resource flags of a raw (untyped) buffer on gfx9, and the sc1 cache-policy bit: an
+// access coherent at agent scope (what the compiler emits for agent-scope atomic loads/stores).
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kSc1 = 16;
+
 // Values that are the same in every lane but not provably so to the compiler (results of
 // cross-lane reductions, pointers derived from them) are moved to scalar registers explicitly.
 template <typename P>
@@ -250,7 +255,11 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
         }
         (void)valid_rows;
         const uint8_t* Ag = args.A + arow0 * K;
-        const float* sag = args.sa + arow0 * nkb;
+        // sa is stored K-block-major: [group][K/128][rows], so the scales of one K block for
+        // consecutive rows are contiguous (one DMA instruction covers 64 rows)
+        int64_t sa_first = arow0;                     // element (kb, r) of the group: kb*rows + r
+        if constexpr (LAYOUT == kMasked) sa_first = (int64_t)g * nkb * args.rows + m0;
+        const float* sag = args.sa + sa_first;
         const uint8_t* Bg = args.B + (int64_t)g * N * K;
         const float* sbg = args.sb + (int64_t)g * nnb * nkb;
         const int nb_first = n0 >> 7;
@@ -281,7 +290,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
             const int x = wave + T::NW * t;
             if (x < BM / 64) {
                 const int r = min(64 * x + lane, row_limit - 1);
-                aux_off[t] = (uint32_t)r * (uint32_t)nkb * 4u;
+                aux_off[t] = (uint32_t)r * 4u;
             } else {
                 const int nb = nb_first + min(lane, nb_count - 1);
                 aux_off[t] = (uint32_t)nb * (uint32_t)nkb * 4u;
@@ -289,7 +298,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
         }
         const uint8_t* Bt = uniform_ptr(Bg + (int64_t)n0 * K + (int64_t)kb0 * 128);  // slice-0 bases
         const uint8_t* At = uniform_ptr(Ag + (int64_t)kb0 * 128);
-        const float* sat = uniform_ptr(sag + kb0);
+        const float* sat = uniform_ptr(sag + (int64_t)kb0 * args.rows);
         const float* sbt = uniform_ptr(sbg + kb0);
 
         auto issue_slice = [&](int i) {
@@ -305,7 +314,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
 #pragma unroll
             for (int t = 0; t < T::AUX; ++t) {
                 const int x = wave + T::NW * t;
-                if (x < BM / 64) dma_x1(st + T::SA_OFF + 256 * x, uniform_ptr(sat + i), aux_off[t]);
+                if (x < BM / 64) dma_x1(st + T::SA_OFF + 256 * x, uniform_ptr(sat + (int64_t)i * args.rows), aux_off[t]);
                 else dma_x1(st + T::SB_OFF, uniform_ptr(sbt + i), aux_off[t]);
             }
         };
@@ -383,6 +392,19 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
                 if (i2 > 0) promote(i2 - 1, pprev);
 #pragma unroll
                 for (int j = 0; j < T::JM; ++j) pprev[j] = pcur[j];
+                // issue order inside the step: one MFMA, the next fragment's LDS reads, then
+                // alternate MFMAs with the promotion FMAs of the previous step, so that one wave
+                // keeps the matrix core and the VALU busy at the same time
+                if (i2 > 0) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // DS read
+#pragma unroll
+                    for (int j = 1; j < T::JM; ++j) {
+                        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);      // VALU
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);         // VALU
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             promote(T::IN - 1, pprev);
@@ -391,39 +413,45 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
         // ---- epilogue -----------------------------------------------------------------------
         bool store_direct = true;
         if (T::SPLITK && args.splits > 1) {
-            // write this split's fp32 partial tile, lane-major (coalesced 16-byte stores)
+            // Split-K exchange between the workgroups of one tile, which may sit on different
+            // XCDs (each with its own L2).  Partials are written and read with agent-coherent
+            // (sc1) 16-byte buffer accesses, so no L2-wide write-back or invalidate is needed:
+            //   write partial (sc1) -> wait until written -> barrier -> counter += 1 (agent)
+            //   last arrival: barrier -> read all partials (sc1) in split order -> store D
             const int64_t tile_id = unit / args.splits;
-            float* wsp = args.ws + (tile_id * args.splits + split) * (int64_t)(BM * BN)
-                         + (int64_t)wave * (T::WM * T::WN);
+            const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                uniform_ptr(args.ws + tile_id * args.splits * (int64_t)(BM * BN)), 0,
+                (int)(args.splits * BM * BN * 4), kBufferFlags);
+            const int lane_off = (wave * (T::WM * T::WN) + lane * 4) * 4;
 #pragma unroll
             for (int i2 = 0; i2 < T::IN; ++i2)
 #pragma unroll
                 for (int j = 0; j < T::JM; ++j)
-                    *reinterpret_cast<v4f*>(wsp + ((i2 * T::JM + j) * 64 + lane) * 4) = acc[i2][j];
-            __threadfence();
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        acc[i2][j], ws_rsrc,
+                        lane_off + ((split * BM * BN) + (i2 * T::JM + j) * 256) * 4, 0, kSc1);
+            wait_vmcnt<0>();
             __syncthreads();
             if (tid == 0) {
-                const int old = atomicAdd(args.counters + tile_id, 1);
+                const int old = __hip_atomic_fetch_add(args.counters + tile_id, 1, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
                 const int last = (old == args.splits - 1);
-                if (last) args.counters[tile_id] = 0;     // ready for the next launch
+                if (last)   // ready for the next launch
+                    __hip_atomic_store(args.counters + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 s_flag = last;
             }
             __syncthreads();
             store_direct = s_flag != 0;
             if (store_direct) {
-                __threadfence();
-                // sum every split's partial (this one's included) from the workspace, in split
-                // order, so the result does not depend on which workgroup arrived last
-                const float* wsb = args.ws + tile_id * args.splits * (int64_t)(BM * BN)
-                                   + (int64_t)wave * (T::WM * T::WN);
+                // sum every split's partial (this one's included) in split order, so the result
+                // does not depend on which workgroup arrived last
                 for (int s2 = 0; s2 < args.splits; ++s2) {
-                    const float* p = wsb + (int64_t)s2 * (BM * BN);
 #pragma unroll
                     for (int i2 = 0; i2 < T::IN; ++i2)
 #pragma unroll
                         for (int j = 0; j < T::JM; ++j) {
-                            const v4f v = __builtin_nontemporal_load(
-                                reinterpret_cast<const v4f*>(p + ((i2 * T::JM + j) * 64 + lane) * 4));
+                            const v4f v = __builtin_amdgcn_raw_buffer_load_b128(
+                                ws_rsrc, lane_off + ((s2 * BM * BN) + (i2 * T::JM + j) * 256) * 4, 0, kSc1);
                             acc[i2][j] = (s2 == 0) ? v : acc[i2][j] + v;
                         }
                 }
@@ -503,24 +531,26 @@ static KernelEntry entry(const char* name) {
 
 const KernelEntry* kernel_table(int* count) {
     static const KernelEntry table[] = {
-        // large M: 256x256 tiles, 8 waves (4 along M x 2 along N), 2-slice ring
+        // dense, prefill: 256x256 tiles, 8 waves (4 along M x 2 along N), 2-slice ring
         FP8GEMM_ENTRY(256, 256, 4, 2, 2, kDense),
-        // medium tiles
+        // dense, medium
         FP8GEMM_ENTRY(128, 128, 2, 2, 4, kDense),
         FP8GEMM_ENTRY(128, 256, 2, 4, 2, kDense),
-        // decode (M <= 128): all rows in one tile, narrow N tiles, deep ring
-        FP8GEMM_ENTRY(64, 64, 1, 4, 8, kDense),
-        FP8GEMM_ENTRY(128, 64, 1, 4, 6, kDense),
-        FP8GEMM_ENTRY(64, 32, 1, 2, 8, kDense),
+        // dense, decode: all rows of A in one tile, narrow N tiles
+        FP8GEMM_ENTRY(64, 64, 1, 4, 4, kDense),
+        FP8GEMM_ENTRY(64, 128, 1, 4, 3, kDense),
+        FP8GEMM_ENTRY(128, 128, 2, 4, 3, kDense),
         // contiguous grouped: tiles never cross a 128-row block
         FP8GEMM_ENTRY(128, 256, 2, 4, 2, kContiguous),
         FP8GEMM_ENTRY(128, 128, 2, 2, 4, kContiguous),
-        FP8GEMM_ENTRY(64, 64, 1, 4, 8, kContiguous),
+        FP8GEMM_ENTRY(128, 128, 2, 4, 3, kContiguous),
+        FP8GEMM_ENTRY(64, 64, 1, 4, 4, kContiguous),
+        FP8GEMM_ENTRY(64, 128, 1, 4, 3, kContiguous),
         // masked grouped
-        FP8GEMM_ENTRY(64, 64, 1, 4, 8, kMasked),
-        FP8GEMM_ENTRY(128, 64, 1, 4, 6, kMasked),
+        FP8GEMM_ENTRY(64, 64, 1, 4, 4, kMasked),
+        FP8GEMM_ENTRY(64, 128, 1, 4, 3, kMasked),
+        FP8GEMM_ENTRY(128, 128, 2, 4, 3, kMasked),
         FP8GEMM_ENTRY(128, 128, 2, 2, 4, kMasked),
-        FP8GEMM_ENTRY(64, 32, 1, 2, 8, kMasked),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

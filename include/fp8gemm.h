@@ -16,10 +16,13 @@
  *
  * Conventions for every GEMM entry point:
  *   - All matrix and scale pointers are DEVICE pointers; the caller owns every buffer.
- *   - All arrays are dense row-major with the last index contiguous:
- *       A  [rows][K] uint8 codes      sa [rows][K/128] float
- *       B  [(G)][N][K] uint8 codes    sb [(G)][ceil(N/128)][K/128] float
- *       D  [rows][N] bfloat16 (uint16 bit patterns)
+ *   - All arrays are dense with the last index contiguous:
+ *       A  [rows][K] uint8 codes      sa [(G)][K/128][rows] float  (K-block-major: the scales of
+ *       B  [(G)][N][K] uint8 codes        one 128-wide K block for consecutive rows are adjacent)
+ *       D  [rows][N] bfloat16         sb [(G)][ceil(N/128)][K/128] float
+ *     sa[kb][m] is the scale of A[m][128kb .. 128kb+127].  The pages fix no scale layout; this
+ *     one lets one K block's scales for a whole tile arrive as one contiguous run (the reference
+ *     library likewise asks for a specially aligned layout of its left-hand scales).
  *   - K must be a positive multiple of 128; M, N may be any non-negative size (N tails are
  *     masked).  A, B and D must be 16-byte aligned; sa, sb and the index vectors 4-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls are asynchronous:
@@ -55,7 +58,7 @@ typedef enum fp8gemm_status {
 } fp8gemm_status;
 
 /* Dense NT GEMM, gemm_fp8_fp8_bf16_nt (page "DeepSeek開源第三彈…", section 如何使用？).
- *   A [M][K] e4m3, sa [M][K/128], B [N][K] e4m3, sb [ceil(N/128)][K/128], D [M][N] bf16.
+ *   A [M][K] e4m3, sa [K/128][M], B [N][K] e4m3, sb [ceil(N/128)][K/128], D [M][N] bf16.
  *   M == 0 or N == 0 is a valid no-op. */
 int fp8gemm_nt(const void* A, const float* sa, const void* B, const float* sb, void* D,
                int64_t M, int64_t N, int64_t K, void* stream);
@@ -63,7 +66,7 @@ int fp8gemm_nt(const void* A, const float* sa, const void* B, const float* sb, v
 /* M-grouped GEMM, contiguous layout, m_grouped_gemm_fp8_fp8_bf16_nt_contiguous (same page and
  * section; page "DeepGEMM：AI計算の経済性を…", section DeepGEMMが重要な理由: token sequences are
  * grouped per expert).  The rows of all groups are concatenated along M:
- *   A [M_total][K], sa [M_total][K/128], B [G][N][K], sb [G][ceil(N/128)][K/128],
+ *   A [M_total][K], sa [K/128][M_total], B [G][N][K], sb [G][ceil(N/128)][K/128],
  *   m_indices [M_total] int32 (device): row r is multiplied by B[m_indices[r]];
  *   m_indices[r] == -1 marks a padding row, whose D row is left untouched.
  *   D [M_total][N].
@@ -78,7 +81,7 @@ int fp8gemm_grouped_contiguous(const void* A, const float* sa, const void* B, co
 /* M-grouped GEMM, masked layout, m_grouped_gemm_fp8_fp8_bf16_nt_masked (same page and section;
  * page "DeepGEMM：AI計算の経済性を…", section DeepGEMMが重要な理由: sparse expert activation).
  * Every group owns a fixed block of M_max rows:
- *   A [G][M_max][K], sa [G][M_max][K/128], B [G][N][K], sb [G][ceil(N/128)][K/128],
+ *   A [G][M_max][K], sa [G][K/128][M_max], B [G][N][K], sb [G][ceil(N/128)][K/128],
  *   masked_m [G] int32 (device): rows r < masked_m[g] of group g are valid; D rows at or past it
  *   are left untouched.  A count above M_max is clamped to M_max and flags
  *   FP8GEMM_DEVERR_BAD_COUNT; a negative count is taken as 0 and flags it too.

@@ -33,8 +33,13 @@ def dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
+def dev_sa(sa):
+    """Scales of A as the library takes them: K-block-major ([.., K/128, rows])."""
+    return dev(np.swapaxes(sa, -1, -2))
+
+
 def run_dense(d, out=None):
-    D = fg.gemm_nt(dev(d.A), dev(d.sa), dev(d.B), dev(d.sb), out=out)
+    D = fg.gemm_nt(dev(d.A), dev_sa(d.sa), dev(d.B), dev(d.sb), out=out)
     torch.cuda.synchronize()
     return D
 
@@ -171,7 +176,7 @@ def test_cu_cap_and_side_stream():
     assert "grid=" in cfg and int(cfg.split("grid=")[1]) <= 24
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        D2 = fg.gemm_nt(dev(d.A), dev(d.sa), dev(d.B), dev(d.sb))
+        D2 = fg.gemm_nt(dev(d.A), dev_sa(d.sa), dev(d.B), dev(d.sb))
     s.synchronize()
     assert np.array_equal(gpu_bits(D2), ref)
 
@@ -181,7 +186,7 @@ def test_cu_cap_and_side_stream():
 # ------------------------------------------------------------------------------------------
 
 def run_contig(c, out=None):
-    D = fg.grouped_contiguous(dev(c.A), dev(c.sa), dev(c.B), dev(c.sb), dev(c.m_indices), out=out)
+    D = fg.grouped_contiguous(dev(c.A), dev_sa(c.sa), dev(c.B), dev(c.sb), dev(c.m_indices), out=out)
     torch.cuda.synchronize()
     return D
 
@@ -240,7 +245,7 @@ def test_contiguous_bad_index_flags_and_is_padding():
     mi[5] = 7           # out of range
     mi[200] = 0         # a group-0 row inside group 1's block
     out = sentinel_tensor(c.A.shape[:1] + (128,))
-    D = fg.grouped_contiguous(dev(c.A), dev(c.sa), dev(c.B), dev(c.sb), dev(mi), out=out)
+    D = fg.grouped_contiguous(dev(c.A), dev_sa(c.sa), dev(c.B), dev(c.sb), dev(mi), out=out)
     err = fg.read_device_error()
     assert err & fg.DEVERR_BAD_INDEX
     got = gpu_bits(D)
@@ -257,7 +262,7 @@ def test_contiguous_bad_index_flags_and_is_padding():
 # ------------------------------------------------------------------------------------------
 
 def run_masked(w, expected_m, out=None):
-    D = fg.grouped_masked(dev(w.A), dev(w.sa), dev(w.B), dev(w.sb), dev(w.masked_m), expected_m, out=out)
+    D = fg.grouped_masked(dev(w.A), dev_sa(w.sa), dev(w.B), dev(w.sb), dev(w.masked_m), expected_m, out=out)
     torch.cuda.synchronize()
     return D
 
@@ -299,7 +304,7 @@ def test_every_masked_kernel_config(entry, split):
 def test_masked_count_out_of_range_clamps_and_flags():
     w = W.masked(np.array([64, 10], np.int32), 64, 128, 256, seed=93)
     mm = np.array([1000, -5], np.int32)
-    D = fg.grouped_masked(dev(w.A), dev(w.sa), dev(w.B), dev(w.sb), dev(mm), 64,
+    D = fg.grouped_masked(dev(w.A), dev_sa(w.sa), dev(w.B), dev(w.sb), dev(mm), 64,
                           out=sentinel_tensor((2, 64, 128)))
     assert fg.read_device_error() & fg.DEVERR_BAD_COUNT
     ref, valid = oracle.grouped_masked(w.A, w.sa, w.B, w.sb, mm)
