@@ -4,13 +4,23 @@ One step = the dense decode/prefill sweep over DeepSeek-V3-like projection shape
 {64, 128, 4096} x (N, K) in {(2112,7168), (24576,1536), (32768,512), (7168,16384), (4096,7168),
 (7168,2048)} -- 18 GEMMs, each D[M,N] bf16 = A[M,K] e4m3 (1x128 fp32 scales) . B[N,K]^T e4m3
 (128x128 fp32 scales).  Inputs are synthetic, seeded, quantised from N(0,1) and resident in HBM
-before timing; consecutive GEMMs use different buffers (about 1.3 GB per step), so each GEMM's
-operands are not left in the 256 MB last-level cache by the previous one.
+before timing.
 
-Prints ONE JSON line: value = aggregate FP8 TFLOP/s of the sweep (total flop / total time),
-per-shape TFLOP/s and GB/s with their roofline fractions, the roofline of the dominant kernel
-measured with HIP events on the launch stream, the grouped (MoE) configurations, and the CPU
-oracle timed on a bounded sample on the host's cores.
+Launch path: each step's 18 library calls are captured once into a HIP graph (the library
+allocates nothing per call, so capture is safe once each stream's workspace exists) and the
+graph is replayed; R copies of every operand set rotate between steps and between the launches
+of the per-shape graphs, so no GEMM finds its operands in the 256 MB last-level cache.
+Graph outputs are checked bit for bit against eager calls before timing.
+
+Prints ONE JSON line:
+  value        aggregate FP8 TFLOP/s of the sweep = flop per step / wall-clock time per step
+               (K graph replays between two device synchronisations)
+  per_shape    per GEMM: average launch time from HIP events around per-shape graphs of R
+               launches (on the launch stream), TFLOP/s, GB/s and roofline fractions
+  roofline     the dominant kernel (largest share of the step's time): algorithmic flop per
+               launch / average launch time, against the 5.0 PFLOP/s dense FP8 peak
+  grouped      the contiguous and masked MoE configurations (context, not part of value)
+  cpu_baseline the CPU oracle on a bounded sample of the same workload on this host's cores
 """
 from __future__ import annotations
 
@@ -27,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA (AMD published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (AMD published)
+COPIES = 4                     # rotated operand copies
 
 
 def log(*a):
@@ -60,97 +71,146 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fg.init()
+    stream = torch.cuda.Stream(dev)
 
-    # ---- inputs: all 18 sweep cases resident on the device -----------------------------------
+    # ---- inputs: all 18 sweep cases resident on the device, COPIES copies each -----------------
     t0 = time.time()
     cases = []
-    b_cache = {}
+    b_host = {}
     for nki, (N, K) in enumerate(W.SWEEP_NK):
-        for mi, M in enumerate(W.SWEEP_M):
-            a_seed, b_seed = W.sweep_seeds(mi, nki)
-            if nki not in b_cache:
-                rng_b = np.random.default_rng(b_seed)
-                Bq, sbq = W.quantize_128x128(W.normal(rng_b, (N, K)))
-                b_cache[nki] = (torch.from_numpy(Bq).to(dev), torch.from_numpy(sbq).to(dev), Bq, sbq)
-            Bd, sbd, Bq, sbq = b_cache[nki]
-            Aq, saq = W._acts(np.random.default_rng(a_seed), M, K)
-            cases.append(dict(M=M, N=N, K=K, A=torch.from_numpy(Aq).to(dev),
-                              sa=torch.from_numpy(np.ascontiguousarray(saq.T)).to(dev),
-                              B=Bd, sb=sbd, D=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
-                              hostA=Aq, hostsa=saq, hostB=Bq, hostsb=sbq))
-    # interleave M values so that no two consecutive GEMMs share a weight matrix
-    order = sorted(range(len(cases)), key=lambda i: (W.SWEEP_M.index(cases[i]["M"]), i))
-    cases = [cases[i] for i in order]
+        a_seed, b_seed = W.sweep_seeds(0, nki)
+        rng_b = np.random.default_rng(b_seed)
+        b_host[nki] = W.quantize_128x128(W.normal(rng_b, (N, K)))
+    for mi, M in enumerate(W.SWEEP_M):          # M outer: consecutive GEMMs use other weights
+        for nki, (N, K) in enumerate(W.SWEEP_NK):
+            a_seed, _ = W.sweep_seeds(mi, nki)
+            Aq, saq = W.acts(np.random.default_rng(a_seed), M, K)
+            Bq, sbq = b_host[nki]
+            base = dict(A=torch.from_numpy(Aq).to(dev),
+                        sa=torch.from_numpy(np.ascontiguousarray(saq.T)).to(dev),   # [K/128, M]
+                        B=torch.from_numpy(Bq).to(dev), sb=torch.from_numpy(sbq).to(dev))
+            copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(COPIES - 1)]
+            for c in copies:
+                c["D"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            cases.append(dict(M=M, N=N, K=K, copies=copies, hostA=Aq, hostsa=saq, hostB=Bq, hostsb=sbq))
     log("inputs ready in %.1f s" % (time.time() - t0))
 
-    stream = torch.cuda.current_stream(dev)
-
-    def run_case(c):
+    def call(case, r):
+        c = case["copies"][r]
         fg.gemm_nt(c["A"], c["sa"], c["B"], c["sb"], out=c["D"], stream=stream)
 
+    # ---- eager reference outputs and launch configurations ------------------------------------
     configs = []
-    for c in cases:
-        run_case(c)
-        configs.append(fg.last_config())
-    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for case in cases:
+            for r in range(COPIES):
+                call(case, r)
+            configs.append(fg.last_config())
+    stream.synchronize()
+    eager = [[c["D"].clone() for c in case["copies"]] for case in cases]
 
-    for _ in range(args.warmup):
-        for c in cases:
-            run_case(c)
-    torch.cuda.synchronize()
+    # ---- graphs: one per step copy, one per shape (COPIES launches) --------------------------
+    step_graphs = []
+    for r in range(COPIES):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for case in cases:
+                call(case, r)
+        step_graphs.append(g)
+    shape_graphs = []
+    for case in cases:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(COPIES):
+                call(case, r)
+        shape_graphs.append(g)
 
-    # ---- timed region: K steps, HIP events around every launch on the launch stream ----------
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in cases] for _ in range(args.steps)]
+    def replay(g):
+        with torch.cuda.stream(stream):
+            g.replay()
+
+    # graph replays must reproduce the eager outputs bit for bit
+    for case in cases:
+        for c in case["copies"]:
+            c["D"].zero_()
+    for r in range(COPIES):
+        replay(step_graphs[r])
+    stream.synchronize()
+    for i, case in enumerate(cases):
+        for r in range(COPIES):
+            if not torch.equal(case["copies"][r]["D"], eager[i][r]):
+                raise RuntimeError("graph replay differs from eager output (case %d copy %d)" % (i, r))
+
+    flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)    # 1 GiB, read only
+    sink = torch.zeros(1, device=dev)
+
+    def read_flush():
+        with torch.cuda.stream(stream):
+            sink.add_(flush.sum())
+
+    # ---- timed region: K steps --------------------------------------------------------------
+    for s in range(args.warmup):
+        replay(step_graphs[s % COPIES])
+    stream.synchronize()
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    e_start.record(stream)
     for s in range(args.steps):
-        for i, c in enumerate(cases):
-            ev[s][i][0].record(stream)
-            run_case(c)
-            ev[s][i][1].record(stream)
+        replay(step_graphs[s % COPIES])
+    e_end.record(stream)
+    stream.synchronize()
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
     ms_per_step = 1e3 * t_total / args.steps
+    gpu_ms_per_step = e_start.elapsed_time(e_end) / args.steps
 
+    # ---- per-shape launch times: HIP events around per-shape graphs on the launch stream -------
+    reps = 5
     per = []
     total_flop = 0
-    kern_time = {}
-    kern_flop = {}
-    kern_bytes = {}
-    for i, c in enumerate(cases):
-        ms = float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
-        flop, byts = W.dense_work(c["M"], c["N"], c["K"])
+    kern_time, kern_flop, kern_launch = {}, {}, {}
+    for i, case in enumerate(cases):
+        ts = []
+        for _ in range(reps):
+            read_flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            replay(shape_graphs[i])
+            e1.record(stream)
+            stream.synchronize()
+            ts.append(e0.elapsed_time(e1) / COPIES)
+        ms = float(np.mean(ts))
+        flop, byts = W.dense_work(case["M"], case["N"], case["K"])
         total_flop += flop
         tf = flop / (ms * 1e-3) / 1e12
         gbs = byts / (ms * 1e-3) / 1e9
         kname = configs[i].split(" split=")[0]
         kern_time[kname] = kern_time.get(kname, 0.0) + ms
         kern_flop[kname] = kern_flop.get(kname, 0) + flop
-        kern_bytes[kname] = kern_bytes.get(kname, 0) + byts
-        ai = flop / byts
-        bound = "mfma" if ai * PEAK_HBM_GBS * 1e9 > PEAK_FP8_TFLOPS * 1e12 else "hbm"
-        per.append(dict(M=c["M"], N=c["N"], K=c["K"], us=round(ms * 1e3, 2), tflops=round(tf, 1),
+        kern_launch[kname] = kern_launch.get(kname, 0) + 1
+        bound = "mfma" if flop / byts * PEAK_HBM_GBS * 1e9 > PEAK_FP8_TFLOPS * 1e12 else "hbm"
+        per.append(dict(M=case["M"], N=case["N"], K=case["K"], us=round(ms * 1e3, 2), tflops=round(tf, 1),
                         gbs=round(gbs, 1), frac_mfma=round(tf / PEAK_FP8_TFLOPS, 4),
                         frac_hbm=round(gbs / PEAK_HBM_GBS, 4), roof=bound, config=configs[i]))
-    sum_kernel_ms = sum(p["us"] for p in per) / 1e3
-    value = total_flop / (sum_kernel_ms * 1e-3) / 1e12
+    value = total_flop / (ms_per_step * 1e-3) / 1e12
 
     dom = max(kern_time, key=kern_time.get)
-    dom_launches = sum(1 for i in range(len(cases)) if configs[i].split(" split=")[0] == dom)
-    dom_avg_us = kern_time[dom] / dom_launches * 1e3
     ach = kern_flop[dom] / (kern_time[dom] * 1e-3) / 1e12
     roofline = dict(bound="mfma", achieved=round(ach, 1), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
                     frac=round(ach / PEAK_FP8_TFLOPS, 4), traffic=None, kernel=dom,
-                    launches_per_step=dom_launches, avg_launch_us=round(dom_avg_us, 2),
-                    flop_per_launch=kern_flop[dom] // dom_launches)
+                    launches_per_step=kern_launch[dom],
+                    avg_launch_us=round(kern_time[dom] / kern_launch[dom] * 1e3, 2),
+                    flop_per_launch=kern_flop[dom] // kern_launch[dom],
+                    share_of_step=round(kern_time[dom] / sum(kern_time.values()), 3))
 
-    # ---- grouped (MoE) configurations ----------------------------------------------------------
     grouped = {}
     if not args.no_grouped:
+        del flush
         grouped = bench_grouped(fg, W, torch, dev, stream)
 
-    # ---- CPU oracle on a bounded sample of the same workload ----------------------------------
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cases, args.cpu_seconds)
@@ -172,7 +232,8 @@ def main():
                                "{(2112,7168),(24576,1536),(32768,512),(7168,16384),(4096,7168),(7168,2048)}, "
                                "18 GEMMs per step, bf16 out",
                    "gemms_per_step": len(cases), "flop_per_step": total_flop,
-                   "kernel_ms_per_step": round(sum_kernel_ms, 4)},
+                   "gpu_ms_per_step": round(gpu_ms_per_step, 4), "launch": "hip graph replay",
+                   "operand_copies": COPIES},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_shape": per,
@@ -202,18 +263,26 @@ def bench_grouped(fg, W, torch, dev, stream, reps=10):
             call = lambda: fg.grouped_masked(A, sa, B, sb, mm, w.expected_m, out=D, stream=stream)
             counts = [int(x) for x in w.masked_m]
             flop, byts = W.grouped_work(counts, N, K, index_bytes=4 * len(counts))
-        call()
+        with torch.cuda.stream(stream):
+            call()
         cfg = fg.last_config()
-        for _ in range(3):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
             call()
-        torch.cuda.synchronize()
-        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for e0, e1 in es:
-            e0.record(stream)
-            call()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in es]))
+        flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+        sink = torch.zeros(1, device=dev)
+        ts = []
+        for _ in range(reps):
+            with torch.cuda.stream(stream):
+                sink.add_(flush.sum())
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+            stream.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.mean(ts))
         tf = flop / (ms * 1e-3) / 1e12
         gbs = byts / (ms * 1e-3) / 1e9
         out[name] = dict(us=round(ms * 1e3, 1), tflops=round(tf, 1), gbs=round(gbs, 1),
@@ -221,7 +290,7 @@ def bench_grouped(fg, W, torch, dev, stream, reps=10):
                          valid_rows=int(sum(counts)), config=cfg)
         log("%s: %.1f us, %.1f TFLOP/s, %.1f GB/s (%s) [inputs %.1f s]" % (name, ms * 1e3, tf, gbs, cfg,
                                                                             time.time() - t0))
-        del A, sa, B, sb, D
+        del A, sa, B, sb, D, flush, g
         torch.cuda.empty_cache()
     return out
 
@@ -234,10 +303,10 @@ def cpu_baseline(cases, target_s):
     nth = oracle.num_threads(0)
     probe = cases[0]
     t0 = time.perf_counter()
-    oracle.gemm_nt(probe["hostA"][:1], probe["hostsa"][:1], probe["hostB"], probe["hostsb"])
-    t_probe = time.perf_counter() - t0
+    oracle.gemm_nt(probe["hostA"][:4], probe["hostsa"][:4], probe["hostB"], probe["hostsb"])
+    t_probe = (time.perf_counter() - t0) / 4
     per_row_all = t_probe * sum(c["N"] * c["K"] for c in cases) / (probe["N"] * probe["K"])
-    rows = int(max(1, min(64, target_s / max(per_row_all, 1e-9))))
+    rows = int(max(1, min(512, target_s / max(per_row_all, 1e-9))))
     flop = 0
     t0 = time.perf_counter()
     for c in cases:
@@ -247,7 +316,7 @@ def cpu_baseline(cases, target_s):
     dt = time.perf_counter() - t0
     log("cpu oracle: %d rows of each case, %.1f GFLOP in %.1f s on %d threads" % (rows, flop / 1e9, dt, nth))
     return dict(value=round(flop / dt / 1e12, 6), unit="TFLOP/s", cores=nth, kind="oracle",
-                sample="first %d rows of each of the 18 sweep GEMMs (all N, all K), %.1f GFLOP, %.1f s"
+                sample="first %d rows (at most M) of each of the 18 sweep GEMMs, all N and K: %.1f GFLOP in %.1f s"
                        % (rows, flop / 1e9, dt))
 
 

@@ -109,23 +109,24 @@ int workspace(DeviceState* d, hipStream_t stream, size_t partial_bytes, size_t c
     return FP8GEMM_OK;
 }
 
-int find_entry(int layout, int bm, int bn, int wm, int wn, int stages) {
+int find_entry(int layout, int bm, int bn, int wm, int wn, int stages, int prefetch = 0) {
     int n = 0;
     const KernelEntry* tab = kernel_table(&n);
     for (int i = 0; i < n; ++i)
         if (tab[i].layout == layout && tab[i].bm == bm && tab[i].bn == bn && tab[i].waves_m == wm &&
-            tab[i].waves_n == wn && tab[i].stages == stages)
+            tab[i].waves_n == wn && tab[i].stages == stages && tab[i].prefetch == prefetch)
             return i;
     return -1;
 }
 
-// Optional override for experiments: FP8GEMM_FORCE_CONFIG=BMxBN:WMxWN:STAGES:SPLIT
+// Optional override for experiments: FP8GEMM_FORCE_CONFIG=BMxBN:WMxWN:STAGES:SPLIT[:PREFETCH]
 bool forced_config(int layout, int* idx, int* split) {
     const char* s = std::getenv("FP8GEMM_FORCE_CONFIG");
     if (!s || !*s) return false;
-    int bm, bn, wm, wn, st, sp;
-    if (std::sscanf(s, "%dx%d:%dx%d:%d:%d", &bm, &bn, &wm, &wn, &st, &sp) != 6) return false;
-    int i = find_entry(layout, bm, bn, wm, wn, st);
+    int bm, bn, wm, wn, st, sp, pf = 0;
+    int got = std::sscanf(s, "%dx%d:%dx%d:%d:%d:%d", &bm, &bn, &wm, &wn, &st, &sp, &pf);
+    if (got < 6) return false;
+    int i = find_entry(layout, bm, bn, wm, wn, st, pf);
     if (i < 0) return false;
     *idx = i;
     *split = std::max(1, sp);
@@ -137,10 +138,11 @@ struct Choice {
     int split;
 };
 
-// K splits so that tiles * splits is about one unit per CU, each split keeping >= 4 K slices.
+// K splits so that tiles * splits fills the CUs with at most one unit each (a second, partly
+// empty round of units would double the time), each split keeping >= 4 K slices.
 int pick_split(int64_t tiles, int nkb, int cus) {
     if (tiles >= cus) return 1;
-    int64_t s = (cus + tiles / 2) / tiles;
+    int64_t s = cus / tiles;
     s = std::min<int64_t>(s, std::max(1, nkb / 4));
     return (int)std::max<int64_t>(1, s);
 }
@@ -216,9 +218,9 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream)
     int64_t grid = std::min<int64_t>(a.units, slots);
     if (grid <= 0) return FP8GEMM_OK;
     std::snprintf(g_last_config, sizeof g_last_config,
-                  "%s tile=%dx%d waves=%dx%d stages=%d split=%d kb_per_split=%d units=%lld grid=%lld",
+                  "%s tile=%dx%d waves=%dx%d stages=%d prefetch=%d split=%d kb_per_split=%d units=%lld grid=%lld",
                   layout == kDense ? "nt" : (layout == kContiguous ? "contiguous" : "masked"), e.bm,
-                  e.bn, e.waves_m, e.waves_n, e.stages, a.splits, a.kb_per_split,
+                  e.bn, e.waves_m, e.waves_n, e.stages, e.prefetch, a.splits, a.kb_per_split,
                   (long long)a.units, (long long)grid);
     if (std::getenv("FP8GEMM_LOG")) std::fprintf(stderr, "[fp8gemm] %s\n", g_last_config);
     e.launch(dim3((unsigned)grid), a, stream);

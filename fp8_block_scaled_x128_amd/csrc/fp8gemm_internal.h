@@ -35,6 +35,7 @@ struct KernelEntry {
     const char* name;
     int layout;
     int bm, bn, waves_m, waves_n, stages;
+    int prefetch;               // L2 prefetch distance in K slices (0 = none)
     int threads;
     bool splitk;                // compiled with the split-K partial reduction
     int lds_bytes;

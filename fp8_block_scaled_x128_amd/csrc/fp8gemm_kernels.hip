@@ -64,14 +64,15 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-// Wait until at most `per * k` of this wave's DMA loads are in flight, 0 <= k <= KMAX.
-template <int PER, int KMAX>
+// Wait until at most `extra + per * k` of this wave's DMA loads are in flight, 0 <= k <= KMAX
+// (loads complete in issue order, so everything older than those is done).
+template <int PER, int KMAX, int EXTRA>
 __device__ __forceinline__ void wait_slices(int k) {
     if constexpr (KMAX == 0) {
-        wait_vmcnt<0>();
+        wait_vmcnt<EXTRA>();
     } else {
-        if (k >= KMAX) wait_vmcnt<PER * KMAX>();
-        else wait_slices<PER, KMAX - 1>(k);
+        if (k >= KMAX) wait_vmcnt<EXTRA + PER * KMAX>();
+        else wait_slices<PER, KMAX - 1, EXTRA>(k);
     }
 }
 
@@ -125,7 +126,7 @@ __device__ __forceinline__ int wave_min(int v) {
 // the kernel
 // ------------------------------------------------------------------------------------------
 
-template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT>
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PFD>
 struct Tile {
     static constexpr int NW = WMW * WNW;            // waves per workgroup
     static constexpr int NT = 64 * NW;
@@ -141,12 +142,17 @@ struct Tile {
     static constexpr int SA_OFF = (BN + BM) * 128;
     static constexpr int SB_OFF = SA_OFF + BM * 4;
     static constexpr int STAGE_BYTES = SB_OFF + 256;
-    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    // L2 prefetch: PFD > 0 adds, per slice, one x1 gather per 64 tile rows that touches the
+    // cache line of every A and B row of slice i + PFD (data lands in a scratch LDS word)
+    static constexpr int PF_PER = PFD > 0 ? (BM + BN) / (64 * NW) : 0;
+    static_assert(PFD == 0 || (BM + BN) % (64 * NW) == 0, "prefetch rows split evenly over waves");
+    static constexpr int STAGES_BYTES_END = STAGES * STAGE_BYTES;
+    static constexpr int LDS_BYTES = STAGES_BYTES_END + (PFD > 0 ? 256 : 0);
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static constexpr int B_DMA = BN / (8 * NW);     // x4 loads per wave per slice for B
     static constexpr int A_DMA = BM / (8 * NW);
     static constexpr int AUX = (BM / 64 + 1 + NW - 1) / NW;  // x1 loads per wave: sa chunks + sb
-    static constexpr int NDMA = B_DMA + A_DMA + AUX;
+    static constexpr int NDMA = B_DMA + A_DMA + AUX + PF_PER;   // loads per wave per slice
     static_assert(NDMA * (STAGES - 1) < 64, "vmcnt range");
     // every wave's N range lies inside one 128-row block of B scales
     static constexpr bool NB_UNIFORM = (BN % 128 == 0) && (128 % WN == 0);
@@ -154,9 +160,9 @@ struct Tile {
     static constexpr bool SPLITK = BM * BN <= 128 * 256;
 };
 
-template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT>
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PFD>
 __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArgs args) {
-    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT>;
+    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT, PFD>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
     __shared__ int s_flag;
 
@@ -296,6 +302,14 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
                 aux_off[t] = (uint32_t)nb * (uint32_t)nkb * 4u;
             }
         }
+        uint32_t pf_off[T::PF_PER > 0 ? T::PF_PER : 1];
+#pragma unroll
+        for (int t = 0; t < T::PF_PER; ++t) {
+            const int chunk = wave * T::PF_PER + t;
+            const int r = 64 * chunk + lane;
+            if (chunk < BM / 64) pf_off[t] = (uint32_t)min(r, row_limit - 1) * (uint32_t)K;
+            else pf_off[t] = (uint32_t)min(r - BM, N - 1 - n0) * (uint32_t)K;
+        }
         const uint8_t* Bt = uniform_ptr(Bg + (int64_t)n0 * K + (int64_t)kb0 * 128);  // slice-0 bases
         const uint8_t* At = uniform_ptr(Ag + (int64_t)kb0 * 128);
         const float* sat = uniform_ptr(sag + (int64_t)kb0 * args.rows);
@@ -317,6 +331,19 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
                 if (x < BM / 64) dma_x1(st + T::SA_OFF + 256 * x, uniform_ptr(sat + (int64_t)i * args.rows), aux_off[t]);
                 else dma_x1(st + T::SB_OFF, uniform_ptr(sbt + i), aux_off[t]);
             }
+            if constexpr (T::PF_PER > 0) {
+                // issued after this slice's own loads: it may complete one slice later without
+                // delaying them; clamped so that every slice issues the same number of loads
+                const int j = min(i + PFD, nks - 1);
+#pragma unroll
+                for (int t = 0; t < T::PF_PER; ++t) {
+                    const int chunk = wave * T::PF_PER + t;            // 64 rows of [A rows | B rows]
+                    if (chunk < BM / 64)
+                        dma_x1(smem_base + T::STAGES_BYTES_END, uniform_ptr(At + (int64_t)j * 128), pf_off[t]);
+                    else
+                        dma_x1(smem_base + T::STAGES_BYTES_END, uniform_ptr(Bt + (int64_t)j * 128), pf_off[t]);
+                }
+            }
         };
 
         // ---- accumulators -------------------------------------------------------------------
@@ -334,7 +361,8 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
         // ---- main loop over 128-wide K slices -----------------------------------------------
         for (int i = 0; i < nks; ++i) {
             // slice i landed (this wave's loads), then every wave's loads
-            wait_slices<T::NDMA, STAGES - 2>(min(STAGES - 2, nks - 1 - i));
+            // (slice i's own prefetch, issued after its tile loads, may still be in flight)
+            wait_slices<T::NDMA, STAGES - 2, T::PF_PER>(min(STAGES - 2, nks - 1 - i));
             __syncthreads();
             if (i + STAGES - 1 < nks) issue_slice(i + STAGES - 1);
 
@@ -501,15 +529,15 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
 // instantiation table
 // ------------------------------------------------------------------------------------------
 
-template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT>
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PFD>
 static void launch_impl(dim3 grid, const KernelArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT>), grid,
+    hipLaunchKernelGGL((fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT, PFD>), grid,
                        dim3(WMW * WNW * 64), 0, s, a);
 }
 
-template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT>
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PFD>
 static KernelEntry entry(const char* name) {
-    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT>;
+    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT, PFD>;
     KernelEntry e;
     e.name = name;
     e.layout = LAYOUT;
@@ -521,18 +549,24 @@ static KernelEntry entry(const char* name) {
     e.threads = T::NT;
     e.splitk = T::SPLITK;
     e.lds_bytes = T::LDS_BYTES;
-    e.func = reinterpret_cast<const void*>(&fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT>);
-    e.launch = &launch_impl<BM, BN, WMW, WNW, STAGES, LAYOUT>;
+    e.prefetch = PFD;
+    e.func = reinterpret_cast<const void*>(&fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT, PFD>);
+    e.launch = &launch_impl<BM, BN, WMW, WNW, STAGES, LAYOUT, PFD>;
     return e;
 }
 
 #define FP8GEMM_ENTRY(BM, BN, WMW, WNW, ST, L) \
-    entry<BM, BN, WMW, WNW, ST, L>(#L " " #BM "x" #BN " waves " #WMW "x" #WNW " stages " #ST)
+    entry<BM, BN, WMW, WNW, ST, L, 0>(#L " " #BM "x" #BN " waves " #WMW "x" #WNW " stages " #ST)
+#define FP8GEMM_ENTRY_PF(BM, BN, WMW, WNW, ST, L, PFD) \
+    entry<BM, BN, WMW, WNW, ST, L, PFD>(#L " " #BM "x" #BN " waves " #WMW "x" #WNW " stages " #ST " prefetch " #PFD)
 
 const KernelEntry* kernel_table(int* count) {
     static const KernelEntry table[] = {
         // dense, prefill: 256x256 tiles, 8 waves (4 along M x 2 along N), 2-slice ring
         FP8GEMM_ENTRY(256, 256, 4, 2, 2, kDense),
+        FP8GEMM_ENTRY_PF(256, 256, 4, 2, 2, kDense, 2),
+        FP8GEMM_ENTRY_PF(256, 256, 4, 2, 2, kDense, 3),
+        FP8GEMM_ENTRY_PF(256, 256, 4, 2, 2, kDense, 5),
         // dense, medium
         FP8GEMM_ENTRY(128, 128, 2, 2, 4, kDense),
         FP8GEMM_ENTRY(128, 256, 2, 4, 2, kDense),

@@ -136,7 +136,8 @@ def _weights(rng, N, K):
     return quantize_128x128(normal(rng, (N, K)))
 
 
-def _acts(rng, M, K, chunk_rows=4096):
+def acts(rng, M, K, chunk_rows=4096):
+    """A operand: N(0,1) rows quantised per 1x128 block -> (codes [M,K], scales [M, K/128])."""
     nkb = -(-K // BLOCK)
     codes = np.empty((M, K), dtype=np.uint8)
     scales = np.empty((M, nkb), dtype=np.float32)
@@ -156,7 +157,7 @@ def dense(M: int, N: int, K: int, seed: int, seed_b: int | None = None) -> Dense
     rng_b = np.random.default_rng(seed if seed_b is None else seed_b)
     rng_a = np.random.default_rng(seed) if seed_b is not None else rng_b
     B, sb = _weights(rng_b, N, K)
-    A, sa = _acts(rng_a, M, K)
+    A, sa = acts(rng_a, M, K)
     return Dense(A, sa, B, sb)
 
 
@@ -191,7 +192,7 @@ def contiguous(counts, slot: int, N: int, K: int, seed: int, packed: bool = Fals
         b, s = _weights(rng, N, K)
         Bs.append(b)
         sbs.append(s)
-    A, sa = _acts(rng, M, K)
+    A, sa = acts(rng, M, K)
     return Contiguous(A, sa, np.stack(Bs), np.stack(sbs), m_idx, list(counts))
 
 
@@ -211,7 +212,7 @@ def masked(masked_m, M_max: int, N: int, K: int, seed: int, expected_m: int = 0)
     for g in range(G):
         c = int(min(max(masked_m[g], 0), M_max))
         if c:
-            A[g, :c], sa[g, :c] = _acts(rng, c, K)
+            A[g, :c], sa[g, :c] = acts(rng, c, K)
         if c < M_max:
             A[g, c:] = random_codes(rng, (M_max - c, K))
             sa[g, c:] = np.exp(rng.standard_normal((M_max - c, nkb))).astype(np.float32) * 0.01
