@@ -109,17 +109,17 @@ int workspace(DeviceState* d, hipStream_t stream, size_t partial_bytes, size_t c
     return FP8GEMM_OK;
 }
 
-int find_entry(int layout, int bm, int bn, int wm, int wn, int stages, int prefetch = 0) {
+int find_entry(int layout, int bm, int bn, int wm, int wn, int stages, int pipe = 0) {
     int n = 0;
     const KernelEntry* tab = kernel_table(&n);
     for (int i = 0; i < n; ++i)
         if (tab[i].layout == layout && tab[i].bm == bm && tab[i].bn == bn && tab[i].waves_m == wm &&
-            tab[i].waves_n == wn && tab[i].stages == stages && tab[i].prefetch == prefetch)
+            tab[i].waves_n == wn && tab[i].stages == stages && tab[i].pipe == pipe)
             return i;
     return -1;
 }
 
-// Optional override for experiments: FP8GEMM_FORCE_CONFIG=BMxBN:WMxWN:STAGES:SPLIT[:PREFETCH]
+// Optional override for experiments: FP8GEMM_FORCE_CONFIG=BMxBN:WMxWN:STAGES:SPLIT[:PIPE]
 bool forced_config(int layout, int* idx, int* split) {
     const char* s = std::getenv("FP8GEMM_FORCE_CONFIG");
     if (!s || !*s) return false;
@@ -201,13 +201,23 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream)
     a.kb_per_split = (a.nkb + split - 1) / split;
     a.splits = (a.nkb + a.kb_per_split - 1) / a.kb_per_split;
     const int64_t groups = (layout == kMasked) ? a.G : 1;
-    a.units = groups * a.tiles_m * a.tiles_n * a.splits;
+    const int64_t units = groups * a.tiles_m * a.tiles_n * a.splits;
+    if (units >= (int64_t(1) << 30)) return FP8GEMM_ERR_UNSUPPORTED;   // unit ids stay far below 2^31
+    a.units = (int32_t)units;
     a.group_m = (layout != kMasked && a.tiles_m >= 8) ? (layout == kDense ? 4 : 8) : 1;
+    a.div_splits = make_fastdiv((uint32_t)a.splits);
+    a.div_tiles_m = make_fastdiv((uint32_t)a.tiles_m);
+    a.div_tiles_n = make_fastdiv((uint32_t)a.tiles_n);
+    a.div_group_tiles = make_fastdiv((uint32_t)(a.tiles_m * a.tiles_n));
+    a.div_band_units = make_fastdiv((uint32_t)(a.group_m * a.tiles_n));
+    a.div_band_h = make_fastdiv((uint32_t)a.group_m);
+    const int bands = (a.tiles_m + a.group_m - 1) / a.group_m;
+    a.div_band_h_last = make_fastdiv((uint32_t)(a.tiles_m - a.group_m * (bands - 1)));
     a.err = d->err;
     a.ws = nullptr;
     a.counters = nullptr;
     if (a.splits > 1) {
-        const int64_t tiles = a.units / a.splits;
+        const int64_t tiles = (int64_t)a.units / a.splits;
         Workspace* w = nullptr;
         st = workspace(d, stream, (size_t)a.units * e.bm * e.bn * sizeof(float), (size_t)tiles, &w);
         if (st != FP8GEMM_OK) return st;
@@ -218,9 +228,9 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream)
     int64_t grid = std::min<int64_t>(a.units, slots);
     if (grid <= 0) return FP8GEMM_OK;
     std::snprintf(g_last_config, sizeof g_last_config,
-                  "%s tile=%dx%d waves=%dx%d stages=%d prefetch=%d split=%d kb_per_split=%d units=%lld grid=%lld",
+                  "%s tile=%dx%d waves=%dx%d stages=%d pipe=%d split=%d kb_per_split=%d units=%lld grid=%lld",
                   layout == kDense ? "nt" : (layout == kContiguous ? "contiguous" : "masked"), e.bm,
-                  e.bn, e.waves_m, e.waves_n, e.stages, e.prefetch, a.splits, a.kb_per_split,
+                  e.bn, e.waves_m, e.waves_n, e.stages, e.pipe, a.splits, a.kb_per_split,
                   (long long)a.units, (long long)grid);
     if (std::getenv("FP8GEMM_LOG")) std::fprintf(stderr, "[fp8gemm] %s\n", g_last_config);
     e.launch(dim3((unsigned)grid), a, stream);

@@ -10,6 +10,33 @@ enum Layout { kDense = 0, kContiguous = 1, kMasked = 2 };
 
 enum DevErr { kDevErrBadIndex = 1, kDevErrBadCount = 2 };
 
+// Unsigned division by a launch constant d >= 1 as multiply-high, add and shift (the round-up
+// reciprocal method of Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994), exact for dividends below 2^31.  Built on the host; on the device the
+// fields are kernel arguments, so the division runs on the scalar unit.
+struct FastDiv {
+    uint32_t d;       // divisor
+    uint32_t mul;     // floor(2^32 * (2^shift - d) / d) + 1
+    uint32_t shift;   // ceil(log2(d))
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    if (d == 0) d = 1;  // empty dimensions launch nothing; keep the fields well defined
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    const uint64_t mul = (((1ull << 32) * ((1ull << s) - d)) / d) + 1;
+    return FastDiv{d, (uint32_t)mul, s};
+}
+
+__host__ __device__ inline uint32_t fast_div(uint32_t n, const FastDiv& f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t hi = __umulhi(n, f.mul);
+#else
+    const uint32_t hi = (uint32_t)(((uint64_t)n * f.mul) >> 32);
+#endif
+    return (hi + n) >> f.shift;
+}
+
 // Everything one launch needs; passed by value as the kernel argument.
 struct KernelArgs {
     const uint8_t* A;           // [rows_total][K] E4M3 codes
@@ -23,19 +50,25 @@ struct KernelArgs {
     float* ws;                  // split-K partial tiles [tiles][splits][BM*BN]
     int32_t* counters;          // split-K arrival counters [tiles], zero between launches
     int64_t rows;               // dense: M; contiguous: M_total; masked: M_max
-    int64_t units;              // work units = groups * tiles_m * tiles_n * splits
+    int32_t units;              // work units = groups * tiles_m * tiles_n * splits (< 2^30)
     int32_t N, K, G;
     int32_t nkb, nnb;           // K/128, ceil(N/128)
     int32_t tiles_m, tiles_n;
     int32_t splits, kb_per_split;
     int32_t group_m;            // M tiles per band of the unit order (1 = plain order)
+    // divisors of the unit decode
+    FastDiv div_splits, div_tiles_m, div_tiles_n;
+    FastDiv div_group_tiles;    // tiles_m * tiles_n
+    FastDiv div_band_units;     // group_m * tiles_n
+    FastDiv div_band_h;         // group_m (height of a full band)
+    FastDiv div_band_h_last;    // height of the last band, tiles_m - group_m * (bands - 1)
 };
 
 struct KernelEntry {
     const char* name;
     int layout;
     int bm, bn, waves_m, waves_n, stages;
-    int prefetch;               // L2 prefetch distance in K slices (0 = none)
+    int pipe;                   // K pipeline: 0 = ring of whole slices, 1 = split-phase
     int threads;
     bool splitk;                // compiled with the split-K partial reduction
     int lds_bytes;

@@ -25,8 +25,12 @@
 // slice, in the same order (the hardware pairs equal positions of X and Y).
 //
 // LDS layout of one slice: rows of 128 bytes, 16-byte chunk c of row r stored at chunk
-// position c ^ ((r >> 1) & 7), so the 16 lanes of a ds_read_b128 phase (rows r..r+15, one
-// chunk) hit 16 distinct 16-byte bank groups of the 64-bank (256 B) LDS.
+// position c ^ s(r) with s(r) = (r>>1 & 3) | ((r>>2 ^ r>>3) & 1) << 2.  A fragment read
+// (ds_read_b128, lane l: row l%16, chunk 2*(l/16)+h) is served 16 lanes per LDS cycle; measured
+// on gfx950, the lanes served together are those of one half-wave with equal parity of lane
+// bits 2..4.  The permutation gives those 16 lanes 16 distinct 16-byte bank groups of the
+// 256-byte-wide LDS (it is also conflict-free for runs of 8 or 16 consecutive lanes), so a
+// fragment read runs at the full ds_read_b128 rate; the DMA writes are contiguous 1 KB runs.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -76,7 +80,10 @@ __device__ __forceinline__ void wait_slices(int k) {
     }
 }
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// Chunk permutation of a 128-byte LDS row (see the layout note at the top of the file).
+__device__ __forceinline__ int swz(int row) {
+    return ((row >> 1) & 3) | ((((row >> 2) ^ (row >> 3)) & 1) << 2);
+}
 
 // Buffer resource flags of a raw (untyped) buffer on gfx9, and the sc1 cache-policy bit: an
 // access coherent at agent scope (what the compiler emits for agent-scope atomic loads/stores).
@@ -126,7 +133,22 @@ __device__ __forceinline__ int wave_min(int v) {
 // the kernel
 // ------------------------------------------------------------------------------------------
 
-template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PFD>
+// PIPE selects the K pipeline:
+//   0  a ring of STAGES whole slices; slice i + STAGES - 1 is issued when slice i is consumed.
+//   1  two stages, each slice split into three parts that are refilled as soon as every wave is
+//      done with them: A (read into registers at the start of the slice, with the scales), B1
+//      (the B rows of the first half of every wave's N sub-tiles) and B2 (the second half).
+//      With a barrier at the start and in the middle of every slice, B2 of slice i+1 is issued
+//      at the start of slice i and A, B1 of slice i+2 in its middle, so every part has 1.5
+//      slices of compute to arrive instead of one.
+//   2  two stages, two wave groups half a slice apart ("ping-pong"): the waves of the first
+//      N half lead, those of the second half trail by one phase, and every SIMD holds one wave
+//      of each group, so the matrix core is fed by one group while the other passes a barrier
+//      and reads its A fragments.  Loads of slice i+1 go out when the previous contents of
+//      their stage are read: the A tile and scales (leading waves) and the B rows except the
+//      last WN/2 (trailing waves) at barrier 2i, and those last B rows -- read by the trailing
+//      group one phase later than everything else -- at barrier 2i+1.
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PIPE>
 struct Tile {
     static constexpr int NW = WMW * WNW;            // waves per workgroup
     static constexpr int NT = 64 * NW;
@@ -142,27 +164,40 @@ struct Tile {
     static constexpr int SA_OFF = (BN + BM) * 128;
     static constexpr int SB_OFF = SA_OFF + BM * 4;
     static constexpr int STAGE_BYTES = SB_OFF + 256;
-    // L2 prefetch: PFD > 0 adds, per slice, one x1 gather per 64 tile rows that touches the
-    // cache line of every A and B row of slice i + PFD (data lands in a scratch LDS word)
-    static constexpr int PF_PER = PFD > 0 ? (BM + BN) / (64 * NW) : 0;
-    static_assert(PFD == 0 || (BM + BN) % (64 * NW) == 0, "prefetch rows split evenly over waves");
-    static constexpr int STAGES_BYTES_END = STAGES * STAGE_BYTES;
-    static constexpr int LDS_BYTES = STAGES_BYTES_END + (PFD > 0 ? 256 : 0);
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-    static constexpr int B_DMA = BN / (8 * NW);     // x4 loads per wave per slice for B
-    static constexpr int A_DMA = BM / (8 * NW);
-    static constexpr int AUX = (BM / 64 + 1 + NW - 1) / NW;  // x1 loads per wave: sa chunks + sb
-    static constexpr int NDMA = B_DMA + A_DMA + AUX + PF_PER;   // loads per wave per slice
+    static constexpr int DW = NW;                   // waves that issue loads (PIPE 0, 1)
+    static constexpr int B_DMA = BN / (8 * DW);     // x4 loads per loading wave per slice for B
+    static constexpr int A_DMA = BM / (8 * DW);
+    static constexpr int AUX = (BM / 64 + 1 + DW - 1) / DW;  // x1 loads per wave: sa chunks + sb
+    static constexpr int NDMA = B_DMA + A_DMA + AUX;          // loads per wave per slice
     static_assert(NDMA * (STAGES - 1) < 64, "vmcnt range");
     // every wave's N range lies inside one 128-row block of B scales
     static constexpr bool NB_UNIFORM = (BN % 128 == 0) && (128 % WN == 0);
     // split-K partial reduction is compiled for tiles small enough to need it (decode shapes)
     static constexpr bool SPLITK = BM * BN <= 128 * 256;
+    // split-phase pipeline: half of every wave's B loads fill B1, half B2
+    static constexpr int B_HALF = B_DMA / 2;        // x4 loads per wave for each of B1, B2
+    static constexpr int GROUPS_PER_HALF = WN / 16; // 8-row groups in half of a wave's N range
+    static_assert(PIPE != 1 || (STAGES == 2 && IN % 2 == 0 && B_DMA % 2 == 0 && NB_UNIFORM),
+                  "split-phase pipeline: two stages, an even number of N sub-tiles per wave");
+    // ping-pong: per slice, each leading wave moves BM/GW rows of A (P2_A x4 loads) and the
+    // scales, each trailing wave (BN - WN/2)/GW rows of B (P2_BM loads) and WN/2/GW tail rows
+    // (P2_BT loads); GW waves per group
+    static constexpr int GW = NW / 2;
+    static constexpr int P2_A = BM / (8 * GW);
+    static constexpr int P2_BM = (BN - WN / 2) / (8 * GW);
+    static constexpr int P2_BT = (WN / 2) / (8 * GW);
+    static constexpr int P2_PER = P2_A > P2_BM + P2_BT ? P2_A : P2_BM + P2_BT;
+    static_assert(PIPE != 2 || (STAGES == 2 && WNW == 2 && IN % 2 == 0 && NB_UNIFORM && P2_BT >= 1 &&
+                                BM % (8 * GW) == 0 && (WN / 2) % (8 * GW) == 0 &&
+                                (BN - WN / 2) % (8 * GW) == 0 && BM / 64 <= GW),
+                  "ping-pong pipeline: two stages, two wave groups along N");
 };
 
-template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PFD>
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PIPE>
 __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArgs args) {
-    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT, PFD>;
+    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT, PIPE>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
     __shared__ int s_flag;
 
@@ -173,6 +208,10 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
     const int wn = wave / WMW;              // wave position along N
     const int row16 = lane & 15;
     const int grp = lane >> 4;
+    // every fragment row a lane reads is row16 plus a multiple of 16, so its two 16-byte chunks
+    // sit at the same swizzled positions in every row
+    const int frag_lo = ((2 * grp) ^ swz(row16)) << 4;
+    const int frag_hi = ((2 * grp + 1) ^ swz(row16)) << 4;
 
     const int K = args.K;
     const int N = args.N;
@@ -186,27 +225,34 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
     int logical = blockIdx.x;
     if ((P & 7) == 0) logical = (blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3);
 
-    for (int64_t unit = logical; unit < args.units; unit += P) {
+    for (int unit = logical; unit < args.units; unit += P) {
         // ---- decode the unit: split s fastest, then M tile, N tile, group -------------------
-        int64_t u = unit;
-        const int split = (int)(u % args.splits); u /= args.splits;
+        // (uniform integer work on the scalar unit: multiply-shift divisions by launch constants)
+        uint32_t u = (uint32_t)unit;
+        const uint32_t tile_id = fast_div(u, args.div_splits);   // unit / splits
+        const int split = (int)(u - tile_id * (uint32_t)args.splits);
+        u = tile_id;
         int tm, tn;
         if (args.group_m > 1) {
             // bands of group_m M tiles; inside a band the M tile varies fastest
-            const int64_t per_group_units = (int64_t)args.tiles_m * args.tiles_n;
-            const int64_t grp_i = u / per_group_units;
-            int64_t v = u % per_group_units;
-            const int band_units = args.group_m * args.tiles_n;
-            const int band = (int)(v / band_units);
-            const int inb = (int)(v % band_units);
-            const int band_m0 = band * args.group_m;
-            const int band_h = min(args.group_m, args.tiles_m - band_m0);
-            tm = band_m0 + inb % band_h;
-            tn = inb / band_h;
+            const uint32_t grp_i = fast_div(u, args.div_group_tiles);
+            const uint32_t v = u - grp_i * args.div_group_tiles.d;
+            const uint32_t band = fast_div(v, args.div_band_units);
+            const uint32_t inb = v - band * args.div_band_units.d;
+            const int band_m0 = (int)band * args.group_m;
+            const bool full = band_m0 + args.group_m <= args.tiles_m;
+            const FastDiv& bh = full ? args.div_band_h : args.div_band_h_last;
+            const uint32_t q = fast_div(inb, bh);
+            tm = band_m0 + (int)(inb - q * bh.d);
+            tn = (int)q;
             u = grp_i;
         } else {
-            tm = (int)(u % args.tiles_m); u /= args.tiles_m;
-            tn = (int)(u % args.tiles_n); u /= args.tiles_n;
+            const uint32_t q = fast_div(u, args.div_tiles_m);
+            tm = (int)(u - q * (uint32_t)args.tiles_m);
+            u = q;
+            const uint32_t q2 = fast_div(u, args.div_tiles_n);
+            tn = (int)(u - q2 * (uint32_t)args.tiles_n);
+            u = q2;
         }
         const int gidx = (int)u;                       // group (masked layout), else 0
         const int m0 = tm * BM;                        // first row of the tile (within group)
@@ -272,11 +318,24 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
         const int nb_count = min(nnb, (n0 + BN + 127) >> 7) - nb_first;
 
         // ---- per-lane DMA source offsets (32-bit, relative to uniform per-slice bases) -------
-        // B and A: x4 load e of the workgroup covers tile rows 8e..8e+7; lane -> (row, chunk).
+        // B and A: x4 load e of the workgroup covers 8 tile rows; lane -> (row, chunk).
+        // PIPE 0: wave w's load q covers B rows 8 (w B_DMA + q) ..; PIPE 1: its first B_HALF
+        // loads cover 8-row groups of B1 (the first half of each wave's N range), the others
+        // the matching groups of B2.
+        auto b_row = [&](int q) -> int {
+            if constexpr (PIPE == 0) {
+                return 8 * (wave * T::B_DMA + q);
+            } else {
+                const int half = q / T::B_HALF;
+                const int k = wave * T::B_HALF + q % T::B_HALF;     // group within B1 (or B2)
+                return (k / T::GROUPS_PER_HALF) * T::WN + half * (T::WN / 2) +
+                       (k % T::GROUPS_PER_HALF) * 8;
+            }
+        };
         uint32_t b_off[T::B_DMA];
 #pragma unroll
         for (int q = 0; q < T::B_DMA; ++q) {
-            const int r = 8 * (wave * T::B_DMA + q) + (lane >> 3);
+            const int r = b_row(q) + (lane >> 3);
             const int c = (lane & 7) ^ swz(r);
             const int n = min(r, N - 1 - n0);          // clamp the N tail to a real row
             b_off[q] = (uint32_t)n * (uint32_t)K + (uint32_t)(c * 16);
@@ -293,7 +352,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
         uint32_t aux_off[T::AUX];
 #pragma unroll
         for (int t = 0; t < T::AUX; ++t) {
-            const int x = wave + T::NW * t;
+            const int x = wave + T::DW * t;
             if (x < BM / 64) {
                 const int r = min(64 * x + lane, row_limit - 1);
                 aux_off[t] = (uint32_t)r * 4u;
@@ -302,47 +361,32 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
                 aux_off[t] = (uint32_t)nb * (uint32_t)nkb * 4u;
             }
         }
-        uint32_t pf_off[T::PF_PER > 0 ? T::PF_PER : 1];
-#pragma unroll
-        for (int t = 0; t < T::PF_PER; ++t) {
-            const int chunk = wave * T::PF_PER + t;
-            const int r = 64 * chunk + lane;
-            if (chunk < BM / 64) pf_off[t] = (uint32_t)min(r, row_limit - 1) * (uint32_t)K;
-            else pf_off[t] = (uint32_t)min(r - BM, N - 1 - n0) * (uint32_t)K;
-        }
         const uint8_t* Bt = uniform_ptr(Bg + (int64_t)n0 * K + (int64_t)kb0 * 128);  // slice-0 bases
         const uint8_t* At = uniform_ptr(Ag + (int64_t)kb0 * 128);
         const float* sat = uniform_ptr(sag + (int64_t)kb0 * args.rows);
         const float* sbt = uniform_ptr(sbg + kb0);
 
-        auto issue_slice = [&](int i) {
-            const uint32_t st = smem_base + (uint32_t)((i % STAGES) * T::STAGE_BYTES);
+        auto stage_addr = [&](int i) { return smem_base + (uint32_t)((i % STAGES) * T::STAGE_BYTES); };
+        // B loads q in [q0, q1) of slice i
+        auto issue_b = [&](int i, int q0, int q1) {
+            const uint32_t st = stage_addr(i);
             const uint8_t* bs = uniform_ptr(Bt + (int64_t)i * 128);
-            const uint8_t* as = uniform_ptr(At + (int64_t)i * 128);
 #pragma unroll
             for (int q = 0; q < T::B_DMA; ++q)
-                dma_x4(st + T::B_OFF + 8 * (wave * T::B_DMA + q) * 128, bs, b_off[q]);
+                if (q >= q0 && q < q1) dma_x4(st + T::B_OFF + b_row(q) * 128, bs, b_off[q]);
+        };
+        // A tile and scale loads of slice i
+        auto issue_a = [&](int i) {
+            const uint32_t st = stage_addr(i);
+            const uint8_t* as = uniform_ptr(At + (int64_t)i * 128);
 #pragma unroll
             for (int q = 0; q < T::A_DMA; ++q)
                 dma_x4(st + T::A_OFF + 8 * (wave * T::A_DMA + q) * 128, as, a_off[q]);
 #pragma unroll
             for (int t = 0; t < T::AUX; ++t) {
-                const int x = wave + T::NW * t;
+                const int x = wave + T::DW * t;
                 if (x < BM / 64) dma_x1(st + T::SA_OFF + 256 * x, uniform_ptr(sat + (int64_t)i * args.rows), aux_off[t]);
                 else dma_x1(st + T::SB_OFF, uniform_ptr(sbt + i), aux_off[t]);
-            }
-            if constexpr (T::PF_PER > 0) {
-                // issued after this slice's own loads: it may complete one slice later without
-                // delaying them; clamped so that every slice issues the same number of loads
-                const int j = min(i + PFD, nks - 1);
-#pragma unroll
-                for (int t = 0; t < T::PF_PER; ++t) {
-                    const int chunk = wave * T::PF_PER + t;            // 64 rows of [A rows | B rows]
-                    if (chunk < BM / 64)
-                        dma_x1(smem_base + T::STAGES_BYTES_END, uniform_ptr(At + (int64_t)j * 128), pf_off[t]);
-                    else
-                        dma_x1(smem_base + T::STAGES_BYTES_END, uniform_ptr(Bt + (int64_t)j * 128), pf_off[t]);
-                }
             }
         };
 
@@ -353,23 +397,20 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
 #pragma unroll
             for (int j = 0; j < T::JM; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-        // ---- pipeline prologue --------------------------------------------------------------
-#pragma unroll
-        for (int i = 0; i < STAGES - 1; ++i)
-            if (i < nks) issue_slice(i);
-
-        // ---- main loop over 128-wide K slices -----------------------------------------------
-        for (int i = 0; i < nks; ++i) {
-            // slice i landed (this wave's loads), then every wave's loads
-            // (slice i's own prefetch, issued after its tile loads, may still be in flight)
-            wait_slices<T::NDMA, STAGES - 2, T::PF_PER>(min(STAGES - 2, nks - 1 - i));
-            __syncthreads();
-            if (i + STAGES - 1 < nks) issue_slice(i + STAGES - 1);
-
+        // ---- one 128-wide K slice on the matrix cores ---------------------------------------
+        // `mid` runs once, before the MFMAs of sub-tile IN/2 - 1 (PIPE 1: the mid-slice wait,
+        // barrier and loads; the MFMAs after it cover the latency of the first B2 fragment).
+        auto compute_slice = [&](int i, auto&& mid) {
             const uint8_t* st = smem + (i % STAGES) * T::STAGE_BYTES;
             const float* sa_l = reinterpret_cast<const float*>(st + T::SA_OFF);
             const float* sb_l = reinterpret_cast<const float*>(st + T::SB_OFF);
-
+            auto load_bf = [&](int i2) {
+                const int r = wn * T::WN + 16 * i2 + row16;
+                const uint8_t* rp = st + T::B_OFF + r * 128;
+                const v4i lo = *reinterpret_cast<const v4i*>(rp + frag_lo);
+                const v4i hi = *reinterpret_cast<const v4i*>(rp + frag_hi);
+                return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            };
             // A fragments (Y operand) and their scales for this wave's JM sub-tiles
             v8i af[T::JM];
             float sav[T::JM];
@@ -377,8 +418,8 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
             for (int j = 0; j < T::JM; ++j) {
                 const int r = wm * T::WM + 16 * j + row16;
                 const uint8_t* rp = st + T::A_OFF + r * 128;
-                const v4i lo = *reinterpret_cast<const v4i*>(rp + (((2 * grp) ^ swz(r)) << 4));
-                const v4i hi = *reinterpret_cast<const v4i*>(rp + (((2 * grp + 1) ^ swz(r)) << 4));
+                const v4i lo = *reinterpret_cast<const v4i*>(rp + frag_lo);
+                const v4i hi = *reinterpret_cast<const v4i*>(rp + frag_hi);
                 af[j] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
                 sav[j] = sa_l[r];
             }
@@ -388,16 +429,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
 #pragma unroll
                 for (int j = 0; j < T::JM; ++j) sw[j] = sav[j] * sbw;
             }
-            // Software pipeline over the N sub-tiles: the MFMAs of sub-tile i2 are issued before
-            // the promotion FMAs of sub-tile i2-1, so the matrix core and the VALU overlap and
-            // only one sub-tile row of partials is live.
-            auto load_bf = [&](int i2) {
-                const int r = wn * T::WN + 16 * i2 + row16;
-                const uint8_t* rp = st + T::B_OFF + r * 128;
-                const v4i lo = *reinterpret_cast<const v4i*>(rp + (((2 * grp) ^ swz(r)) << 4));
-                const v4i hi = *reinterpret_cast<const v4i*>(rp + (((2 * grp + 1) ^ swz(r)) << 4));
-                return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            };
+            v8i bf = load_bf(0);
             auto promote = [&](int i2, const v4f (&p)[T::JM]) {
                 float sbi = 0.f;
                 if constexpr (!T::NB_UNIFORM) sbi = sb_l[((n0 + wn * T::WN + 16 * i2) >> 7) - nb_first];
@@ -409,10 +441,13 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
                     acc[i2][j] += p[j] * s;
                 }
             };
+            // Software pipeline over the N sub-tiles: the MFMAs of sub-tile i2 are issued before
+            // the promotion FMAs of sub-tile i2-1, so the matrix core and the VALU overlap and
+            // only one sub-tile row of partials is live.
             v4f pprev[T::JM];
-            v8i bf = load_bf(0);
 #pragma unroll
             for (int i2 = 0; i2 < T::IN; ++i2) {
+                if (i2 == T::IN / 2 - 1) mid();
                 v4f pcur[T::JM];
 #pragma unroll
                 for (int j = 0; j < T::JM; ++j) pcur[j] = mfma16x16x128(bf, af[j]);
@@ -436,6 +471,136 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
                 __builtin_amdgcn_sched_barrier(0);
             }
             promote(T::IN - 1, pprev);
+        };
+
+        if constexpr (PIPE == 0) {
+            // ---- ring of whole slices -----------------------------------------------------
+#pragma unroll
+            for (int i = 0; i < STAGES - 1; ++i)
+                if (i < nks) { issue_b(i, 0, T::B_DMA); issue_a(i); }
+            for (int i = 0; i < nks; ++i) {
+                // slice i landed (this wave's loads), then every wave's loads
+                wait_slices<T::NDMA, STAGES - 2, 0>(min(STAGES - 2, nks - 1 - i));
+                __syncthreads();
+                if (i + STAGES - 1 < nks) { issue_b(i + STAGES - 1, 0, T::B_DMA); issue_a(i + STAGES - 1); }
+                compute_slice(i, [] {});
+            }
+        } else if constexpr (PIPE == 2) {
+            // ---- ping-pong --------------------------------------------------------------------
+            // Barrier k opens phase k.  Leading waves (wn == 0) compute the first part of slice i
+            // (A fragments, N sub-tiles before IN/2 - 1) in phase 2i and the rest in phase 2i+1;
+            // trailing waves one phase later.  Loads of slice i+1:
+            //   leading wave t: A rows [t BM/GW, +BM/GW) and sa chunk t (wave 0 also sb), issued
+            //     after barrier 2i, awaited (vmcnt 0) before barrier 2i+2;
+            //   trailing wave t: B rows [t R, +R), R = (BN - WN/2)/GW, issued after barrier 2i,
+            //     awaited before barrier 2i+2; tail rows [BN - WN/2 + t WN/2/GW, ...) issued after
+            //     barrier 2i+1, awaited before barrier 2i+4 (read from phase 2i+4 on).
+            // Their stage held slice i-1, which both groups finished reading by barrier 2i (the
+            // tail rows by barrier 2i+1).
+            const bool lead = (wn == 0);
+            const int t = wm;                                   // wave within its group
+            uint32_t p2_off[T::P2_PER];
+#pragma unroll
+            for (int q = 0; q < T::P2_PER; ++q) {
+                int r, lim;
+                if (lead) {
+                    r = t * (BM / T::GW) + 8 * min(q, T::P2_A - 1) + (lane >> 3);
+                    lim = row_limit;
+                } else if (q < T::P2_BM) {
+                    r = t * (8 * T::P2_BM) + 8 * q + (lane >> 3);
+                    lim = N - n0;
+                } else {
+                    r = BN - T::WN / 2 + t * (8 * T::P2_BT) + 8 * (q - T::P2_BM) + (lane >> 3);
+                    lim = N - n0;
+                }
+                const int c = (lane & 7) ^ swz(r);
+                p2_off[q] = (uint32_t)min(r, lim - 1) * (uint32_t)K + (uint32_t)(c * 16);
+            }
+            uint32_t p2_aux = 0;      // lead wave t: sa rows 64t..; (wave 0: sb via its own offset)
+            if (lead) p2_aux = (uint32_t)min(64 * t + lane, row_limit - 1) * 4u;
+            const uint32_t p2_sb = (uint32_t)(nb_first + min(lane, nb_count - 1)) * (uint32_t)nkb * 4u;
+            auto issue_main = [&](int i) {
+                const uint32_t st = stage_addr(i);
+                if (lead) {
+                    const uint8_t* as = uniform_ptr(At + (int64_t)i * 128);
+#pragma unroll
+                    for (int q = 0; q < T::P2_A; ++q)
+                        dma_x4(st + T::A_OFF + (t * (BM / T::GW) + 8 * q) * 128, as, p2_off[q]);
+                    if (t < BM / 64)
+                        dma_x1(st + T::SA_OFF + 256 * t, uniform_ptr(sat + (int64_t)i * args.rows), p2_aux);
+                    if (t == 0) dma_x1(st + T::SB_OFF, uniform_ptr(sbt + i), p2_sb);
+                } else {
+                    const uint8_t* bs = uniform_ptr(Bt + (int64_t)i * 128);
+#pragma unroll
+                    for (int q = 0; q < T::P2_BM; ++q)
+                        dma_x4(st + T::B_OFF + (t * (8 * T::P2_BM) + 8 * q) * 128, bs, p2_off[q]);
+                }
+            };
+            auto issue_tail = [&](int i) {
+                const uint32_t st = stage_addr(i);
+                const uint8_t* bs = uniform_ptr(Bt + (int64_t)i * 128);
+#pragma unroll
+                for (int q = 0; q < T::P2_BT; ++q)
+                    dma_x4(st + T::B_OFF + (BN - T::WN / 2 + t * (8 * T::P2_BT) + 8 * q) * 128, bs,
+                           p2_off[T::P2_BM + q]);
+            };
+            if (lead) {
+                issue_main(0);
+            } else {
+                issue_main(0);
+                issue_tail(0);
+                wait_vmcnt<T::P2_BT>();          // own part of slice 0 landed; its tail may not
+                __syncthreads();                 // barrier 0: trailing waves start a phase behind
+                if (nks > 1) issue_main(1);
+            }
+            for (int i = 0; i < nks; ++i) {
+                if (lead) {
+                    wait_vmcnt<0>();             // own A part of slice i
+                    __syncthreads();             // barrier 2i
+                    if (i + 1 < nks) issue_main(i + 1);
+                } else {
+                    __syncthreads();             // barrier 2i+1
+                    if (i + 1 < nks) issue_tail(i + 1);
+                }
+                compute_slice(i, [&] {
+                    if (lead) {
+                        __syncthreads();         // barrier 2i+1
+                    } else {
+                        // own B part of slice i+1 and the tail of slice i landed; the tail of
+                        // slice i+1 (issued after them) may still be in flight
+                        if (i + 1 < nks) wait_vmcnt<T::P2_BT>();
+                        else wait_vmcnt<0>();
+                        __syncthreads();         // barrier 2i+2
+                        if (i + 2 < nks) issue_main(i + 2);
+                    }
+                });
+            }
+            if (lead) __syncthreads();           // barrier 2 nks: the trailing waves' last phase
+        } else {
+            // ---- split-phase two-stage pipeline -------------------------------------------
+            // issue order: A,B1 (0) | B2 (0) | A,B1 (1) | B2 (1) | A,B1 (2) | ...; at each wait,
+            // the loads issued after the awaited part are exactly one slice's worth (NDMA), or
+            // fewer at the end of the K range
+            constexpr int NB2 = T::B_DMA - T::B_HALF;
+            issue_a(0);
+            issue_b(0, 0, T::B_HALF);
+            issue_b(0, T::B_HALF, T::B_DMA);
+            if (nks > 1) { issue_a(1); issue_b(1, 0, T::B_HALF); }
+            for (int i = 0; i < nks; ++i) {
+                // A, B1 of slice i
+                if (i + 1 < nks) wait_vmcnt<T::NDMA>();
+                else wait_vmcnt<NB2>();
+                __syncthreads();
+                if (i + 1 < nks) issue_b(i + 1, T::B_HALF, T::B_DMA);
+                compute_slice(i, [&] {
+                    // B2 of slice i; then A and B1 of slice i+2 go into the stage of slice i,
+                    // whose A and B1 every wave has finished reading
+                    if (i + 1 < nks) wait_vmcnt<T::NDMA>();
+                    else wait_vmcnt<0>();
+                    __syncthreads();
+                    if (i + 2 < nks) { issue_a(i + 2); issue_b(i + 2, 0, T::B_HALF); }
+                });
+            }
         }
 
         // ---- epilogue -----------------------------------------------------------------------
@@ -446,7 +611,6 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
             // (sc1) 16-byte buffer accesses, so no L2-wide write-back or invalidate is needed:
             //   write partial (sc1) -> wait until written -> barrier -> counter += 1 (agent)
             //   last arrival: barrier -> read all partials (sc1) in split order -> store D
-            const int64_t tile_id = unit / args.splits;
             const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(
                 uniform_ptr(args.ws + tile_id * args.splits * (int64_t)(BM * BN)), 0,
                 (int)(args.splits * BM * BN * 4), kBufferFlags);
@@ -529,15 +693,15 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
 // instantiation table
 // ------------------------------------------------------------------------------------------
 
-template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PFD>
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PIPE>
 static void launch_impl(dim3 grid, const KernelArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT, PFD>), grid,
+    hipLaunchKernelGGL((fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT, PIPE>), grid,
                        dim3(WMW * WNW * 64), 0, s, a);
 }
 
-template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PFD>
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PIPE>
 static KernelEntry entry(const char* name) {
-    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT, PFD>;
+    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT, PIPE>;
     KernelEntry e;
     e.name = name;
     e.layout = LAYOUT;
@@ -549,24 +713,23 @@ static KernelEntry entry(const char* name) {
     e.threads = T::NT;
     e.splitk = T::SPLITK;
     e.lds_bytes = T::LDS_BYTES;
-    e.prefetch = PFD;
-    e.func = reinterpret_cast<const void*>(&fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT, PFD>);
-    e.launch = &launch_impl<BM, BN, WMW, WNW, STAGES, LAYOUT, PFD>;
+    e.pipe = PIPE;
+    e.func = reinterpret_cast<const void*>(&fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT, PIPE>);
+    e.launch = &launch_impl<BM, BN, WMW, WNW, STAGES, LAYOUT, PIPE>;
     return e;
 }
 
 #define FP8GEMM_ENTRY(BM, BN, WMW, WNW, ST, L) \
     entry<BM, BN, WMW, WNW, ST, L, 0>(#L " " #BM "x" #BN " waves " #WMW "x" #WNW " stages " #ST)
-#define FP8GEMM_ENTRY_PF(BM, BN, WMW, WNW, ST, L, PFD) \
-    entry<BM, BN, WMW, WNW, ST, L, PFD>(#L " " #BM "x" #BN " waves " #WMW "x" #WNW " stages " #ST " prefetch " #PFD)
+#define FP8GEMM_ENTRY_PIPE(BM, BN, WMW, WNW, ST, L, PIPE) \
+    entry<BM, BN, WMW, WNW, ST, L, PIPE>(#L " " #BM "x" #BN " waves " #WMW "x" #WNW " stages " #ST " pipe " #PIPE)
 
 const KernelEntry* kernel_table(int* count) {
     static const KernelEntry table[] = {
         // dense, prefill: 256x256 tiles, 8 waves (4 along M x 2 along N), 2-slice ring
         FP8GEMM_ENTRY(256, 256, 4, 2, 2, kDense),
-        FP8GEMM_ENTRY_PF(256, 256, 4, 2, 2, kDense, 2),
-        FP8GEMM_ENTRY_PF(256, 256, 4, 2, 2, kDense, 3),
-        FP8GEMM_ENTRY_PF(256, 256, 4, 2, 2, kDense, 5),
+        FP8GEMM_ENTRY_PIPE(256, 256, 4, 2, 2, kDense, 1),
+        FP8GEMM_ENTRY_PIPE(256, 256, 4, 2, 2, kDense, 2),
         // dense, medium
         FP8GEMM_ENTRY(128, 128, 2, 2, 4, kDense),
         FP8GEMM_ENTRY(128, 256, 2, 4, 2, kDense),
