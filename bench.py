@@ -52,11 +52,48 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-grouped", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
+    p.add_argument("--counters", action="store_true",
+                   help="launch each M=4096 sweep GEMM and a 1 GiB copy a few times, eagerly (run under "
+                        "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)")
+    p.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="turn the two rocprofv3 --pmc output folders of a --counters run into " + TRAFFIC_FILE)
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join("profiles", "traffic_dense_256x256_m4096_sweep.txt")
+COPY_BYTES = 1 << 30           # calibration copy: reads and writes this many bytes
+
+
+def kernel_source_hash():
+    import hashlib
+    src = os.path.join(ROOT, "fp8_block_scaled_x128_amd", "csrc", "fp8gemm_kernels.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """Measured HBM traffic per launch of the dominant kernel from the committed counter summary,
+    or None when there is none or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)"
               % args.gpus, file=sys.stderr)
@@ -98,6 +135,10 @@ def main():
     def call(case, r):
         c = case["copies"][r]
         fg.gemm_nt(c["A"], c["sa"], c["B"], c["sb"], out=c["D"], stream=stream)
+
+    if args.counters:
+        counters_run(fg, W, torch, dev, stream, cases, call)
+        return
 
     # ---- eager reference outputs and launch configurations ------------------------------------
     configs = []
@@ -199,8 +240,9 @@ def main():
 
     dom = max(kern_time, key=kern_time.get)
     ach = kern_flop[dom] / (kern_time[dom] * 1e-3) / 1e12
+    traffic = read_traffic() if dom.startswith("nt tile=256x256") else None
     roofline = dict(bound="mfma", achieved=round(ach, 1), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / PEAK_FP8_TFLOPS, 4), traffic=None, kernel=dom,
+                    frac=round(ach / PEAK_FP8_TFLOPS, 4), traffic=traffic, kernel=dom,
                     launches_per_step=kern_launch[dom],
                     avg_launch_us=round(kern_time[dom] / kern_launch[dom] * 1e3, 2),
                     flop_per_launch=kern_flop[dom] // kern_launch[dom],
@@ -240,6 +282,96 @@ def main():
         "grouped": grouped,
     }
     print(json.dumps(line), flush=True)
+
+
+COUNTER_REPS = 3
+
+
+def counters_run(fg, W, torch, dev, stream, cases, call):
+    """Eager launches for hardware-counter passes: every M=4096 sweep GEMM (the 256x256 kernel)
+    COUNTER_REPS times after a read-only cache flush, then an elementwise copy (dst = src + 0) of
+    COPY_BYTES COUNTER_REPS times.  Prints the launch order."""
+    flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), device=dev)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    order = []
+    with torch.cuda.stream(stream):
+        for case in cases:
+            if case["M"] != 4096:
+                continue
+            for r in range(COUNTER_REPS):
+                torch.sum(flush, dim=0, out=sink)   # read-only flush: a reduction, no elementwise kernel
+                call(case, r % COPIES)
+                order.append("gemm %d %d %d" % (case["M"], case["N"], case["K"]))
+        # the calibration copy: the last elementwise kernels of the run (read and write COPY_BYTES)
+        for r in range(COUNTER_REPS):
+            torch.add(src, 0.0, out=dst)
+            order.append("copy %d" % COPY_BYTES)
+    stream.synchronize()
+    print(json.dumps({"counter_launches": order, "config": fg.last_config()}), flush=True)
+
+
+def _counter_rows(folder, counter):
+    """(kernel name, value in KiB) per dispatch, in dispatch order, from a rocprofv3 csv folder."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % folder)
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = int(r["Dispatch_Id"])
+            name, val = per.get(key, (r["Kernel_Name"], 0.0))
+            per[key] = (name, val + float(r["Counter_Value"]))
+    return [per[k] for k in sorted(per)]
+
+
+def traffic_summary(fetch_dir, write_dir):
+    """HBM traffic of the 256x256 kernel per launch on the M=4096 sweep shapes, from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) each scaled by what the counter reads for a plain copy of
+    COPY_BYTES (true bytes / counted bytes)."""
+    import workloads as W
+    out = {}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(folder, counter)
+        gem = [v for n, v in rows if "fp8gemm_kernel" in n]
+        cop = [v for n, v in rows if "elementwise" in n.lower()]
+        if len(cop) < 1 or len(gem) != COUNTER_REPS * len(W.SWEEP_NK):
+            raise SystemExit("%s: %d gemm and %d copy dispatches found" % (counter, len(gem), len(cop)))
+        copy_kib = float(np.median(cop[-COUNTER_REPS:]))
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        shapes = []
+        for i, (N, K) in enumerate(W.SWEEP_NK):
+            kib = float(np.median(gem[i * COUNTER_REPS:(i + 1) * COUNTER_REPS]))
+            shapes.append((N, K, kib, kib * 1024.0 * factor))
+        out[counter] = (copy_kib, factor, shapes)
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    fetch, write = out["FETCH_SIZE"], out["WRITE_SIZE"]
+    total = [f[3] + w[3] for f, w in zip(fetch[2], write[2])]
+    per_launch = int(round(sum(total) / len(total)))
+    with open(path, "w") as f:
+        f.write("HBM traffic of the dense 256x256 kernel on the M=4096 sweep shapes (rocprofv3 --pmc)\n")
+        f.write("command (per counter): rocprofv3 --pmc <FETCH_SIZE | WRITE_SIZE> --output-format csv -d <dir> "
+                "-- python3 bench.py --counters\n")
+        f.write("summary: python3 bench.py --traffic-summary <fetch dir> <write dir>\n")
+        f.write("kernel_source_sha256_16: %s\n" % kernel_source_hash())
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            copy_kib, factor, shapes = out[counter]
+            f.write("%s_copy_calibration: %.0f KiB counted for a %d-byte copy, factor %.4f\n"
+                    % (counter, copy_kib, COPY_BYTES, factor))
+        f.write("per shape (median of %d launches; bytes = KiB * 1024 * factor; algorithmic = A + B + scales + D):\n"
+                % COUNTER_REPS)
+        for (N, K, fk, fb), (_, _, wk, wb) in zip(fetch[2], write[2]):
+            alg = W.dense_work(4096, N, K)[1]
+            f.write("  M=4096 N=%-5d K=%-5d fetch %10.0f KiB  write %9.0f KiB  traffic %6.1f MB  algorithmic %6.1f MB  ratio %.2f\n"
+                    % (N, K, fk, wk, (fb + wb) / 1e6, alg / 1e6, (fb + wb) / alg))
+        f.write("traffic_bytes_per_launch: %d\n" % per_launch)
+    print(open(path).read())
 
 
 def bench_grouped(fg, W, torch, dev, stream, reps=10):
@@ -301,10 +433,12 @@ def cpu_baseline(cases, target_s):
     import oracle
 
     nth = oracle.num_threads(0)
-    probe = cases[0]
+    # the oracle spreads rows over its threads: probe with two rows per thread
+    probe = max(cases, key=lambda c: c["M"])
+    pr = min(probe["M"], 2 * nth)
     t0 = time.perf_counter()
-    oracle.gemm_nt(probe["hostA"][:4], probe["hostsa"][:4], probe["hostB"], probe["hostsb"])
-    t_probe = (time.perf_counter() - t0) / 4
+    oracle.gemm_nt(probe["hostA"][:pr], probe["hostsa"][:pr], probe["hostB"], probe["hostsb"])
+    t_probe = (time.perf_counter() - t0) / pr
     per_row_all = t_probe * sum(c["N"] * c["K"] for c in cases) / (probe["N"] * probe["K"])
     rows = int(max(1, min(512, target_s / max(per_row_all, 1e-9))))
     flop = 0

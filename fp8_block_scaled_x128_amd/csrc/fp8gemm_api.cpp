@@ -109,24 +109,24 @@ int workspace(DeviceState* d, hipStream_t stream, size_t partial_bytes, size_t c
     return FP8GEMM_OK;
 }
 
-int find_entry(int layout, int bm, int bn, int wm, int wn, int stages, int pipe = 0) {
+int find_entry(int layout, int bm, int bn, int wm, int wn, int stages) {
     int n = 0;
     const KernelEntry* tab = kernel_table(&n);
     for (int i = 0; i < n; ++i)
         if (tab[i].layout == layout && tab[i].bm == bm && tab[i].bn == bn && tab[i].waves_m == wm &&
-            tab[i].waves_n == wn && tab[i].stages == stages && tab[i].pipe == pipe)
+            tab[i].waves_n == wn && tab[i].stages == stages)
             return i;
     return -1;
 }
 
-// Optional override for experiments: FP8GEMM_FORCE_CONFIG=BMxBN:WMxWN:STAGES:SPLIT[:PIPE]
+// Optional override for experiments: FP8GEMM_FORCE_CONFIG=BMxBN:WMxWN:STAGES:SPLIT
 bool forced_config(int layout, int* idx, int* split) {
     const char* s = std::getenv("FP8GEMM_FORCE_CONFIG");
     if (!s || !*s) return false;
-    int bm, bn, wm, wn, st, sp, pf = 0;
-    int got = std::sscanf(s, "%dx%d:%dx%d:%d:%d:%d", &bm, &bn, &wm, &wn, &st, &sp, &pf);
+    int bm, bn, wm, wn, st, sp;
+    int got = std::sscanf(s, "%dx%d:%dx%d:%d:%d", &bm, &bn, &wm, &wn, &st, &sp);
     if (got < 6) return false;
-    int i = find_entry(layout, bm, bn, wm, wn, st, pf);
+    int i = find_entry(layout, bm, bn, wm, wn, st);
     if (i < 0) return false;
     *idx = i;
     *split = std::max(1, sp);
@@ -228,9 +228,9 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream)
     int64_t grid = std::min<int64_t>(a.units, slots);
     if (grid <= 0) return FP8GEMM_OK;
     std::snprintf(g_last_config, sizeof g_last_config,
-                  "%s tile=%dx%d waves=%dx%d stages=%d pipe=%d split=%d kb_per_split=%d units=%lld grid=%lld",
+                  "%s tile=%dx%d waves=%dx%d stages=%d split=%d kb_per_split=%d units=%lld grid=%lld",
                   layout == kDense ? "nt" : (layout == kContiguous ? "contiguous" : "masked"), e.bm,
-                  e.bn, e.waves_m, e.waves_n, e.stages, e.pipe, a.splits, a.kb_per_split,
+                  e.bn, e.waves_m, e.waves_n, e.stages, a.splits, a.kb_per_split,
                   (long long)a.units, (long long)grid);
     if (std::getenv("FP8GEMM_LOG")) std::fprintf(stderr, "[fp8gemm] %s\n", g_last_config);
     e.launch(dim3((unsigned)grid), a, stream);

@@ -68,7 +68,6 @@ struct KernelEntry {
     const char* name;
     int layout;
     int bm, bn, waves_m, waves_n, stages;
-    int pipe;                   // K pipeline: 0 = ring of whole slices, 1 = split-phase
     int threads;
     bool splitk;                // compiled with the split-K partial reduction
     int lds_bytes;

@@ -133,22 +133,7 @@ __device__ __forceinline__ int wave_min(int v) {
 // the kernel
 // ------------------------------------------------------------------------------------------
 
-// PIPE selects the K pipeline:
-//   0  a ring of STAGES whole slices; slice i + STAGES - 1 is issued when slice i is consumed.
-//   1  two stages, each slice split into three parts that are refilled as soon as every wave is
-//      done with them: A (read into registers at the start of the slice, with the scales), B1
-//      (the B rows of the first half of every wave's N sub-tiles) and B2 (the second half).
-//      With a barrier at the start and in the middle of every slice, B2 of slice i+1 is issued
-//      at the start of slice i and A, B1 of slice i+2 in its middle, so every part has 1.5
-//      slices of compute to arrive instead of one.
-//   2  two stages, two wave groups half a slice apart ("ping-pong"): the waves of the first
-//      N half lead, those of the second half trail by one phase, and every SIMD holds one wave
-//      of each group, so the matrix core is fed by one group while the other passes a barrier
-//      and reads its A fragments.  Loads of slice i+1 go out when the previous contents of
-//      their stage are read: the A tile and scales (leading waves) and the B rows except the
-//      last WN/2 (trailing waves) at barrier 2i, and those last B rows -- read by the trailing
-//      group one phase later than everything else -- at barrier 2i+1.
-template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PIPE>
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT>
 struct Tile {
     static constexpr int NW = WMW * WNW;            // waves per workgroup
     static constexpr int NT = 64 * NW;
@@ -166,38 +151,20 @@ struct Tile {
     static constexpr int STAGE_BYTES = SB_OFF + 256;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-    static constexpr int DW = NW;                   // waves that issue loads (PIPE 0, 1)
-    static constexpr int B_DMA = BN / (8 * DW);     // x4 loads per loading wave per slice for B
-    static constexpr int A_DMA = BM / (8 * DW);
-    static constexpr int AUX = (BM / 64 + 1 + DW - 1) / DW;  // x1 loads per wave: sa chunks + sb
+    static constexpr int B_DMA = BN / (8 * NW);     // x4 loads per wave per slice for B
+    static constexpr int A_DMA = BM / (8 * NW);
+    static constexpr int AUX = (BM / 64 + 1 + NW - 1) / NW;  // x1 loads per wave: sa chunks + sb
     static constexpr int NDMA = B_DMA + A_DMA + AUX;          // loads per wave per slice
     static_assert(NDMA * (STAGES - 1) < 64, "vmcnt range");
     // every wave's N range lies inside one 128-row block of B scales
     static constexpr bool NB_UNIFORM = (BN % 128 == 0) && (128 % WN == 0);
     // split-K partial reduction is compiled for tiles small enough to need it (decode shapes)
     static constexpr bool SPLITK = BM * BN <= 128 * 256;
-    // split-phase pipeline: half of every wave's B loads fill B1, half B2
-    static constexpr int B_HALF = B_DMA / 2;        // x4 loads per wave for each of B1, B2
-    static constexpr int GROUPS_PER_HALF = WN / 16; // 8-row groups in half of a wave's N range
-    static_assert(PIPE != 1 || (STAGES == 2 && IN % 2 == 0 && B_DMA % 2 == 0 && NB_UNIFORM),
-                  "split-phase pipeline: two stages, an even number of N sub-tiles per wave");
-    // ping-pong: per slice, each leading wave moves BM/GW rows of A (P2_A x4 loads) and the
-    // scales, each trailing wave (BN - WN/2)/GW rows of B (P2_BM loads) and WN/2/GW tail rows
-    // (P2_BT loads); GW waves per group
-    static constexpr int GW = NW / 2;
-    static constexpr int P2_A = BM / (8 * GW);
-    static constexpr int P2_BM = (BN - WN / 2) / (8 * GW);
-    static constexpr int P2_BT = (WN / 2) / (8 * GW);
-    static constexpr int P2_PER = P2_A > P2_BM + P2_BT ? P2_A : P2_BM + P2_BT;
-    static_assert(PIPE != 2 || (STAGES == 2 && WNW == 2 && IN % 2 == 0 && NB_UNIFORM && P2_BT >= 1 &&
-                                BM % (8 * GW) == 0 && (WN / 2) % (8 * GW) == 0 &&
-                                (BN - WN / 2) % (8 * GW) == 0 && BM / 64 <= GW),
-                  "ping-pong pipeline: two stages, two wave groups along N");
 };
 
-template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PIPE>
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT>
 __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArgs args) {
-    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT, PIPE>;
+    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
     __shared__ int s_flag;
 
@@ -318,20 +285,8 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
         const int nb_count = min(nnb, (n0 + BN + 127) >> 7) - nb_first;
 
         // ---- per-lane DMA source offsets (32-bit, relative to uniform per-slice bases) -------
-        // B and A: x4 load e of the workgroup covers 8 tile rows; lane -> (row, chunk).
-        // PIPE 0: wave w's load q covers B rows 8 (w B_DMA + q) ..; PIPE 1: its first B_HALF
-        // loads cover 8-row groups of B1 (the first half of each wave's N range), the others
-        // the matching groups of B2.
-        auto b_row = [&](int q) -> int {
-            if constexpr (PIPE == 0) {
-                return 8 * (wave * T::B_DMA + q);
-            } else {
-                const int half = q / T::B_HALF;
-                const int k = wave * T::B_HALF + q % T::B_HALF;     // group within B1 (or B2)
-                return (k / T::GROUPS_PER_HALF) * T::WN + half * (T::WN / 2) +
-                       (k % T::GROUPS_PER_HALF) * 8;
-            }
-        };
+        // B and A: x4 load q of wave w covers tile rows 8 (w count + q) .. + 7; lane -> (row, chunk)
+        auto b_row = [&](int q) -> int { return 8 * (wave * T::B_DMA + q); };
         uint32_t b_off[T::B_DMA];
 #pragma unroll
         for (int q = 0; q < T::B_DMA; ++q) {
@@ -352,7 +307,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
         uint32_t aux_off[T::AUX];
 #pragma unroll
         for (int t = 0; t < T::AUX; ++t) {
-            const int x = wave + T::DW * t;
+            const int x = wave + T::NW * t;
             if (x < BM / 64) {
                 const int r = min(64 * x + lane, row_limit - 1);
                 aux_off[t] = (uint32_t)r * 4u;
@@ -384,7 +339,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
                 dma_x4(st + T::A_OFF + 8 * (wave * T::A_DMA + q) * 128, as, a_off[q]);
 #pragma unroll
             for (int t = 0; t < T::AUX; ++t) {
-                const int x = wave + T::DW * t;
+                const int x = wave + T::NW * t;
                 if (x < BM / 64) dma_x1(st + T::SA_OFF + 256 * x, uniform_ptr(sat + (int64_t)i * args.rows), aux_off[t]);
                 else dma_x1(st + T::SB_OFF, uniform_ptr(sbt + i), aux_off[t]);
             }
@@ -398,9 +353,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
             for (int j = 0; j < T::JM; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
         // ---- one 128-wide K slice on the matrix cores ---------------------------------------
-        // `mid` runs once, before the MFMAs of sub-tile IN/2 - 1 (PIPE 1: the mid-slice wait,
-        // barrier and loads; the MFMAs after it cover the latency of the first B2 fragment).
-        auto compute_slice = [&](int i, auto&& mid) {
+        auto compute_slice = [&](int i) {
             const uint8_t* st = smem + (i % STAGES) * T::STAGE_BYTES;
             const float* sa_l = reinterpret_cast<const float*>(st + T::SA_OFF);
             const float* sb_l = reinterpret_cast<const float*>(st + T::SB_OFF);
@@ -447,7 +400,6 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
             v4f pprev[T::JM];
 #pragma unroll
             for (int i2 = 0; i2 < T::IN; ++i2) {
-                if (i2 == T::IN / 2 - 1) mid();
                 v4f pcur[T::JM];
 #pragma unroll
                 for (int j = 0; j < T::JM; ++j) pcur[j] = mfma16x16x128(bf, af[j]);
@@ -473,134 +425,16 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
             promote(T::IN - 1, pprev);
         };
 
-        if constexpr (PIPE == 0) {
-            // ---- ring of whole slices -----------------------------------------------------
+        // ---- ring of whole slices: slice i + STAGES - 1 goes into the stage slice i - 1 used
 #pragma unroll
-            for (int i = 0; i < STAGES - 1; ++i)
-                if (i < nks) { issue_b(i, 0, T::B_DMA); issue_a(i); }
-            for (int i = 0; i < nks; ++i) {
-                // slice i landed (this wave's loads), then every wave's loads
-                wait_slices<T::NDMA, STAGES - 2, 0>(min(STAGES - 2, nks - 1 - i));
-                __syncthreads();
-                if (i + STAGES - 1 < nks) { issue_b(i + STAGES - 1, 0, T::B_DMA); issue_a(i + STAGES - 1); }
-                compute_slice(i, [] {});
-            }
-        } else if constexpr (PIPE == 2) {
-            // ---- ping-pong --------------------------------------------------------------------
-            // Barrier k opens phase k.  Leading waves (wn == 0) compute the first part of slice i
-            // (A fragments, N sub-tiles before IN/2 - 1) in phase 2i and the rest in phase 2i+1;
-            // trailing waves one phase later.  Loads of slice i+1:
-            //   leading wave t: A rows [t BM/GW, +BM/GW) and sa chunk t (wave 0 also sb), issued
-            //     after barrier 2i, awaited (vmcnt 0) before barrier 2i+2;
-            //   trailing wave t: B rows [t R, +R), R = (BN - WN/2)/GW, issued after barrier 2i,
-            //     awaited before barrier 2i+2; tail rows [BN - WN/2 + t WN/2/GW, ...) issued after
-            //     barrier 2i+1, awaited before barrier 2i+4 (read from phase 2i+4 on).
-            // Their stage held slice i-1, which both groups finished reading by barrier 2i (the
-            // tail rows by barrier 2i+1).
-            const bool lead = (wn == 0);
-            const int t = wm;                                   // wave within its group
-            uint32_t p2_off[T::P2_PER];
-#pragma unroll
-            for (int q = 0; q < T::P2_PER; ++q) {
-                int r, lim;
-                if (lead) {
-                    r = t * (BM / T::GW) + 8 * min(q, T::P2_A - 1) + (lane >> 3);
-                    lim = row_limit;
-                } else if (q < T::P2_BM) {
-                    r = t * (8 * T::P2_BM) + 8 * q + (lane >> 3);
-                    lim = N - n0;
-                } else {
-                    r = BN - T::WN / 2 + t * (8 * T::P2_BT) + 8 * (q - T::P2_BM) + (lane >> 3);
-                    lim = N - n0;
-                }
-                const int c = (lane & 7) ^ swz(r);
-                p2_off[q] = (uint32_t)min(r, lim - 1) * (uint32_t)K + (uint32_t)(c * 16);
-            }
-            uint32_t p2_aux = 0;      // lead wave t: sa rows 64t..; (wave 0: sb via its own offset)
-            if (lead) p2_aux = (uint32_t)min(64 * t + lane, row_limit - 1) * 4u;
-            const uint32_t p2_sb = (uint32_t)(nb_first + min(lane, nb_count - 1)) * (uint32_t)nkb * 4u;
-            auto issue_main = [&](int i) {
-                const uint32_t st = stage_addr(i);
-                if (lead) {
-                    const uint8_t* as = uniform_ptr(At + (int64_t)i * 128);
-#pragma unroll
-                    for (int q = 0; q < T::P2_A; ++q)
-                        dma_x4(st + T::A_OFF + (t * (BM / T::GW) + 8 * q) * 128, as, p2_off[q]);
-                    if (t < BM / 64)
-                        dma_x1(st + T::SA_OFF + 256 * t, uniform_ptr(sat + (int64_t)i * args.rows), p2_aux);
-                    if (t == 0) dma_x1(st + T::SB_OFF, uniform_ptr(sbt + i), p2_sb);
-                } else {
-                    const uint8_t* bs = uniform_ptr(Bt + (int64_t)i * 128);
-#pragma unroll
-                    for (int q = 0; q < T::P2_BM; ++q)
-                        dma_x4(st + T::B_OFF + (t * (8 * T::P2_BM) + 8 * q) * 128, bs, p2_off[q]);
-                }
-            };
-            auto issue_tail = [&](int i) {
-                const uint32_t st = stage_addr(i);
-                const uint8_t* bs = uniform_ptr(Bt + (int64_t)i * 128);
-#pragma unroll
-                for (int q = 0; q < T::P2_BT; ++q)
-                    dma_x4(st + T::B_OFF + (BN - T::WN / 2 + t * (8 * T::P2_BT) + 8 * q) * 128, bs,
-                           p2_off[T::P2_BM + q]);
-            };
-            if (lead) {
-                issue_main(0);
-            } else {
-                issue_main(0);
-                issue_tail(0);
-                wait_vmcnt<T::P2_BT>();          // own part of slice 0 landed; its tail may not
-                __syncthreads();                 // barrier 0: trailing waves start a phase behind
-                if (nks > 1) issue_main(1);
-            }
-            for (int i = 0; i < nks; ++i) {
-                if (lead) {
-                    wait_vmcnt<0>();             // own A part of slice i
-                    __syncthreads();             // barrier 2i
-                    if (i + 1 < nks) issue_main(i + 1);
-                } else {
-                    __syncthreads();             // barrier 2i+1
-                    if (i + 1 < nks) issue_tail(i + 1);
-                }
-                compute_slice(i, [&] {
-                    if (lead) {
-                        __syncthreads();         // barrier 2i+1
-                    } else {
-                        // own B part of slice i+1 and the tail of slice i landed; the tail of
-                        // slice i+1 (issued after them) may still be in flight
-                        if (i + 1 < nks) wait_vmcnt<T::P2_BT>();
-                        else wait_vmcnt<0>();
-                        __syncthreads();         // barrier 2i+2
-                        if (i + 2 < nks) issue_main(i + 2);
-                    }
-                });
-            }
-            if (lead) __syncthreads();           // barrier 2 nks: the trailing waves' last phase
-        } else {
-            // ---- split-phase two-stage pipeline -------------------------------------------
-            // issue order: A,B1 (0) | B2 (0) | A,B1 (1) | B2 (1) | A,B1 (2) | ...; at each wait,
-            // the loads issued after the awaited part are exactly one slice's worth (NDMA), or
-            // fewer at the end of the K range
-            constexpr int NB2 = T::B_DMA - T::B_HALF;
-            issue_a(0);
-            issue_b(0, 0, T::B_HALF);
-            issue_b(0, T::B_HALF, T::B_DMA);
-            if (nks > 1) { issue_a(1); issue_b(1, 0, T::B_HALF); }
-            for (int i = 0; i < nks; ++i) {
-                // A, B1 of slice i
-                if (i + 1 < nks) wait_vmcnt<T::NDMA>();
-                else wait_vmcnt<NB2>();
-                __syncthreads();
-                if (i + 1 < nks) issue_b(i + 1, T::B_HALF, T::B_DMA);
-                compute_slice(i, [&] {
-                    // B2 of slice i; then A and B1 of slice i+2 go into the stage of slice i,
-                    // whose A and B1 every wave has finished reading
-                    if (i + 1 < nks) wait_vmcnt<T::NDMA>();
-                    else wait_vmcnt<0>();
-                    __syncthreads();
-                    if (i + 2 < nks) { issue_a(i + 2); issue_b(i + 2, 0, T::B_HALF); }
-                });
-            }
+        for (int i = 0; i < STAGES - 1; ++i)
+            if (i < nks) { issue_b(i, 0, T::B_DMA); issue_a(i); }
+        for (int i = 0; i < nks; ++i) {
+            // slice i landed (this wave's loads), then every wave's loads
+            wait_slices<T::NDMA, STAGES - 2, 0>(min(STAGES - 2, nks - 1 - i));
+            __syncthreads();
+            if (i + STAGES - 1 < nks) { issue_b(i + STAGES - 1, 0, T::B_DMA); issue_a(i + STAGES - 1); }
+            compute_slice(i);
         }
 
         // ---- epilogue -----------------------------------------------------------------------
@@ -693,15 +527,15 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
 // instantiation table
 // ------------------------------------------------------------------------------------------
 
-template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PIPE>
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT>
 static void launch_impl(dim3 grid, const KernelArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT, PIPE>), grid,
+    hipLaunchKernelGGL((fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT>), grid,
                        dim3(WMW * WNW * 64), 0, s, a);
 }
 
-template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int PIPE>
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT>
 static KernelEntry entry(const char* name) {
-    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT, PIPE>;
+    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT>;
     KernelEntry e;
     e.name = name;
     e.layout = LAYOUT;
@@ -713,23 +547,18 @@ static KernelEntry entry(const char* name) {
     e.threads = T::NT;
     e.splitk = T::SPLITK;
     e.lds_bytes = T::LDS_BYTES;
-    e.pipe = PIPE;
-    e.func = reinterpret_cast<const void*>(&fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT, PIPE>);
-    e.launch = &launch_impl<BM, BN, WMW, WNW, STAGES, LAYOUT, PIPE>;
+    e.func = reinterpret_cast<const void*>(&fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT>);
+    e.launch = &launch_impl<BM, BN, WMW, WNW, STAGES, LAYOUT>;
     return e;
 }
 
 #define FP8GEMM_ENTRY(BM, BN, WMW, WNW, ST, L) \
-    entry<BM, BN, WMW, WNW, ST, L, 0>(#L " " #BM "x" #BN " waves " #WMW "x" #WNW " stages " #ST)
-#define FP8GEMM_ENTRY_PIPE(BM, BN, WMW, WNW, ST, L, PIPE) \
-    entry<BM, BN, WMW, WNW, ST, L, PIPE>(#L " " #BM "x" #BN " waves " #WMW "x" #WNW " stages " #ST " pipe " #PIPE)
+    entry<BM, BN, WMW, WNW, ST, L>(#L " " #BM "x" #BN " waves " #WMW "x" #WNW " stages " #ST)
 
 const KernelEntry* kernel_table(int* count) {
     static const KernelEntry table[] = {
         // dense, prefill: 256x256 tiles, 8 waves (4 along M x 2 along N), 2-slice ring
         FP8GEMM_ENTRY(256, 256, 4, 2, 2, kDense),
-        FP8GEMM_ENTRY_PIPE(256, 256, 4, 2, 2, kDense, 1),
-        FP8GEMM_ENTRY_PIPE(256, 256, 4, 2, 2, kDense, 2),
         // dense, medium
         FP8GEMM_ENTRY(128, 128, 2, 2, 4, kDense),
         FP8GEMM_ENTRY(128, 256, 2, 4, 2, kDense),

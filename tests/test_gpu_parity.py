@@ -51,15 +51,15 @@ def sentinel_tensor(shape):
 
 def kernel_table():
     src = open(os.path.join(ROOT, "fp8_block_scaled_x128_amd", "csrc", "fp8gemm_kernels.hip")).read()
-    return [(int(a), int(b), int(c), int(d), int(e), f, int(g or 0)) for a, b, c, d, e, f, g in
-            re.findall(r"FP8GEMM_ENTRY(?:_PIPE)?\((\d+), (\d+), (\d+), (\d+), (\d+), (k\w+)(?:, (\d+))?\)", src)]
+    return [(int(a), int(b), int(c), int(d), int(e), f) for a, b, c, d, e, f in
+            re.findall(r"FP8GEMM_ENTRY\((\d+), (\d+), (\d+), (\d+), (\d+), (k\w+)\)", src)]
 
 
 class forced:
     """Force the launch configuration of the calls inside the block (FP8GEMM_FORCE_CONFIG)."""
 
-    def __init__(self, bm, bn, wm, wn, st, split, pipe=0):
-        self.v = "%dx%d:%dx%d:%d:%d:%d" % (bm, bn, wm, wn, st, split, pipe)
+    def __init__(self, bm, bn, wm, wn, st, split):
+        self.v = "%dx%d:%dx%d:%d:%d" % (bm, bn, wm, wn, st, split)
 
     def __enter__(self):
         os.environ["FP8GEMM_FORCE_CONFIG"] = self.v
@@ -121,17 +121,17 @@ def test_random_ragged_shapes(M, N, K):
 
 
 @pytest.mark.parametrize("entry", [e for e in kernel_table() if e[5] == "kDense"],
-                         ids=lambda e: "%dx%d_w%dx%d_s%d_p%d" % (e[:5] + e[6:7]))
+                         ids=lambda e: "%dx%d_w%dx%d_s%d" % e[:5])
 @pytest.mark.parametrize("split", [1, 3])
 def test_every_dense_kernel_config(entry, split):
-    bm, bn, wm, wn, st, _, pipe = entry
+    bm, bn, wm, wn, st, _ = entry
     M, N, K = 2 * bm + 5, 2 * bn + 17, 1152
     d = W.dense(M, N, K, seed=bm * bn + split)
     ref = oracle.gemm_nt(d.A, d.sa, d.B, d.sb)
-    with forced(bm, bn, wm, wn, st, split, pipe):
+    with forced(bm, bn, wm, wn, st, split):
         D = run_dense(d)
         cfg = fg.last_config()
-    assert "tile=%dx%d" % (bm, bn) in cfg and "pipe=%d" % pipe in cfg, cfg
+    assert "tile=%dx%d" % (bm, bn) in cfg, cfg
     assert_close(gpu_bits(D), ref, what=cfg)
     # integer inputs through the same configuration are bit-exact
     rng = np.random.default_rng(5)
@@ -139,13 +139,13 @@ def test_every_dense_kernel_config(entry, split):
     sa = (2.0 ** rng.integers(-1, 2, size=(M, K // 128))).astype(np.float32)
     sb = (2.0 ** rng.integers(-1, 2, size=((N + 127) // 128, K // 128))).astype(np.float32)
     ref2 = oracle.gemm_nt(A, sa, B, sb)
-    with forced(bm, bn, wm, wn, st, split, pipe):
+    with forced(bm, bn, wm, wn, st, split):
         D2 = run_dense(W.Dense(A, sa, B, sb))
     assert_bit_exact(gpu_bits(D2), ref2, what=cfg)
     # a 3-CU cap makes every workgroup loop over several tiles (stage reuse across tiles)
     fg.set_num_cus(3)
     try:
-        with forced(bm, bn, wm, wn, st, split, pipe):
+        with forced(bm, bn, wm, wn, st, split):
             D3 = run_dense(W.Dense(A, sa, B, sb))
             cfg3 = fg.last_config()
     finally:
@@ -227,10 +227,10 @@ def test_contiguous_parity_and_padding_untouched(counts, N, K):
 
 
 @pytest.mark.parametrize("entry", [e for e in kernel_table() if e[5] == "kContiguous"],
-                         ids=lambda e: "%dx%d_w%dx%d_s%d_p%d" % (e[:5] + e[6:7]))
+                         ids=lambda e: "%dx%d_w%dx%d_s%d" % e[:5])
 @pytest.mark.parametrize("split", [1, 2])
 def test_every_contiguous_kernel_config(entry, split):
-    bm, bn, wm, wn, st, _, pipe = entry
+    bm, bn, wm, wn, st, _ = entry
     c = W.contiguous([130, 0, 250], 0, 2 * bn + 40, 640, seed=bm + bn + split, packed=True)
     ref, valid = oracle.grouped_contiguous(c.A, c.sa, c.B, c.sb, c.m_indices)
     with forced(bm, bn, wm, wn, st, split):
@@ -299,10 +299,10 @@ def test_masked_parity_rows_past_count_untouched(mm, M_max, N, K):
 
 
 @pytest.mark.parametrize("entry", [e for e in kernel_table() if e[5] == "kMasked"],
-                         ids=lambda e: "%dx%d_w%dx%d_s%d_p%d" % (e[:5] + e[6:7]))
+                         ids=lambda e: "%dx%d_w%dx%d_s%d" % e[:5])
 @pytest.mark.parametrize("split", [1, 3])
 def test_every_masked_kernel_config(entry, split):
-    bm, bn, wm, wn, st, _, pipe = entry
+    bm, bn, wm, wn, st, _ = entry
     w = W.masked(np.array([bm + 3, 0, 17, 2 * bm], np.int32), 2 * bm, 2 * bn + 24, 768, seed=bm * 3 + split)
     ref, valid = oracle.grouped_masked(w.A, w.sa, w.B, w.sb, w.masked_m)
     with forced(bm, bn, wm, wn, st, split):
