@@ -168,7 +168,22 @@ Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_row
         if (N >= 16384 || K >= 8192) c.entry = find_entry(layout, 128, 128, 2, 4, 3);
         else c.entry = find_entry(layout, 64, 64, 1, 4, 4);
     } else if (m >= 1024 && N >= 256 && layout == kDense) {
-        c.entry = find_entry(layout, 256, 256, 4, 2, 2);
+        // N tile width: fewest rounds of CUs times the time of one tile (a 256x160 tile takes
+        // about 0.86 of a 256x256 one on MI355X: the A operand and the per-slice fixed work do not
+        // shrink with the width)
+        struct Width { int bn; int64_t tile_time; } widths[] = {{256, 100}, {160, 86}};
+        int64_t best = -1;
+        const int64_t tiles_m = (m + 255) / 256;
+        for (const Width& w : widths) {
+            const int e = find_entry(layout, 256, w.bn, 4, 2, 2);
+            if (e < 0) continue;
+            const int64_t tiles = tiles_m * ((N + w.bn - 1) / w.bn);
+            const int64_t cost = ((tiles + cus - 1) / cus) * w.tile_time;
+            if (best < 0 || cost < best) {
+                best = cost;
+                c.entry = e;
+            }
+        }
     } else if (m >= 1024 && N >= 256 && layout == kContiguous) {
         c.entry = find_entry(layout, 128, 256, 2, 4, 2);
     } else {

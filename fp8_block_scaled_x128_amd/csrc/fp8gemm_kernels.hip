@@ -142,7 +142,7 @@ struct Tile {
     static constexpr int JM = WM / 16;              // 16-wide M sub-tiles per wave
     static constexpr int IN = WN / 16;              // 16-wide N sub-tiles per wave
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
-    static_assert(BN % (8 * NW) == 0 && BM % (8 * NW) == 0, "each wave moves whole 8-row groups");
+    static_assert(BN % 8 == 0 && BM % (8 * NW) == 0, "whole 8-row groups; every wave moves the same A rows count");
     static_assert(BM % 64 == 0, "scale rows of A are moved 64 at a time");
     static constexpr int B_OFF = 0;
     static constexpr int A_OFF = BN * 128;
@@ -151,7 +151,11 @@ struct Tile {
     static constexpr int STAGE_BYTES = SB_OFF + 256;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-    static constexpr int B_DMA = BN / (8 * NW);     // x4 loads per wave per slice for B
+    // x4 loads per wave per slice for B; when the BN/8 row groups do not split evenly over the
+    // waves, the spare slots repeat the last group (the same bytes to the same LDS rows), so every
+    // wave issues the same number of loads and waits with the same counts
+    static constexpr int B_GROUPS = BN / 8;
+    static constexpr int B_DMA = (B_GROUPS + NW - 1) / NW;
     static constexpr int A_DMA = BM / (8 * NW);
     static constexpr int AUX = (BM / 64 + 1 + NW - 1) / NW;  // x1 loads per wave: sa chunks + sb
     static constexpr int NDMA = B_DMA + A_DMA + AUX;          // loads per wave per slice
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
 
         // ---- per-lane DMA source offsets (32-bit, relative to uniform per-slice bases) -------
         // B and A: x4 load q of wave w covers tile rows 8 (w count + q) .. + 7; lane -> (row, chunk)
-        auto b_row = [&](int q) -> int { return 8 * (wave * T::B_DMA + q); };
+        auto b_row = [&](int q) -> int { return 8 * min(wave * T::B_DMA + q, T::B_GROUPS - 1); };
         uint32_t b_off[T::B_DMA];
 #pragma unroll
         for (int q = 0; q < T::B_DMA; ++q) {
@@ -559,6 +563,8 @@ const KernelEntry* kernel_table(int* count) {
     static const KernelEntry table[] = {
         // dense, prefill: 256x256 tiles, 8 waves (4 along M x 2 along N), 2-slice ring
         FP8GEMM_ENTRY(256, 256, 4, 2, 2, kDense),
+        // dense, prefill, narrower N tiles for widths whose 256-wide tile count leaves CUs idle
+        FP8GEMM_ENTRY(256, 160, 4, 2, 2, kDense),
         // dense, medium
         FP8GEMM_ENTRY(128, 128, 2, 2, 4, kDense),
         FP8GEMM_ENTRY(128, 256, 2, 4, 2, kDense),
