@@ -84,7 +84,7 @@ def read_traffic():
     if vals.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     try:
-        return int(vals["traffic_bytes_per_launch"])
+        return int(vals["traffic_bytes_per_launch"].split()[0])
     except (KeyError, ValueError):
         return None
 
@@ -331,15 +331,19 @@ def _counter_rows(folder, counter):
     return [per[k] for k in sorted(per)]
 
 
+DOMINANT_KERNEL = "fp8gemm_kernel<256, 256, 4, 2, 2, 0>"
+
+
 def traffic_summary(fetch_dir, write_dir):
-    """HBM traffic of the 256x256 kernel per launch on the M=4096 sweep shapes, from FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch) each scaled by what the counter reads for a plain copy of
-    COPY_BYTES (true bytes / counted bytes)."""
+    """HBM traffic per launch of the dense 256x256 kernel on the M=4096 sweep shapes that use it,
+    from FETCH_SIZE and WRITE_SIZE (KiB per dispatch) each scaled by what the counter reads for a
+    plain copy of COPY_BYTES (true bytes / counted bytes).  Shapes that run another kernel are
+    listed for reference and left out of the per-launch figure."""
     import workloads as W
     out = {}
     for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(folder, counter)
-        gem = [v for n, v in rows if "fp8gemm_kernel" in n]
+        gem = [(n, v) for n, v in rows if "fp8gemm_kernel" in n]
         cop = [v for n, v in rows if "elementwise" in n.lower()]
         if len(cop) < 1 or len(gem) != COUNTER_REPS * len(W.SWEEP_NK):
             raise SystemExit("%s: %d gemm and %d copy dispatches found" % (counter, len(gem), len(cop)))
@@ -347,13 +351,16 @@ def traffic_summary(fetch_dir, write_dir):
         factor = COPY_BYTES / (copy_kib * 1024.0)
         shapes = []
         for i, (N, K) in enumerate(W.SWEEP_NK):
-            kib = float(np.median(gem[i * COUNTER_REPS:(i + 1) * COUNTER_REPS]))
-            shapes.append((N, K, kib, kib * 1024.0 * factor))
+            part = gem[i * COUNTER_REPS:(i + 1) * COUNTER_REPS]
+            kib = float(np.median([v for _, v in part]))
+            name = part[0][0]
+            kern = name[name.index("fp8gemm_kernel"):name.index(">") + 1] if ">" in name else name
+            shapes.append((N, K, kern, kib, kib * 1024.0 * factor))
         out[counter] = (copy_kib, factor, shapes)
     path = os.path.join(ROOT, TRAFFIC_FILE)
     fetch, write = out["FETCH_SIZE"], out["WRITE_SIZE"]
-    total = [f[3] + w[3] for f, w in zip(fetch[2], write[2])]
-    per_launch = int(round(sum(total) / len(total)))
+    dom = [f[4] + w[4] for f, w in zip(fetch[2], write[2]) if f[2] == DOMINANT_KERNEL]
+    per_launch = int(round(sum(dom) / len(dom)))
     with open(path, "w") as f:
         f.write("HBM traffic of the dense 256x256 kernel on the M=4096 sweep shapes (rocprofv3 --pmc)\n")
         f.write("command (per counter): rocprofv3 --pmc <FETCH_SIZE | WRITE_SIZE> --output-format csv -d <dir> "
@@ -366,11 +373,13 @@ def traffic_summary(fetch_dir, write_dir):
                     % (counter, copy_kib, COPY_BYTES, factor))
         f.write("per shape (median of %d launches; bytes = KiB * 1024 * factor; algorithmic = A + B + scales + D):\n"
                 % COUNTER_REPS)
-        for (N, K, fk, fb), (_, _, wk, wb) in zip(fetch[2], write[2]):
+        for (N, K, kern, fk, fb), (_, _, _, wk, wb) in zip(fetch[2], write[2]):
             alg = W.dense_work(4096, N, K)[1]
-            f.write("  M=4096 N=%-5d K=%-5d fetch %10.0f KiB  write %9.0f KiB  traffic %6.1f MB  algorithmic %6.1f MB  ratio %.2f\n"
-                    % (N, K, fk, wk, (fb + wb) / 1e6, alg / 1e6, (fb + wb) / alg))
-        f.write("traffic_bytes_per_launch: %d\n" % per_launch)
+            f.write("  M=4096 N=%-5d K=%-5d %-38s fetch %10.0f KiB  write %9.0f KiB  traffic %6.1f MB  "
+                    "algorithmic %6.1f MB  ratio %.2f\n"
+                    % (N, K, kern, fk, wk, (fb + wb) / 1e6, alg / 1e6, (fb + wb) / alg))
+        f.write("traffic_bytes_per_launch: %d   (mean over the %d shapes run by %s)\n"
+                % (per_launch, len(dom), DOMINANT_KERNEL))
     print(open(path).read())
 
 
@@ -440,7 +449,7 @@ def cpu_baseline(cases, target_s):
     oracle.gemm_nt(probe["hostA"][:pr], probe["hostsa"][:pr], probe["hostB"], probe["hostsb"])
     t_probe = (time.perf_counter() - t0) / pr
     per_row_all = t_probe * sum(c["N"] * c["K"] for c in cases) / (probe["N"] * probe["K"])
-    rows = int(max(1, min(512, target_s / max(per_row_all, 1e-9))))
+    rows = int(max(1, min(4096, target_s / max(per_row_all, 1e-9))))
     flop = 0
     t0 = time.perf_counter()
     for c in cases:
