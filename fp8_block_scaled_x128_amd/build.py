@@ -64,13 +64,17 @@ def check_isa(asm_text: str) -> None:
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, "--offload-arch=" + ARCH] + COMMON + DEVICE_FLAGS + ["-shared", "-o", tmp] + SOURCES)
-    with tempfile.TemporaryDirectory() as td:
-        asm = os.path.join(td, "kernels.s")
-        _run([HIPCC, "--offload-arch=" + ARCH] + COMMON + DEVICE_FLAGS +
-             ["--cuda-device-only", "-S", "-o", asm, SOURCES[0]])
-        check_isa(open(asm).read())
-    os.replace(tmp, LIB)
+    try:
+        _run([HIPCC, "--offload-arch=" + ARCH] + COMMON + DEVICE_FLAGS + ["-shared", "-o", tmp] + SOURCES)
+        with tempfile.TemporaryDirectory() as td:
+            asm = os.path.join(td, "kernels.s")
+            _run([HIPCC, "--offload-arch=" + ARCH] + COMMON + DEVICE_FLAGS +
+                 ["--cuda-device-only", "-S", "-o", asm, SOURCES[0]])
+            check_isa(open(asm).read())
+        os.replace(tmp, LIB)
+    finally:
+        if os.path.exists(tmp):
+            os.remove(tmp)
     if verbose:
         print("built", LIB)
     return LIB

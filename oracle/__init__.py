@@ -41,6 +41,10 @@ def _load():
         lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
         lib.oracle_bf16_bits.restype = ctypes.c_uint16
         lib.oracle_bf16_bits.argtypes = [ctypes.c_double]
+        lib.oracle_e4m3_code.restype = ctypes.c_uint8
+        lib.oracle_e4m3_code.argtypes = [ctypes.c_double]
+        lib.oracle_quantize_1x128.restype = ctypes.c_int
+        lib.oracle_quantize_1x128.argtypes = [P, I64, I64, P, P, ctypes.c_int]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = [ctypes.c_int]
         lib.oracle_gemm_nt.restype = ctypes.c_int
@@ -77,6 +81,10 @@ def e4m3_value(code: int) -> float:
 
 def bf16_bits(x: float) -> int:
     return _load().oracle_bf16_bits(float(x))
+
+
+def e4m3_code(x: float) -> int:
+    return _load().oracle_e4m3_code(float(x))
 
 
 def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
@@ -160,3 +168,14 @@ def elements(A, sa, B, sb, a_rows, b_rows, sb_rows, with_acc: bool = False, nthr
     if rc:
         raise MemoryError("oracle_elements")
     return (out, acc) if with_acc else out
+
+
+def quantize_1x128(X_bits, nthreads: int = 0):
+    """Activation quantiser: X bf16 bit patterns (uint16 [M,K]) -> (codes uint8 [M,K],
+    sa float32 [M, ceil(K/128)]), one scale per 1x128 block (definition in ``oracle.c``)."""
+    X = _c(X_bits, np.uint16)
+    M, K = X.shape
+    codes = np.empty((M, K), dtype=np.uint8)
+    sa = np.empty((M, -(-K // 128)), dtype=np.float32)
+    _load().oracle_quantize_1x128(_ptr(X), M, K, _ptr(codes), _ptr(sa), nthreads)
+    return codes, sa

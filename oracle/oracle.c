@@ -31,11 +31,22 @@
  * sa*sb of two fp32 values is exact in fp64 (48-bit significand).  The sum over K-blocks is done
  * with fp64 fused multiply-add, then rounded once, fp64 -> bf16, round to nearest even.
  *
+ * The activation quantiser (oracle_quantize_1x128) is the step just before the product: the pages
+ * take fine-grained scaling from DeepSeek V3 ([P1], section 深入了解DeepGEMM) and name no
+ * quantiser, so its definition is the plain reading of a 1x128 block scale: per block of 128
+ * consecutive K values of a row, amax = max |x| (floored at fp32(1e-4) so that an all-zero block
+ * keeps a finite scale), s = fp32(amax / 448), code = E4M3 round-to-nearest-even of fp32(x / s)
+ * saturated to +-448.  448 is E4M3's largest finite value, so the largest element of every block
+ * maps to +-448.
+ *
  * Parity pins (tests/test_oracle_pins.py): e4m3 decode against the OCP table anchors and an
  * independent library decoder; bf16 rounding against exact rational rounding; whole products
  * against exact rational brute force on tiny shapes, integer closed forms, power-of-two scale
  * closed forms, a library fp64 matmul of the dequantised operands, and the grouping/permutation/
- * padding invariants.  No function below is "parity unpinned".
+ * padding invariants; the E4M3 encoder against torch's float8 cast over every fp32 neighbour of
+ * every E4M3 value and rounding midpoint; the quantiser against hand-worked golden blocks, the
+ * block-maximum, sign-symmetry and power-of-two scaling invariants and the format's rounding
+ * error bound.  No function below is "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
@@ -82,6 +93,28 @@ ORACLE_API uint16_t oracle_bf16_bits(double x) {
     uint32_t bits;
     memcpy(&bits, &qf, sizeof bits);
     return (uint16_t)(sign | (uint16_t)((bits >> 16) & 0x7FFF));
+}
+
+/* Encode a finite value as E4M3, round to nearest, ties to even, saturating at +-448 (the largest
+ * finite value; E4M3 has no infinity).  Between 2^-6 and 448 a binade [2^E, 2^(E+1)) holds 8
+ * values, spaced 2^(E-3); below 2^-6 the values are the multiples of 2^-9 (subnormals, code = the
+ * multiple itself, and the multiple 8 is the code of 2^-6, the smallest normal).  The sign bit is
+ * kept for values that round to zero. */
+ORACLE_API uint8_t oracle_e4m3_code(double x) {
+    uint8_t sign = signbit(x) ? 0x80 : 0;
+    double ax = fabs(x);
+    if (ax >= 448.0) return (uint8_t)(sign | 0x7E);
+    if (ax < ldexp(1.0, -6)) {
+        double f = nearbyint(ldexp(ax, 9));       /* 0..8 multiples of 2^-9 */
+        return (uint8_t)(sign | (uint8_t)f);
+    }
+    int e2;
+    frexp(ax, &e2);                               /* ax in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;                               /* -6 .. 8 */
+    double q = nearbyint(ldexp(ax, 3 - E));       /* 8 .. 16 eighths of 2^E */
+    if (q == 16.0) { q = 8.0; ++E; }              /* rounded up into the next binade */
+    if (E > 8 || (E == 8 && q > 14.0)) return (uint8_t)(sign | 0x7E);
+    return (uint8_t)(sign | (uint8_t)((E + 7) << 3) | (uint8_t)(q - 8.0));
 }
 
 /* ---- one output element ------------------------------------------------------------------ */
@@ -265,4 +298,47 @@ ORACLE_API int oracle_elements(const uint8_t* A, const float* sa, const uint8_t*
         free(b);
     }
     return failed ? -1 : 0;
+}
+
+/* ---- activation quantiser, 1x128 blocks ---------------------------------------------------- */
+
+/* X [M][K] bfloat16 bit patterns -> codes [M][K] (E4M3) and sa [M][ceil(K/128)] (fp32), one scale
+ * per block of 128 consecutive K values of a row (a shorter last block when K is not a multiple
+ * of 128).  Per block:
+ *   amax = max |x|                         (exact: |x| of a bf16 value is a bf16 value)
+ *   amax = max(amax, fp32(1e-4))           (an all-zero or tiny block keeps a finite scale)
+ *   s    = fp32(amax / 448)                (the scale stored in sa)
+ *   v    = fp32(x / s)                     (the value to encode)
+ *   code = E4M3_rne(v), saturating at +-448
+ * Both quotients are formed in fp64 and rounded once to fp32; for a quotient of two fp32 values
+ * fp64 carries more than 2*24+2 bits, so that double rounding equals the correctly rounded fp32
+ * quotient.  Inputs must be finite (a NaN or infinity gives unspecified codes).  Returns 0. */
+ORACLE_API int oracle_quantize_1x128(const uint16_t* X, int64_t M, int64_t K, uint8_t* codes,
+                                     float* sa, int nthreads) {
+    int64_t nkb = (K + 127) / 128;
+    const float floor_amax = 1e-4f;
+    int nt = pick_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+            int64_t k0 = kb * 128, k1 = k0 + 128 < K ? k0 + 128 : K;
+            float xs[128];
+            float amax = 0.0f;
+            for (int64_t k = k0; k < k1; ++k) {
+                uint32_t bits = (uint32_t)X[m * K + k] << 16;   /* bf16 is the top half of fp32 */
+                memcpy(&xs[k - k0], &bits, sizeof bits);
+                float a = fabsf(xs[k - k0]);
+                if (a > amax) amax = a;
+            }
+            if (amax < floor_amax) amax = floor_amax;
+            float s = (float)((double)amax / 448.0);
+            sa[m * nkb + kb] = s;
+            for (int64_t k = k0; k < k1; ++k) {
+                float v = (float)((double)xs[k - k0] / (double)s);
+                codes[m * K + k] = oracle_e4m3_code((double)v);
+            }
+        }
+    }
+    return 0;
 }

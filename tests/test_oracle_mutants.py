@@ -18,6 +18,16 @@ MUTANTS = {
                              "double s = (double)sa_row[0] * (double)sb_row[kb];"),
     "sb_block_from_k_not_n": ("sb + (n / 128) * nkb, K);", "sb + 0 * nkb, K);"),
     "fp32_accumulation": ("acc = fma(s, block, acc);", "acc = (float)(acc + (float)(s * block));"),
+    "encode_ties_away": ("double q = nearbyint(ldexp(ax, 3 - E));", "double q = round(ldexp(ax, 3 - E));"),
+    "encode_subnormal_quantum": ("double f = nearbyint(ldexp(ax, 9));", "double f = nearbyint(ldexp(ax, 10));"),
+    "encode_zero_sign_lost": ("uint8_t sign = signbit(x) ? 0x80 : 0;", "uint8_t sign = x < 0 ? 0x80 : 0;"),
+    "encode_binade_carry_lost": ("if (q == 16.0) { q = 8.0; ++E; }", ""),
+    "quant_floor_dropped": ("if (amax < floor_amax) amax = floor_amax;", ""),
+    "quant_scale_divisor": ("float s = (float)((double)amax / 448.0);", "float s = (float)((double)amax / 240.0);"),
+    "quant_sa_transposed": ("sa[m * nkb + kb] = s;", "sa[kb * M + m] = s;"),
+    "quant_multiplies_by_reciprocal": ("float v = (float)((double)xs[k - k0] / (double)s);",
+                                       "float v = xs[k - k0] * (1.0f / s);"),
+    "quant_amax_skips_last": ("if (a > amax) amax = a;", "if (a > amax && k + 1 < k1) amax = a;"),
 }
 
 

@@ -350,3 +350,167 @@ def test_quantiser_block_max_is_448():
     for nb in range(3):
         blk = b[nb * 128:(nb + 1) * 128].view(-1, 4, 128).amax(dim=(0, 2))
         assert torch.all(blk == 448)
+
+
+# ------------------------------------------------------------------------------------------
+# activation quantiser, 1x128 blocks
+# ------------------------------------------------------------------------------------------
+
+FLOOR = np.float32(1e-4)
+
+
+def bf16_bits_exact(x) -> np.ndarray:
+    """fp32 values that bf16 holds exactly -> their bf16 bit patterns (the top half of fp32)."""
+    b = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32)
+    assert np.all((b & 0xFFFF) == 0), "value not exact in bf16"
+    return (b >> 16).astype(np.uint16)
+
+
+def bf16_bits_rne(x) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (torch's cast)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def widen(bits) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def test_e4m3_encoder_matches_library_cast_at_every_boundary():
+    """Every E4M3 value and every rounding midpoint, with their two nearest fp32 neighbours on
+    each side, plus log-uniform values, both signs: the oracle's encoder against torch's cast."""
+    vals = _DEC[:0x7F].astype(np.float64)           # codes 0x00..0x7E: 0 .. 448 ascending
+    assert np.all(np.diff(vals) > 0)
+    mids = (vals[:-1] + vals[1:]) / 2
+    pts = np.concatenate([vals, mids]).astype(np.float32)
+    cand = [pts]
+    up, dn = pts.copy(), pts.copy()
+    for _ in range(2):
+        up = np.nextafter(up, np.float32(np.inf))
+        dn = np.nextafter(dn, np.float32(0))
+        cand += [up, dn]
+    rng = np.random.default_rng(40)
+    cand.append((2.0 ** rng.uniform(-16, math.log2(448), 4000)).astype(np.float32))
+    x = np.concatenate(cand)
+    x = x[x <= 448]
+    x = np.concatenate([x, -x])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_code(float(v)) for v in x], dtype=np.uint8)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(ref[i])) for i in bad[:8]]
+    # above 448 the encoder saturates (torch's cast turns values past 464 into NaN instead)
+    for v in (448.0, 455.9, 464.0, 470.0, 1e6):
+        assert oracle.e4m3_code(v) == 0x7E and oracle.e4m3_code(-v) == 0xFE
+
+
+def _read_quant_golden(path):
+    blocks = []
+    for line in _read_golden(path):
+        f = line.split()
+        if f[0] == "block":
+            blocks.append((float(f[1]), float(f[2]), []))
+        else:
+            blocks[-1][2].append((float(f[0]), int(f[1], 16)))
+    return blocks
+
+
+def test_quantiser_golden_blocks(golden_dir):
+    """Row 0: the hand-worked blocks side by side.  Row 1: an all-zero block, row 2: a block whose
+    amax is below the floor; both take the floored scale fp32(fp32(1e-4)/448)."""
+    blocks = _read_quant_golden(os.path.join(golden_dir, "quantize_1x128_blocks.txt"))
+    assert len(blocks) == 2
+    K = 128 * len(blocks)
+    x = np.zeros((3, K), dtype=np.float32)
+    want = np.zeros((3, K), dtype=np.uint8)
+    for b, (amax, scale, elems) in enumerate(blocks):
+        for j, (v, code) in enumerate(elems):
+            x[0, 128 * b + j] = v
+            want[0, 128 * b + j] = code
+        assert np.abs(x[0, 128 * b:128 * b + 128]).max() == amax
+    tiny = np.float32(2.0 ** -20)
+    x[2, :] = tiny
+    codes, sa = oracle.quantize_1x128(bf16_bits_exact(x))
+    floored = np.float32(FLOOR / np.float32(448))            # numpy's IEEE fp32 division
+    assert np.array_equal(sa[0], np.array([b[1] for b in blocks], np.float32))
+    assert np.all(sa[1] == floored) and np.all(sa[2] == floored)
+    assert np.array_equal(codes[0], want[0]) and np.all(codes[1] == 0)
+    v = np.float32(tiny / floored)
+    assert np.all(codes[2] == code_of(float(v)))
+
+
+def test_quantiser_scale_layout_closed_form():
+    """Block (m, kb) holds 2^(m+2kb-4) everywhere but one position, which holds 448 times that
+    (negative for odd m+kb): sa[m][kb] = 2^(m+2kb-4), codes 0x38 (1.0) and 0x7E / 0xFE."""
+    M, nkb = 3, 3
+    x = np.zeros((M, 128 * nkb), dtype=np.float32)
+    want = np.zeros_like(x, dtype=np.uint8)
+    for m in range(M):
+        for kb in range(nkb):
+            s = 2.0 ** (m + 2 * kb - 4)
+            p = (7 * m + 13 * kb) % 128
+            x[m, 128 * kb:128 * kb + 128] = s
+            want[m, 128 * kb:128 * kb + 128] = 0x38
+            neg = (m + kb) % 2 == 1
+            x[m, 128 * kb + p] = -448 * s if neg else 448 * s
+            want[m, 128 * kb + p] = 0xFE if neg else 0x7E
+    codes, sa = oracle.quantize_1x128(bf16_bits_exact(x))
+    assert np.array_equal(sa, np.array([[2.0 ** (m + 2 * kb - 4) for kb in range(nkb)]
+                                        for m in range(M)], np.float32))
+    assert np.array_equal(codes, want)
+
+
+def _quant_input(seed, M=37, K=640, lo=-60, hi=60):
+    """bf16 rows of N(0,1) blocks with per-block magnitudes 2^U[lo,hi], a zero block, a block of
+    bf16 subnormals and signed zeros."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    mag = 2.0 ** rng.integers(lo, hi + 1, size=(M, K // 128))
+    x *= np.repeat(mag, 128, axis=1).astype(np.float32)
+    x[3, 128:256] = 0
+    x[5, :128] *= np.float32(2.0 ** -128 / mag[5, 0])
+    x[6, 256:384:3] = -0.0
+    return bf16_bits_rne(x)
+
+
+def test_quantiser_invariants():
+    bits = _quant_input(41)
+    xb = widen(bits).astype(np.float64)
+    codes, sa = oracle.quantize_1x128(bits)
+    M, K = bits.shape
+    dec = _DEC[codes].astype(np.float64)
+    amax = np.abs(xb).reshape(M, -1, 128).max(axis=2)
+    # the block maximum maps to +-448 unless the amax was floored
+    big = amax >= FLOOR
+    assert np.all(np.abs(dec).reshape(M, -1, 128).max(axis=2)[big] == 448)
+    assert np.all(sa[~big] == np.float32(FLOOR / np.float32(448))) and (~big).sum() >= 2
+    # E4M3 rounding error: half a unit in the last place (2^-4 relative for normals, 2^-10 below
+    # 2^-6), plus the fp32 rounding of x/s
+    s = np.repeat(sa.astype(np.float64), 128, axis=1)
+    err = np.abs(dec * s - xb)
+    assert np.all(err <= ((2.0 ** -4 + 2.0 ** -23) * np.abs(xb) + 2.0 ** -10 * s) * (1 + 1e-12))
+    # sign symmetry (zeros included: +0 -> 0x00, -0 -> 0x80)
+    c2, s2 = oracle.quantize_1x128(bits ^ np.uint16(0x8000))
+    assert np.array_equal(c2, codes ^ np.uint8(0x80)) and np.array_equal(s2, sa)
+    assert np.any(codes == 0x80) and np.any(codes == 0x00)
+
+
+def test_quantiser_power_of_two_invariance():
+    """Scaling a row by 2^j scales every block's scale by 2^j and leaves the codes unchanged
+    (magnitudes kept away from the floor and from bf16's range limits)."""
+    bits = np.delete(_quant_input(42, lo=-4, hi=20), [3, 5, 6], axis=0)
+    amax = np.abs(widen(bits)).reshape(bits.shape[0], -1, 128).max(axis=2)
+    assert amax.min() * 2.0 ** -7 > 2 * FLOOR
+    codes, sa = oracle.quantize_1x128(bits)
+    for j in (-7, 3, 11):
+        b2 = bf16_bits_exact(widen(bits) * np.float32(2.0 ** j))
+        c2, s2 = oracle.quantize_1x128(b2)
+        assert np.array_equal(c2, codes)
+        assert np.array_equal(s2, sa * np.float32(2.0 ** j))
+
+
+def test_quantiser_matches_library_composition():
+    """Whole quantiser against the input recipe built from torch's fp32 division and float8 cast."""
+    bits = _quant_input(43, M=64, K=1024)
+    codes, sa = oracle.quantize_1x128(bits)
+    c2, s2 = W.quantize_1x128(widen(bits))
+    assert np.array_equal(codes, c2) and np.array_equal(sa, s2)

@@ -8,8 +8,8 @@ GEMM arithmetic; the oracle and the HIP library both consume the bytes produced 
 Quantisation recipe (input preparation; the pages only say "fine-grained scaling", page
 "DeepSeek開源第三彈：V3/R1訓練推理關鍵秘籍，核心代碼僅300行", section 深入了解DeepGEMM):
   * A (activations) has one scale per 1x128 block of a row, B (weights) one per 128x128 block.
-  * scale = fp32(amax / 448) over the block (448 = largest finite E4M3 value); a block whose
-    amax is 0 uses amax = 1e-4 so that its scale stays finite (its codes are all zero anyway).
+  * scale = fp32(amax / 448) over the block (448 = largest finite E4M3 value); the amax is
+    floored at fp32(1e-4) so that an all-zero block keeps a finite scale (its codes are zero).
   * code = E4M3 round-to-nearest-even of fp32(x / scale), saturated to +-448 first (torch's
     cast would give NaN above 464; saturating is the plain quantiser).
 The float8 cast is torch's library routine; random numbers come from numpy's PCG64
@@ -93,8 +93,7 @@ def quantize_1x128(x: np.ndarray, chunk_rows: int = 8192):
         if K % BLOCK:
             t = torch.nn.functional.pad(t, (0, nkb * BLOCK - K))
         tb = t.view(r1 - r0, nkb, BLOCK)
-        amax = tb.abs().amax(dim=2)
-        amax = torch.where(amax > 0, amax, torch.full_like(amax, 1e-4))
+        amax = tb.abs().amax(dim=2).clamp_min(1e-4)
         s = amax / E4M3_MAX
         q = _cast_e4m3(tb / s.unsqueeze(2)).reshape(r1 - r0, nkb * BLOCK)[:, :K]
         codes[r0:r1] = q.numpy()
@@ -115,8 +114,7 @@ def quantize_128x128(x: np.ndarray):
         if K % BLOCK:
             t = torch.nn.functional.pad(t, (0, nkb * BLOCK - K))
         tb = t.view(r1 - r0, nkb, BLOCK)
-        amax = tb.abs().amax(dim=(0, 2))
-        amax = torch.where(amax > 0, amax, torch.full_like(amax, 1e-4))
+        amax = tb.abs().amax(dim=(0, 2)).clamp_min(1e-4)
         s = amax / E4M3_MAX
         q = _cast_e4m3(tb / s.view(1, nkb, 1)).reshape(r1 - r0, nkb * BLOCK)[:, :K]
         codes[r0:r1] = q.numpy()
