@@ -6,6 +6,8 @@ C ABI declared in include/fp8gemm.h.  torch supplies device memory and the curre
     D = gemm_nt(A, sa, B, sb)                              # dense NT, bf16 out
     D = grouped_contiguous(A, sa, B, sb, m_indices)        # MoE, groups concatenated along M
     D = grouped_masked(A, sa, B, sb, masked_m, expected_m) # MoE, fixed per-group capacity
+    A, sa = quantize_1x128(X)                              # bf16 activations -> codes + scales
+    A, sa = quantize_1x128_masked(X, masked_m)             # the same, masked layout
 
 A and B are E4M3 codes (torch.float8_e4m3fn or uint8), sa one fp32 scale per 1x128 block of a
 row of A stored K-block-major (sa[kb, m], shape [K/128, M]), sb one per 128x128 block of B (page "DeepSeek開源第三彈：V3/R1訓練推理關鍵秘籍，核心代碼僅
@@ -17,7 +19,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gemm_nt", "grouped_contiguous", "grouped_masked", "init", "set_num_cus",
+__all__ = ["gemm_nt", "grouped_contiguous", "grouped_masked", "quantize_1x128",
+           "quantize_1x128_masked", "init", "set_num_cus",
            "last_config", "read_device_error", "status_string", "lib", "library_path",
            "Fp8GemmError", "STATUS", "DEVERR_BAD_INDEX", "DEVERR_BAD_COUNT"]
 
@@ -37,6 +40,8 @@ SIGNATURES = {
     "fp8gemm_nt": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "fp8gemm_grouped_contiguous": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P]),
     "fp8gemm_grouped_masked": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _P]),
+    "fp8gemm_quantize_1x128": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "fp8gemm_quantize_1x128_masked": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _P]),
     "fp8gemm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fp8gemm_init": (ctypes.c_int, []),
     "fp8gemm_set_num_cus": (ctypes.c_int, [ctypes.c_int]),
@@ -224,3 +229,58 @@ def grouped_masked(A, sa, B, sb, masked_m, expected_m: int, out=None, stream=Non
                                           int(expected_m), _stream(stream, A.device))
     _check(st, "fp8gemm_grouped_masked")
     return D
+
+
+def _bf16(t, name):
+    torch = _torch()
+    if t.dtype != torch.bfloat16:
+        raise TypeError("%s must be bfloat16, got %s" % (name, t.dtype))
+    return _dev_contig(t, name)
+
+
+def _quant_outputs(codes, scales, codes_shape, scales_shape, device):
+    torch = _torch()
+    if codes is None:
+        codes = torch.empty(codes_shape, dtype=torch.float8_e4m3fn, device=device)
+    if scales is None:
+        scales = torch.empty(scales_shape, dtype=torch.float32, device=device)
+    codes, scales = _codes(codes, "codes"), _f32(scales, "scales")
+    _shape_check(tuple(codes.shape) == tuple(codes_shape) and tuple(scales.shape) == tuple(scales_shape),
+                 "codes %s, scales %s" % (tuple(codes_shape), tuple(scales_shape)))
+    return codes, scales
+
+
+def quantize_1x128(X, codes=None, scales=None, stream=None):
+    """Activations X bf16 [M,K] -> (E4M3 codes [M,K], scales fp32 [K/128,M]), one scale per 1x128
+    block of a row, in the layout gemm_nt and grouped_contiguous take as A and sa."""
+    torch = _torch()
+    X = _bf16(X, "X")
+    _shape_check(X.dim() == 2, "X [M,K]")
+    M, K = X.shape
+    codes, scales = _quant_outputs(codes, scales, (M, K), (K // 128, M), X.device)
+    with torch.cuda.device(X.device):
+        st = lib().fp8gemm_quantize_1x128(X.data_ptr(), codes.data_ptr(), scales.data_ptr(), M, K,
+                                          _stream(stream, X.device))
+    _check(st, "fp8gemm_quantize_1x128")
+    return codes, scales
+
+
+def quantize_1x128_masked(X, masked_m, codes=None, scales=None, stream=None):
+    """Masked layout: X bf16 [G,M_max,K] -> (codes [G,M_max,K], scales [G,K/128,M_max]); rows at or
+    past masked_m[g] are not written (zeros when the outputs are allocated here)."""
+    torch = _torch()
+    X = _bf16(X, "X")
+    masked_m = _i32(masked_m, "masked_m")
+    _shape_check(X.dim() == 3 and tuple(masked_m.shape) == (X.shape[0],), "X [G,M_max,K], masked_m [G]")
+    G, M_max, K = X.shape
+    if codes is None:
+        codes = torch.zeros((G, M_max, K), dtype=torch.uint8, device=X.device).view(torch.float8_e4m3fn)
+    if scales is None:
+        scales = torch.zeros((G, K // 128, M_max), dtype=torch.float32, device=X.device)
+    codes, scales = _quant_outputs(codes, scales, (G, M_max, K), (G, K // 128, M_max), X.device)
+    with torch.cuda.device(X.device):
+        st = lib().fp8gemm_quantize_1x128_masked(X.data_ptr(), codes.data_ptr(), scales.data_ptr(),
+                                                 masked_m.data_ptr(), G, M_max, K,
+                                                 _stream(stream, X.device))
+    _check(st, "fp8gemm_quantize_1x128_masked")
+    return codes, scales

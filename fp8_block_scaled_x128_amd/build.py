@@ -19,7 +19,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfp8gemm.so")
-SOURCES = [os.path.join(CSRC, "fp8gemm_kernels.hip"), os.path.join(CSRC, "fp8gemm_api.cpp")]
+SOURCES = [os.path.join(CSRC, "fp8gemm_kernels.hip"), os.path.join(CSRC, "quantize_kernels.hip"),
+           os.path.join(CSRC, "fp8gemm_api.cpp")]
+DEVICE_SOURCES = [p for p in SOURCES if p.endswith(".hip")]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU ops are kept out of the device code on purpose.
@@ -67,10 +69,11 @@ def build(verbose: bool = False) -> str:
     try:
         _run([HIPCC, "--offload-arch=" + ARCH] + COMMON + DEVICE_FLAGS + ["-shared", "-o", tmp] + SOURCES)
         with tempfile.TemporaryDirectory() as td:
-            asm = os.path.join(td, "kernels.s")
-            _run([HIPCC, "--offload-arch=" + ARCH] + COMMON + DEVICE_FLAGS +
-                 ["--cuda-device-only", "-S", "-o", asm, SOURCES[0]])
-            check_isa(open(asm).read())
+            for src in DEVICE_SOURCES:
+                asm = os.path.join(td, os.path.basename(src) + ".s")
+                _run([HIPCC, "--offload-arch=" + ARCH] + COMMON + DEVICE_FLAGS +
+                     ["--cuda-device-only", "-S", "-o", asm, src])
+                check_isa(open(asm).read())
         os.replace(tmp, LIB)
     finally:
         if os.path.exists(tmp):

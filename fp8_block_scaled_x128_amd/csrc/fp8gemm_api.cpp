@@ -274,9 +274,62 @@ int check_k(int64_t K) {
     return FP8GEMM_OK;
 }
 
+// Shared launch of the activation quantiser over G groups of `rows` rows.
+int quantize(const void* X, void* A, float* sa, const int32_t* masked_m, int32_t G, int64_t rows,
+             int64_t K, hipStream_t stream) {
+    DeviceState* d = nullptr;
+    int st = device_state(&d);
+    if (st != FP8GEMM_OK) return st;
+    QuantArgs q{};
+    q.X = static_cast<const uint16_t*>(X);
+    q.A = static_cast<uint8_t*>(A);
+    q.sa = sa;
+    q.masked_m = masked_m;
+    q.err = d->err;
+    q.rows = rows;
+    q.K = (int32_t)K;
+    q.nkb = (int32_t)(K / 128);
+    q.G = G;
+    q.row_groups = (int32_t)((rows + kQuantRowsPerWG - 1) / kQuantRowsPerWG);
+    q.div_row_groups = make_fastdiv((uint32_t)q.row_groups);
+    const int64_t gx = (int64_t)G * q.row_groups;
+    const int64_t gy = (q.nkb + kQuantBlocksPerWG - 1) / kQuantBlocksPerWG;
+    if (gx >= (int64_t(1) << 31) || gy > 65535) return FP8GEMM_ERR_UNSUPPORTED;
+    std::snprintf(g_last_config, sizeof g_last_config, "quantize_1x128 tile=%dx%d grid=%lldx%lld",
+                  kQuantRowsPerWG, kQuantBlocksPerWG * 128, (long long)gx, (long long)gy);
+    launch_quantize_1x128(q, dim3((unsigned)gx, (unsigned)gy), stream);
+    if (hipGetLastError() != hipSuccess) return FP8GEMM_ERR_LAUNCH;
+    return FP8GEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int fp8gemm_quantize_1x128(const void* X, void* A, float* sa, int64_t M, int64_t K, void* stream) {
+    if (M < 0) return FP8GEMM_ERR_BAD_SHAPE;
+    int st = check_k(K);
+    if (st != FP8GEMM_OK) return st;
+    if (M > kMaxRows || 2 * M * K >= kMaxBytes) return FP8GEMM_ERR_UNSUPPORTED;
+    if (M == 0) return FP8GEMM_OK;
+    if (!X || !A || !sa) return FP8GEMM_ERR_NULL_PTR;
+    if (!aligned(X, 16) || !aligned(A, 16) || !aligned(sa, 4)) return FP8GEMM_ERR_MISALIGNED;
+    return quantize(X, A, sa, nullptr, 1, M, K, static_cast<hipStream_t>(stream));
+}
+
+int fp8gemm_quantize_1x128_masked(const void* X, void* A, float* sa, const int32_t* masked_m,
+                                  int32_t G, int64_t M_max, int64_t K, void* stream) {
+    if (G <= 0 || M_max < 0) return FP8GEMM_ERR_BAD_SHAPE;
+    int st = check_k(K);
+    if (st != FP8GEMM_OK) return st;
+    if ((int64_t)G * M_max > kMaxRows || 2 * (int64_t)G * M_max * K >= kMaxBytes)
+        return FP8GEMM_ERR_UNSUPPORTED;
+    if (M_max == 0) return FP8GEMM_OK;
+    if (!X || !A || !sa || !masked_m) return FP8GEMM_ERR_NULL_PTR;
+    if (!aligned(X, 16) || !aligned(A, 16) || !aligned(sa, 4) || !aligned(masked_m, 4))
+        return FP8GEMM_ERR_MISALIGNED;
+    return quantize(X, A, sa, masked_m, G, M_max, K, static_cast<hipStream_t>(stream));
+}
 
 int fp8gemm_nt(const void* A, const float* sa, const void* B, const float* sb, void* D, int64_t M,
                int64_t N, int64_t K, void* stream) {

@@ -77,4 +77,23 @@ struct KernelEntry {
 
 const KernelEntry* kernel_table(int* count);
 
+// 1x128 activation quantiser: a workgroup covers kQuantRowsPerWG rows x kQuantBlocksPerWG
+// 128-wide K blocks; grid = (G * row_groups, ceil(nkb / kQuantBlocksPerWG)).
+constexpr int kQuantRowsPerWG = 16;
+constexpr int kQuantBlocksPerWG = 4;
+
+struct QuantArgs {
+    const uint16_t* X;          // [G][rows][K] bf16 bits
+    uint8_t* A;                 // [G][rows][K] E4M3 codes
+    float* sa;                  // [G][nkb][rows]
+    const int32_t* masked_m;    // [G] valid rows per group, or null (all rows)
+    int32_t* err;               // device error word (FP8GEMM_DEVERR_BAD_COUNT)
+    int64_t rows;               // rows per group
+    int32_t K, nkb, G;
+    int32_t row_groups;         // ceil(rows / kQuantRowsPerWG)
+    FastDiv div_row_groups;
+};
+
+void launch_quantize_1x128(const QuantArgs& a, dim3 grid, hipStream_t stream);
+
 }  // namespace fp8gemm

@@ -92,9 +92,31 @@ int fp8gemm_grouped_masked(const void* A, const float* sa, const void* B, const 
                            const int32_t* masked_m, void* D, int32_t G, int64_t M_max, int64_t N,
                            int64_t K, int64_t expected_m, void* stream);
 
+/* Activation quantiser, 1x128 blocks: the step that produces the left operand and its scales.
+ * The pages take fine-grained scaling from DeepSeek V3 (page "DeepSeek開源第三彈…", section
+ * 深入了解DeepGEMM) and give no quantiser; this one is the plain reading of a 1x128 block scale.
+ * For every block of 128 consecutive K values of a row of X:
+ *   amax = max |x| over the block, floored at fp32(1e-4) (an all-zero block keeps a finite scale)
+ *   s    = fp32(amax / 448)                   (448: the largest finite E4M3 value)
+ *   code = E4M3 round-to-nearest-even of fp32(x / s), saturated to +-448
+ * so the largest element of every block is coded +-448 and code * s approximates x.
+ *   X  [M][K] bfloat16 (device), A [M][K] e4m3 codes (device, written), sa [K/128][M] fp32
+ *   (device, written; the K-block-major scale layout fp8gemm_nt and fp8gemm_grouped_contiguous
+ *   read).  K: positive multiple of 128 (else FP8GEMM_ERR_BAD_SHAPE); M == 0 is a no-op.
+ *   X and A 16-byte aligned, sa 4-byte aligned (else FP8GEMM_ERR_MISALIGNED).  X must hold
+ *   finite values: a NaN or infinity gives unspecified codes and scales for its block. */
+int fp8gemm_quantize_1x128(const void* X, void* A, float* sa, int64_t M, int64_t K, void* stream);
+
+/* The same quantiser for the masked layout (see fp8gemm_grouped_masked): X and A [G][M_max][K],
+ * sa [G][K/128][M_max], masked_m [G] int32 (device).  Rows r < masked_m[g] of group g are
+ * quantised; A and sa entries of the rows at or past it are left untouched.  A count outside
+ * [0, M_max] is clamped and flags FP8GEMM_DEVERR_BAD_COUNT.  G <= 0 is FP8GEMM_ERR_BAD_SHAPE. */
+int fp8gemm_quantize_1x128_masked(const void* X, void* A, float* sa, const int32_t* masked_m,
+                                  int32_t G, int64_t M_max, int64_t K, void* stream);
+
 /* Device-side precondition flags (bits of the device error word). */
 #define FP8GEMM_DEVERR_BAD_INDEX 1 /* contiguous: an m_indices entry outside [-1, G) or off its block's group */
-#define FP8GEMM_DEVERR_BAD_COUNT 2 /* masked: a masked_m entry outside [0, M_max] */
+#define FP8GEMM_DEVERR_BAD_COUNT 2 /* masked GEMM or quantiser: a masked_m entry outside [0, M_max] */
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* fp8gemm_status_string(int status);

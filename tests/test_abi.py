@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp8gemm_nt", "fp8gemm_grouped_contiguous", "fp8gemm_grouped_masked",
               "fp8gemm_status_string", "fp8gemm_init", "fp8gemm_set_num_cus",
-              "fp8gemm_last_config", "fp8gemm_read_device_error"):
+              "fp8gemm_last_config", "fp8gemm_read_device_error", "fp8gemm_quantize_1x128",
+              "fp8gemm_quantize_1x128_masked"):
         assert n in names
     assert set(names) == set(fg.SIGNATURES)
 
@@ -81,6 +82,29 @@ def test_grouped_validation_errors(lib):
     assert mg(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0, 64, 128, 8, None) == 0
 
 
+def test_quantiser_validation_errors(lib):
+    q = lib.fp8gemm_quantize_1x128
+    assert q(FAKE, FAKE, FAKE, -1, 128, None) == 2
+    assert q(FAKE, FAKE, FAKE, 8, 100, None) == 2          # K not a multiple of 128
+    assert q(FAKE, FAKE, FAKE, 8, 0, None) == 2
+    assert q(FAKE, FAKE, FAKE, 8, 1 << 25, None) == 4
+    assert q(FAKE, FAKE, FAKE, 1 << 31, 128, None) == 4    # rows beyond the supported range
+    assert q(None, None, None, 0, 128, None) == 0          # empty: a valid no-op
+    assert q(None, FAKE, FAKE, 8, 128, None) == 1
+    assert q(FAKE, None, FAKE, 8, 128, None) == 1
+    assert q(FAKE, FAKE, None, 8, 128, None) == 1
+    assert q(FAKE + 8, FAKE, FAKE, 8, 128, None) == 3
+    assert q(FAKE, FAKE + 8, FAKE, 8, 128, None) == 3
+    assert q(FAKE, FAKE, FAKE + 2, 8, 128, None) == 3
+    qm = lib.fp8gemm_quantize_1x128_masked
+    assert qm(FAKE, FAKE, FAKE, FAKE, 0, 64, 128, None) == 2     # G <= 0
+    assert qm(FAKE, FAKE, FAKE, FAKE, 2, -1, 128, None) == 2
+    assert qm(FAKE, FAKE, FAKE, FAKE, 2, 64, 200, None) == 2
+    assert qm(FAKE, FAKE, FAKE, FAKE, 2, 0, 128, None) == 0
+    assert qm(FAKE, FAKE, FAKE, None, 2, 64, 128, None) == 1     # masked_m
+    assert qm(FAKE, FAKE, FAKE, FAKE + 2, 2, 64, 128, None) == 3
+
+
 def test_knobs(lib):
     assert lib.fp8gemm_set_num_cus(-3) == 2
     assert lib.fp8gemm_set_num_cus(64) == 0
@@ -100,3 +124,9 @@ def test_binding_rejects_bad_tensors():
     sa = torch.zeros((4, 1), dtype=torch.float32)
     with pytest.raises(ValueError):          # host tensors are refused: no CPU path exists
         fg.gemm_nt(A8, sa, A8, sa)
+
+    X = torch.zeros((4, 128), dtype=torch.float32)
+    with pytest.raises(TypeError):           # activations must be bf16
+        fg.quantize_1x128(X)
+    with pytest.raises(ValueError):
+        fg.quantize_1x128(X.to(torch.bfloat16))

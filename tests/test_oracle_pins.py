@@ -366,12 +366,6 @@ def bf16_bits_exact(x) -> np.ndarray:
     return (b >> 16).astype(np.uint16)
 
 
-def bf16_bits_rne(x) -> np.ndarray:
-    """fp32 -> bf16 bit patterns, round to nearest even (torch's cast)."""
-    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
-    return t.view(torch.int16).numpy().view(np.uint16)
-
-
 def widen(bits) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
@@ -460,16 +454,7 @@ def test_quantiser_scale_layout_closed_form():
 
 
 def _quant_input(seed, M=37, K=640, lo=-60, hi=60):
-    """bf16 rows of N(0,1) blocks with per-block magnitudes 2^U[lo,hi], a zero block, a block of
-    bf16 subnormals and signed zeros."""
-    rng = np.random.default_rng(seed)
-    x = rng.standard_normal((M, K)).astype(np.float32)
-    mag = 2.0 ** rng.integers(lo, hi + 1, size=(M, K // 128))
-    x *= np.repeat(mag, 128, axis=1).astype(np.float32)
-    x[3, 128:256] = 0
-    x[5, :128] *= np.float32(2.0 ** -128 / mag[5, 0])
-    x[6, 256:384:3] = -0.0
-    return bf16_bits_rne(x)
+    return W.stress_bf16(M, K, seed, lo=lo, hi=hi)
 
 
 def test_quantiser_invariants():

@@ -253,6 +253,56 @@ def config4() -> Masked:
     return masked(config4_masked_m(), 256, 4096, 7168, seed=4, expected_m=64)
 
 
+# --- bf16 activations: inputs of the 1x128 quantiser -----------------------------------------
+
+#: Activation matrix quantised in the benchmark: the left operand of the contiguous MoE
+#: configuration (32768 rows of K=7168).
+QUANT_M, QUANT_K = 32768, 7168
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even (torch's cast)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def activations_bf16(M: int, K: int, seed: int, chunk_rows: int = 4096) -> np.ndarray:
+    """Hidden-state-like bf16 activations [M,K] (bit patterns): N(0,1) times a per-channel gain,
+    where 1% of the channels (chosen by the seed) carry a gain of 32 -- the outlier channels that
+    make one scale per 128 values worth having."""
+    rng = np.random.default_rng(seed)
+    gain = np.ones(K, dtype=np.float32)
+    gain[rng.choice(K, size=max(1, K // 100), replace=False)] = 32.0
+    out = np.empty((M, K), dtype=np.uint16)
+    for r0 in range(0, M, chunk_rows):
+        r1 = min(M, r0 + chunk_rows)
+        out[r0:r1] = bf16_bits(normal(rng, (r1 - r0, K)) * gain)
+    return out
+
+
+def stress_bf16(M: int, K: int, seed: int, lo: int = -60, hi: int = 60) -> np.ndarray:
+    """bf16 rows [M,K] (bit patterns) whose 128-wide blocks span magnitudes 2^U[lo,hi] (N(0,1)
+    values times a per-block power of two), with, where the shape has room, an all-zero block
+    (row 3, block 1), a block of bf16 subnormals (row 5, block 0) and signed zeros (row 6)."""
+    rng = np.random.default_rng(seed)
+    nkb = -(-K // BLOCK)
+    x = normal(rng, (M, K))
+    mag = 2.0 ** rng.integers(lo, hi + 1, size=(M, nkb))
+    x *= np.repeat(mag, BLOCK, axis=1)[:, :K].astype(np.float32)
+    if M > 3 and nkb > 1:
+        x[3, BLOCK:2 * BLOCK] = 0
+    if M > 5:
+        x[5, :BLOCK] *= np.float32(2.0 ** -128 / mag[5, 0])
+    if M > 6:
+        x[6, ::3] = -0.0
+    return bf16_bits(x)
+
+
+def quantize_work(rows: int, K: int):
+    """Bytes the 1x128 quantiser must move: bf16 in, E4M3 codes and fp32 scales out."""
+    return rows * K * 2 + rows * K + 4 * rows * (-(-K // BLOCK))
+
+
 # --- algorithmic work counts (for throughput and roofline reporting) --------------------------
 
 def dense_work(M, N, K):
