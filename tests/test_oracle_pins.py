@@ -433,15 +433,16 @@ def test_quantiser_golden_blocks(golden_dir):
 
 
 def test_quantiser_scale_layout_closed_form():
-    """Block (m, kb) holds 2^(m+2kb-4) everywhere but one position, which holds 448 times that
-    (negative for odd m+kb): sa[m][kb] = 2^(m+2kb-4), codes 0x38 (1.0) and 0x7E / 0xFE."""
+    """Block (m, kb) holds 2^(m+2kb-4) everywhere but one position (the block's last for a third
+    of the blocks), which holds 448 times that (negative for odd m+kb): sa[m][kb] = 2^(m+2kb-4),
+    codes 0x38 (1.0) and 0x7E / 0xFE."""
     M, nkb = 3, 3
     x = np.zeros((M, 128 * nkb), dtype=np.float32)
     want = np.zeros_like(x, dtype=np.uint8)
     for m in range(M):
         for kb in range(nkb):
             s = 2.0 ** (m + 2 * kb - 4)
-            p = (7 * m + 13 * kb) % 128
+            p = 127 if (m + kb) % 3 == 0 else (7 * m + 13 * kb) % 128
             x[m, 128 * kb:128 * kb + 128] = s
             want[m, 128 * kb:128 * kb + 128] = 0x38
             neg = (m + kb) % 2 == 1
@@ -459,15 +460,24 @@ def _quant_input(seed, M=37, K=640, lo=-60, hi=60):
 
 def test_quantiser_invariants():
     bits = _quant_input(41)
+    M, K = bits.shape
+    # a few blocks whose largest element is their last or their first
+    x = widen(bits).copy()
+    for m, kb, pos in ((0, 0, 127), (1, 2, 127), (2, 4, 0), (4, 3, 64)):
+        blk = x[m, 128 * kb:128 * kb + 128]
+        blk[pos] = -3 * np.abs(blk).max()
+    bits = W.bf16_bits(x)
     xb = widen(bits).astype(np.float64)
     codes, sa = oracle.quantize_1x128(bits)
-    M, K = bits.shape
     dec = _DEC[codes].astype(np.float64)
     amax = np.abs(xb).reshape(M, -1, 128).max(axis=2)
     # the block maximum maps to +-448 unless the amax was floored
     big = amax >= FLOOR
     assert np.all(np.abs(dec).reshape(M, -1, 128).max(axis=2)[big] == 448)
     assert np.all(sa[~big] == np.float32(FLOOR / np.float32(448))) and (~big).sum() >= 2
+    # no element is clipped by the saturation beyond the rounding of the scale
+    ratio = np.abs(xb).reshape(M, -1, 128).max(axis=2) / sa.astype(np.float64)
+    assert np.all(ratio <= 448 * (1 + 2.0 ** -22))
     # E4M3 rounding error: half a unit in the last place (2^-4 relative for normals, 2^-10 below
     # 2^-6), plus the fp32 rounding of x/s
     s = np.repeat(sa.astype(np.float64), 128, axis=1)
