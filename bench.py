@@ -20,6 +20,9 @@ Prints ONE JSON line:
   roofline     the dominant kernel (largest share of the step's time): algorithmic flop per
                launch / average launch time, against the 5.0 PFLOP/s dense FP8 peak
   grouped      the contiguous and masked MoE configurations (context, not part of value)
+  quantize_1x128  the bf16 -> E4M3 1x128 activation quantiser on the contiguous configuration's
+               activations (32768 x 7168) and the masked decode configuration's, with its own
+               HBM roofline (context, not part of value)
   cpu_baseline the CPU oracle on a bounded sample of the same workload on this host's cores
 """
 from __future__ import annotations
@@ -252,6 +255,7 @@ def main():
     if not args.no_grouped:
         del flush
         grouped = bench_grouped(fg, W, torch, dev, stream)
+    quantize = bench_quantize(fg, W, torch, dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -280,6 +284,7 @@ def main():
         "cpu_baseline": cpu,
         "per_shape": per,
         "grouped": grouped,
+        "quantize_1x128": quantize,
     }
     print(json.dumps(line), flush=True)
 
@@ -433,6 +438,97 @@ def bench_grouped(fg, W, torch, dev, stream, reps=10):
                                                                             time.time() - t0))
         del A, sa, B, sb, D, flush, g
         torch.cuda.empty_cache()
+    return out
+
+
+QUANT_LAUNCHES = 16    # launches per timed graph of the quantiser (two operand copies alternate)
+
+
+def bench_quantize(fg, W, torch, dev, stream, reps=5):
+    """The 1x128 activation quantiser on the contiguous MoE configuration's activations
+    (32768 x 7168 bf16) and on the masked decode configuration's (16 groups x 256 rows, about
+    64 valid per group), against the HBM roofline: algorithmic bytes = 2 (bf16 in) + 1 (code
+    out) per element + 4 per 128-element scale, over the average launch time.  Launch times come
+    from HIP events on the launch stream around a graph of QUANT_LAUNCHES launches that alternate
+    between two copies of every operand (940 MB of input for the dense case, well past the 256 MB
+    last-level cache), after reading a 1 GiB buffer."""
+    import oracle
+
+    out = {}
+    M, K = W.QUANT_M, W.QUANT_K
+    t0 = time.time()
+    bits = W.activations_bf16(M, K, seed=31)
+    X0 = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    Xs = [X0, X0.clone()]
+    codes = [torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev) for _ in range(2)]
+    scales = [torch.empty((K // 128, M), dtype=torch.float32, device=dev) for _ in range(2)]
+    mm = W.config4_masked_m()
+    G, M_max = len(mm), 256
+    Xm = [x[:G * M_max].view(G, M_max, K) for x in Xs]
+    mm_dev = torch.from_numpy(mm).to(dev)
+    codes_m = [torch.empty((G, M_max, K), dtype=torch.float8_e4m3fn, device=dev) for _ in range(2)]
+    scales_m = [torch.empty((G, K // 128, M_max), dtype=torch.float32, device=dev) for _ in range(2)]
+    flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1, device=dev)
+
+    def dense(i):
+        fg.quantize_1x128(Xs[i], codes=codes[i], scales=scales[i], stream=stream)
+
+    def masked(i):
+        fg.quantize_1x128_masked(Xm[i], mm_dev, codes=codes_m[i], scales=scales_m[i], stream=stream)
+
+    legs = (("dense_32768x7168", dense, W.quantize_work(M, K)),
+            ("masked_16x256x7168", masked, W.quantize_work(int(mm.sum()), K)))
+    for name, call, byts in legs:
+        with torch.cuda.stream(stream):
+            call(0)
+            call(1)
+        cfg = fg.last_config()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(QUANT_LAUNCHES):
+                call(i % 2)
+        ts = []
+        for _ in range(reps):
+            with torch.cuda.stream(stream):
+                sink.add_(flush.sum())
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+            stream.synchronize()
+            ts.append(e0.elapsed_time(e1) / QUANT_LAUNCHES)
+        ms = float(np.mean(ts))
+        gbs = byts / (ms * 1e-3) / 1e9
+        out[name] = dict(us=round(ms * 1e3, 2), bytes=byts, gbs=round(gbs, 1),
+                         frac_hbm=round(gbs / PEAK_HBM_GBS, 4), config=cfg,
+                         launches_per_graph=QUANT_LAUNCHES)
+        log("quantize %s: %.2f us per launch, %.1f GB/s (%s)" % (name, ms * 1e3, gbs, cfg))
+        del g
+    # the product of the timed launches must equal the oracle's on a sample of rows
+    rows = np.arange(0, M, 977)
+    ref_c, ref_s = oracle.quantize_1x128(bits[rows])
+    idx = torch.from_numpy(rows).to(dev)
+    for i in range(2):
+        got_c = codes[i].view(torch.uint8)[idx].cpu().numpy()
+        got_s = scales[i][:, idx].cpu().numpy().T
+        if not (np.array_equal(got_c, ref_c) and np.array_equal(got_s, ref_s)):
+            raise RuntimeError("quantiser output differs from the oracle on sampled rows")
+    d = out["dense_32768x7168"]
+    d["roofline"] = dict(bound="hbm", achieved=d["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+                         frac=d["frac_hbm"], traffic=None)
+    # the oracle on a bounded sample of the same matrix (context)
+    nth = oracle.num_threads(0)
+    r = min(M, 8192)
+    t1 = time.perf_counter()
+    oracle.quantize_1x128(bits[:r])
+    dt = time.perf_counter() - t1
+    d["cpu_oracle"] = dict(value=round(W.quantize_work(r, K) / dt / 1e9, 3), unit="GB/s", cores=nth,
+                           sample="first %d rows of the 32768 x 7168 matrix in %.2f s" % (r, dt))
+    log("quantiser legs done in %.1f s" % (time.time() - t0))
+    del Xs, Xm, codes, scales, codes_m, scales_m, flush
+    torch.cuda.empty_cache()
     return out
 
 

@@ -277,6 +277,9 @@ int check_k(int64_t K) {
 // Shared launch of the activation quantiser over G groups of `rows` rows.
 int quantize(const void* X, void* A, float* sa, const int32_t* masked_m, int32_t G, int64_t rows,
              int64_t K, hipStream_t stream) {
+    const int64_t nkb = K / 128;
+    const int64_t blocks = (int64_t)G * rows * nkb;
+    if (blocks >= (int64_t(1) << 31)) return FP8GEMM_ERR_UNSUPPORTED;  // block ids stay below 2^31
     DeviceState* d = nullptr;
     int st = device_state(&d);
     if (st != FP8GEMM_OK) return st;
@@ -286,18 +289,18 @@ int quantize(const void* X, void* A, float* sa, const int32_t* masked_m, int32_t
     q.sa = sa;
     q.masked_m = masked_m;
     q.err = d->err;
-    q.rows = rows;
+    q.rows = (int32_t)rows;
     q.K = (int32_t)K;
-    q.nkb = (int32_t)(K / 128);
+    q.nkb = (int32_t)nkb;
     q.G = G;
-    q.row_groups = (int32_t)((rows + kQuantRowsPerWG - 1) / kQuantRowsPerWG);
-    q.div_row_groups = make_fastdiv((uint32_t)q.row_groups);
-    const int64_t gx = (int64_t)G * q.row_groups;
-    const int64_t gy = (q.nkb + kQuantBlocksPerWG - 1) / kQuantBlocksPerWG;
-    if (gx >= (int64_t(1) << 31) || gy > 65535) return FP8GEMM_ERR_UNSUPPORTED;
-    std::snprintf(g_last_config, sizeof g_last_config, "quantize_1x128 tile=%dx%d grid=%lldx%lld",
-                  kQuantRowsPerWG, kQuantBlocksPerWG * 128, (long long)gx, (long long)gy);
-    launch_quantize_1x128(q, dim3((unsigned)gx, (unsigned)gy), stream);
+    q.blocks = (uint32_t)blocks;
+    q.div_nkb = make_fastdiv((uint32_t)nkb);
+    q.div_rows = make_fastdiv((uint32_t)rows);
+    const int64_t wgs = (blocks + kQuantBlocksPerWG - 1) / kQuantBlocksPerWG;
+    const int64_t grid = (wgs + 7) / 8 * 8;
+    std::snprintf(g_last_config, sizeof g_last_config, "quantize_1x128 blocks_per_wg=%d grid=%lld",
+                  kQuantBlocksPerWG, (long long)grid);
+    launch_quantize_1x128(q, dim3((unsigned)grid), stream);
     if (hipGetLastError() != hipSuccess) return FP8GEMM_ERR_LAUNCH;
     return FP8GEMM_OK;
 }

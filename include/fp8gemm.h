@@ -52,8 +52,9 @@ typedef enum fp8gemm_status {
     FP8GEMM_ERR_NULL_PTR = 1,    /* a required pointer is NULL */
     FP8GEMM_ERR_BAD_SHAPE = 2,   /* negative size, K not a positive multiple of 128, G <= 0, expected_m < 0 */
     FP8GEMM_ERR_MISALIGNED = 3,  /* A, B or D not 16-byte aligned, or a scale/index vector not 4-byte aligned */
-    FP8GEMM_ERR_UNSUPPORTED = 4, /* a size beyond the supported range (an operand of 2^40 bytes or more, K >= 2^31,
-                                    2^30 or more output tiles x K splits in one launch) */
+    FP8GEMM_ERR_UNSUPPORTED = 4, /* a size beyond the supported range (an operand of 2^40 bytes or more, K > 2^24,
+                                    2^30 or more output tiles x K splits in one launch, 2^31 or more
+                                    128-value blocks in one quantiser call) */
     FP8GEMM_ERR_LAUNCH = 5,      /* the HIP launch failed (hipGetLastError after the launch) */
     FP8GEMM_ERR_HIP = 6          /* a HIP runtime call failed (device query, workspace allocation, copy) */
 } fp8gemm_status;

@@ -89,6 +89,7 @@ def test_quantiser_validation_errors(lib):
     assert q(FAKE, FAKE, FAKE, 8, 0, None) == 2
     assert q(FAKE, FAKE, FAKE, 8, 1 << 25, None) == 4
     assert q(FAKE, FAKE, FAKE, 1 << 31, 128, None) == 4    # rows beyond the supported range
+    assert q(FAKE, FAKE, FAKE, 1 << 24, 1 << 14, None) == 4  # 2^31 blocks of 128 values
     assert q(None, None, None, 0, 128, None) == 0          # empty: a valid no-op
     assert q(None, FAKE, FAKE, 8, 128, None) == 1
     assert q(FAKE, None, FAKE, 8, 128, None) == 1
