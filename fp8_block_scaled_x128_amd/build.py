@@ -19,8 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfp8gemm.so")
-SOURCES = [os.path.join(CSRC, "fp8gemm_kernels.hip"), os.path.join(CSRC, "quantize_kernels.hip"),
-           os.path.join(CSRC, "fp8gemm_api.cpp")]
+SOURCES = [os.path.join(CSRC, "fp8gemm_kernels.hip"), os.path.join(CSRC, "stream_kernels.hip"),
+           os.path.join(CSRC, "quantize_kernels.hip"), os.path.join(CSRC, "fp8gemm_api.cpp")]
 DEVICE_SOURCES = [p for p in SOURCES if p.endswith(".hip")]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

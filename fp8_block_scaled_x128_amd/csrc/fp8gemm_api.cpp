@@ -44,6 +44,20 @@ struct DeviceState {
 };
 
 DeviceState g_dev[kMaxDevices];
+
+// Every kernel of the library: the tiled table, then the stream table.
+const std::vector<KernelEntry>& kernels() {
+    static const std::vector<KernelEntry> all = [] {
+        std::vector<KernelEntry> v;
+        int n = 0;
+        const KernelEntry* t = kernel_table(&n);
+        v.insert(v.end(), t, t + n);
+        t = stream_table(&n);
+        v.insert(v.end(), t, t + n);
+        return v;
+    }();
+    return all;
+}
 std::atomic<int> g_cu_cap{0};
 thread_local char g_last_config[256] = "";
 
@@ -57,10 +71,9 @@ int device_state(DeviceState** out) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8GEMM_ERR_HIP;
         d.cus = prop.multiProcessorCount;
-        int n = 0;
-        const KernelEntry* tab = kernel_table(&n);
-        d.occupancy.assign(n, 1);
-        for (int i = 0; i < n; ++i) {
+        const std::vector<KernelEntry>& tab = kernels();
+        d.occupancy.assign(tab.size(), 1);
+        for (size_t i = 0; i < tab.size(); ++i) {
             int blocks = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, tab[i].func, tab[i].threads, 0) ==
                     hipSuccess && blocks > 0)
@@ -110,23 +123,39 @@ int workspace(DeviceState* d, hipStream_t stream, size_t partial_bytes, size_t c
 }
 
 int find_entry(int layout, int bm, int bn, int wm, int wn, int stages) {
-    int n = 0;
-    const KernelEntry* tab = kernel_table(&n);
-    for (int i = 0; i < n; ++i)
-        if (tab[i].layout == layout && tab[i].bm == bm && tab[i].bn == bn && tab[i].waves_m == wm &&
-            tab[i].waves_n == wn && tab[i].stages == stages)
-            return i;
+    const std::vector<KernelEntry>& tab = kernels();
+    for (size_t i = 0; i < tab.size(); ++i)
+        if (tab[i].kind == kKindTiled && tab[i].layout == layout && tab[i].bm == bm && tab[i].bn == bn &&
+            tab[i].waves_m == wm && tab[i].waves_n == wn && tab[i].stages == stages)
+            return (int)i;
     return -1;
 }
 
-// Optional override for experiments: FP8GEMM_FORCE_CONFIG=BMxBN:WMxWN:STAGES:SPLIT
+int find_stream(int layout, int mt, int w, int jn, int kp, int pf) {
+    const std::vector<KernelEntry>& tab = kernels();
+    for (size_t i = 0; i < tab.size(); ++i)
+        if (tab[i].kind == kKindStream && tab[i].layout == layout && tab[i].bm == mt && tab[i].waves_n == w &&
+            tab[i].jn == jn && tab[i].kp == kp && tab[i].stages == pf)
+            return (int)i;
+    return -1;
+}
+
+// Optional override for experiments:
+//   FP8GEMM_FORCE_CONFIG=BMxBN:WMxWN:STAGES:SPLIT            (tiled kernel)
+//   FP8GEMM_FORCE_CONFIG=stream:MT:W:JN:KP:PF:SPLIT           (masked decode kernel)
 bool forced_config(int layout, int* idx, int* split) {
     const char* s = std::getenv("FP8GEMM_FORCE_CONFIG");
     if (!s || !*s) return false;
-    int bm, bn, wm, wn, st, sp;
-    int got = std::sscanf(s, "%dx%d:%dx%d:%d:%d", &bm, &bn, &wm, &wn, &st, &sp);
-    if (got < 6) return false;
-    int i = find_entry(layout, bm, bn, wm, wn, st);
+    int i = -1, sp = 1;
+    if (std::strncmp(s, "stream:", 7) == 0) {
+        int mt, w, jn, kp, pf;
+        if (std::sscanf(s + 7, "%d:%d:%d:%d:%d:%d", &mt, &w, &jn, &kp, &pf, &sp) < 6) return false;
+        i = find_stream(layout, mt, w, jn, kp, pf);
+    } else {
+        int bm, bn, wm, wn, st;
+        if (std::sscanf(s, "%dx%d:%dx%d:%d:%d", &bm, &bn, &wm, &wn, &st, &sp) < 6) return false;
+        i = find_entry(layout, bm, bn, wm, wn, st);
+    }
     if (i < 0) return false;
     *idx = i;
     *split = std::max(1, sp);
@@ -147,10 +176,25 @@ int pick_split(int64_t tiles, int nkb, int cus) {
     return (int)std::max<int64_t>(1, s);
 }
 
+// Masked groups at decode sizes (expected rows <= 128): the masked decode kernel, one 128-row
+// tile per group and N tile, B read once straight into registers.  K splits only when the groups
+// times N tiles leave CUs idle.  Returns -1 when the kernel's 32-bit per-lane offsets cannot
+// address K (then the tiled kernel serves the call).
+Choice choose_masked_decode(int64_t N, int nkb, int64_t groups, int cus) {
+    Choice c{find_stream(kMasked, 128, 4, 2, 2, 4), 1};
+    if (c.entry < 0) return c;
+    const KernelEntry& e = kernels()[c.entry];
+    const int64_t K = (int64_t)nkb * 128;
+    if ((int64_t)std::max(e.bm, e.bn + 1) * K >= (int64_t(1) << 31)) return Choice{-1, 1};
+    c.split = pick_split(groups * ((N + e.bn - 1) / e.bn), nkb, cus);
+    return c;
+}
+
 // Launch-shape table.  Rows of A per tile decide the regime:
-//  - <= 128 rows (decode): HBM-bound stream of B.  Tiles span all rows of A (64, or 128 when A
-//    re-reads would cost as much as B: K >= 8192 or very wide N), N tiles of 64 or 128 so that
-//    about one unit per CU is in flight, and split-K to reach that count on narrow N.
+//  - <= 128 rows (decode): HBM-bound stream of B.  Masked groups: the masked decode kernel above.
+//    Otherwise tiles span all rows of A (64, or 128 when A re-reads would cost as much as B:
+//    K >= 8192 or very wide N), N tiles of 64 or 128 so that about one unit per CU is in flight,
+//    and split-K to reach that count on narrow N.
 //  - >= 1024 rows (prefill): MFMA-bound; 256x256 tiles, 8 waves.
 //  - in between: 128x128 tiles.
 Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_rows, int G, int cus) {
@@ -159,12 +203,16 @@ Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_row
     if (forced_config(layout, &forced, &fsplit)) return Choice{forced, fsplit};
     const int64_t m = (layout == kMasked) ? std::max<int64_t>(1, std::min(expected_rows, rows)) : rows;
     const int64_t groups = (layout == kMasked) ? G : 1;
-    const int64_t K = (int64_t)nkb * 128;
+    if (layout == kMasked && m <= 128) {
+        c = choose_masked_decode(N, nkb, groups, cus);
+        if (c.entry >= 0) return c;
+    }
     if (m <= 64) {
         const int64_t t64 = groups * ((N + 63) / 64);
         if (t64 * 2 >= 3 * cus) c.entry = find_entry(layout, 64, 128, 1, 4, 3);
         else c.entry = find_entry(layout, 64, 64, 1, 4, 4);
     } else if (m <= 128) {
+        const int64_t K = (int64_t)nkb * 128;
         if (N >= 16384 || K >= 8192) c.entry = find_entry(layout, 128, 128, 2, 4, 3);
         else c.entry = find_entry(layout, 64, 64, 1, 4, 4);
     } else if (m >= 1024 && N >= 256 && layout == kDense) {
@@ -190,9 +238,7 @@ Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_row
         c.entry = find_entry(layout, 128, 128, 2, 2, 4);
     }
     if (c.entry < 0) return c;
-    int n = 0;
-    const KernelEntry* tab = kernel_table(&n);
-    const KernelEntry& e = tab[c.entry];
+    const KernelEntry& e = kernels()[c.entry];
     const int64_t tiles = groups * ((m + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
     c.split = pick_split(tiles, nkb, cus);
     return c;
@@ -206,9 +252,9 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream)
     int cus = (cap > 0 && cap < d->cus) ? cap : d->cus;
     Choice c = choose(layout, a.rows, a.N, a.nkb, expected_rows, a.G, cus);
     if (c.entry < 0) return FP8GEMM_ERR_UNSUPPORTED;
-    int n = 0;
-    const KernelEntry* tab = kernel_table(&n);
-    const KernelEntry& e = tab[c.entry];
+    const KernelEntry& e = kernels()[c.entry];
+    if (e.kind == kKindStream && (int64_t)std::max(e.bm, e.bn + 1) * a.K >= (int64_t(1) << 31))
+        return FP8GEMM_ERR_UNSUPPORTED;     // a forced stream configuration beyond its offsets
 
     a.tiles_m = (int32_t)((a.rows + e.bm - 1) / e.bm);
     a.tiles_n = (int32_t)((a.N + e.bn - 1) / e.bn);
@@ -217,6 +263,7 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream)
     a.splits = (a.nkb + a.kb_per_split - 1) / a.kb_per_split;
     const int64_t groups = (layout == kMasked) ? a.G : 1;
     const int64_t units = groups * a.tiles_m * a.tiles_n * a.splits;
+    a.div_groups = make_fastdiv((uint32_t)groups);
     if (units >= (int64_t(1) << 30)) return FP8GEMM_ERR_UNSUPPORTED;   // unit ids stay far below 2^31
     a.units = (int32_t)units;
     a.group_m = (layout != kMasked && a.tiles_m >= 8) ? (layout == kDense ? 4 : 8) : 1;
@@ -242,11 +289,18 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream)
     int64_t slots = (int64_t)cus * d->occupancy[c.entry];
     int64_t grid = std::min<int64_t>(a.units, slots);
     if (grid <= 0) return FP8GEMM_OK;
-    std::snprintf(g_last_config, sizeof g_last_config,
-                  "%s tile=%dx%d waves=%dx%d stages=%d split=%d kb_per_split=%d units=%lld grid=%lld",
-                  layout == kDense ? "nt" : (layout == kContiguous ? "contiguous" : "masked"), e.bm,
-                  e.bn, e.waves_m, e.waves_n, e.stages, a.splits, a.kb_per_split,
-                  (long long)a.units, (long long)grid);
+    const char* lname = layout == kDense ? "nt" : (layout == kContiguous ? "contiguous" : "masked");
+    if (e.kind == kKindStream)
+        std::snprintf(g_last_config, sizeof g_last_config,
+                      "%s stream tile=%dx%d waves=%d jn=%d phase=%d depth=%d split=%d kb_per_split=%d "
+                      "units=%lld grid=%lld",
+                      lname, e.bm, e.bn, e.waves_n, e.jn, e.kp, e.stages, a.splits, a.kb_per_split,
+                      (long long)a.units, (long long)grid);
+    else
+        std::snprintf(g_last_config, sizeof g_last_config,
+                      "%s tile=%dx%d waves=%dx%d stages=%d split=%d kb_per_split=%d units=%lld grid=%lld",
+                      lname, e.bm, e.bn, e.waves_m, e.waves_n, e.stages, a.splits, a.kb_per_split,
+                      (long long)a.units, (long long)grid);
     if (std::getenv("FP8GEMM_LOG")) std::fprintf(stderr, "[fp8gemm] %s\n", g_last_config);
     e.launch(dim3((unsigned)grid), a, stream);
     if (hipGetLastError() != hipSuccess) return FP8GEMM_ERR_LAUNCH;

@@ -10,6 +10,10 @@ enum Layout { kDense = 0, kContiguous = 1, kMasked = 2 };
 
 enum DevErr { kDevErrBadIndex = 1, kDevErrBadCount = 2 };
 
+// Kernel families: output tiles staged through an LDS ring (every layout and size), and the
+// masked decode kernel that streams B into registers (masked groups of few valid rows).
+enum KernelKind { kKindTiled = 0, kKindStream = 1 };
+
 // Unsigned division by a launch constant d >= 1 as multiply-high, add and shift (the round-up
 // reciprocal method of Granlund and Montgomery, "Division by invariant integers using
 // multiplication", 1994), exact for dividends below 2^31.  Built on the host; on the device the
@@ -58,6 +62,7 @@ struct KernelArgs {
     int32_t group_m;            // M tiles per band of the unit order (1 = plain order)
     // divisors of the unit decode
     FastDiv div_splits, div_tiles_m, div_tiles_n;
+    FastDiv div_groups;         // masked decode kernel: groups in the unit order (G)
     FastDiv div_group_tiles;    // tiles_m * tiles_n
     FastDiv div_band_units;     // group_m * tiles_n
     FastDiv div_band_h;         // group_m (height of a full band)
@@ -66,8 +71,10 @@ struct KernelArgs {
 
 struct KernelEntry {
     const char* name;
+    int kind;                   // KernelKind
     int layout;
     int bm, bn, waves_m, waves_n, stages;
+    int jn, kp;                 // stream kernel: B fragments per wave, K blocks per A phase
     int threads;
     bool splitk;                // compiled with the split-K partial reduction
     int lds_bytes;
@@ -76,6 +83,7 @@ struct KernelEntry {
 };
 
 const KernelEntry* kernel_table(int* count);
+const KernelEntry* stream_table(int* count);
 
 // 1x128 activation quantiser: a workgroup covers kQuantBlocksPerWG consecutive 128-wide blocks
 // of the flattened [G][rows][K] input; the grid is ceil(blocks / kQuantBlocksPerWG) rounded up to

@@ -1,0 +1,397 @@
+// stream_kernels.hip -- gfx950 kernel of the M-grouped masked FP8 GEMM at decode sizes: each
+// group holds at most a few hundred rows of which about expected_m are valid, so the time is the
+// stream of every group's B from HBM.
+//
+// The operation and the two-level accumulation are those of the tiled kernel (page
+// "DeepSeek開源第三彈：V3/R1訓練推理關鍵秘籍，核心代碼僅300行", sections 深入了解DeepGEMM and
+// 如何使用？, masked layout): per 128-wide K block one MFMA with a zero accumulator gives the
+// block's fresh fp32 partial, which is scaled by sa[m][kb] * sb[n/128][kb] and added to an fp32
+// accumulator; the result is rounded once to bf16.
+//
+// What differs is the data movement:
+//   - A tile covers 128 rows of a group and only its 16-row sub-tiles that hold valid rows are
+//     loaded and multiplied, so a group with up to 128 valid rows streams its B once (the tiled
+//     kernel's 64-row tiles stream it twice for a group past 64 rows).
+//   - B never touches LDS.  Each wave owns JN 16-row fragments of B and loads them straight
+//     into registers, PF K blocks deep (PF - 1 blocks in flight while one is consumed), with no
+//     workgroup barrier on the B path.
+//   - A (shared by every wave of the workgroup) and its scales are staged in LDS in phases of KP
+//     K blocks, double buffered: loaded into registers one phase ahead and written to LDS at the
+//     phase start, one barrier per phase instead of one per K block.  These are ordinary loads,
+//     so the compiler's memory-counter waits for the B registers count them exactly (loads it
+//     cannot see, such as direct-to-LDS DMA written in assembly, would make those waits drain
+//     the B prefetch at every phase).
+//
+// Fragment layout.  The MFMA pairs equal byte positions of its X and Y operands, so any fixed
+// permutation of the 128 K positions, applied to both, leaves the block sum unchanged.  Lane l
+// (row l%16 of a fragment, q = l/16) holds bytes [16q, 16q+16) and [64+16q, 64+16q+16) of its
+// row's K block: each B load instruction then reads 64 contiguous bytes from each of 16 rows.
+// In LDS a row of A is 128 bytes with 16-byte chunk c stored at position c ^ ((r >> 1) & 7);
+// for the two fragment reads (chunks q and 4+q) the 16 lanes the LDS serves together (one
+// half-wave with equal parity of lane bits 2..4, measured on gfx950) hit 16 distinct 16-byte
+// bank groups.
+//
+// Work units are (M tile, group, N tile of BN = 16*JN*W rows, K split), the M tile outermost so
+// the units of tiles past every group's count (skipped at once) spread evenly over a persistent
+// grid.  When K is split, partial tiles are exchanged and summed in split order by the last
+// workgroup of the tile to arrive, as in the tiled kernel.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8gemm_device.h"
+#include "fp8gemm_internal.h"
+
+namespace fp8gemm {
+
+template <int MT, int W, int JN, int KP, int PF>
+struct Stream {
+    static constexpr int NT = 64 * W;
+    static constexpr int BN = 16 * JN * W;          // rows of B per tile
+    static constexpr int MSUB = MT / 16;            // 16-row sub-tiles of A
+    static constexpr int NBW = BN >= 128 ? BN / 128 : 1;    // 128-row scale blocks of B per tile
+    static constexpr int SA_OFF = KP * MT * 128;
+    static constexpr int SB_OFF = SA_OFF + KP * MT * 4;
+    static constexpr int PHASE_BYTES = SB_OFF + 256;
+    static constexpr int LDS_BYTES = 2 * PHASE_BYTES;
+    static constexpr int NA4 = (KP * MT * 8 + NT - 1) / NT;  // 16-byte chunks of A per thread per phase
+    static constexpr int NSA = (KP * MT + NT - 1) / NT;      // scales of A per thread per phase
+    static constexpr int U = (KP % PF == 0) ? KP : (PF % KP == 0 ? PF : KP * PF);  // K blocks per loop trip
+    static_assert(MT % 64 == 0, "scales of A are moved 64 rows at a time");
+    static_assert(128 % (16 * JN) == 0, "a wave's B rows lie inside one 128-row scale block");
+    static_assert(BN < 128 || BN % 128 == 0, "tiles of B are whole scale blocks or inside one");
+    static_assert(NBW * KP <= 64, "one x1 DMA moves the tile's B scales of a phase");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(PF >= 2, "at least one K block in flight");
+};
+
+template <int MT, int W, int JN, int KP, int PF>
+__global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const KernelArgs args) {
+    using T = Stream<MT, W, JN, KP, PF>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
+    __shared__ int s_flag;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15;
+    const int q = lane >> 4;
+    const int rsw = (r16 >> 1) & 7;              // chunk permutation of every fragment row of this lane
+    const int frag_lo = (q ^ rsw) << 4;
+    const int frag_hi = ((4 + q) ^ rsw) << 4;
+
+    const int K = args.K;
+    const int N = args.N;
+    const int nkb = args.nkb;
+    const int nnb = args.nnb;
+
+    for (int unit = blockIdx.x; unit < args.units; unit += gridDim.x) {
+        // ---- unit -> (split fastest, N tile, group, M tile) --------------------------------
+        uint32_t u = (uint32_t)unit;
+        const uint32_t tile_id = fast_div(u, args.div_splits);
+        const int split = (int)(u - tile_id * (uint32_t)args.splits);
+        u = tile_id;
+        uint32_t v = fast_div(u, args.div_tiles_n);
+        const int tn = (int)(u - v * (uint32_t)args.tiles_n);
+        const uint32_t tm_u = fast_div(v, args.div_groups);
+        const int gidx = (int)(v - tm_u * args.div_groups.d);
+        const int tm = (int)tm_u;
+        const int m0 = tm * MT;
+        const int n0 = tn * T::BN;
+        const int kb0 = split * args.kb_per_split;
+        const int nks = min(nkb, kb0 + args.kb_per_split) - kb0;
+
+        // ---- rows of the group: the valid count, clamped (a bad count flags the error word) --
+        const int g = gidx;
+        int cnt = args.masked_m[g];
+        if (cnt < 0 || cnt > args.rows) {
+            if (tm == 0 && tn == 0 && split == 0 && tid == 0) atomicOr(args.err, kDevErrBadCount);
+            cnt = cnt < 0 ? 0 : (int)args.rows;
+        }
+        if (m0 >= cnt) continue;                       // uniform: whole workgroup skips
+        const int64_t arow0 = (int64_t)g * args.rows + m0;
+        const int row_limit = (int)min((int64_t)MT, args.rows - m0);   // rows of the tile in the group
+        const int valid_rows = min(MT, cnt - m0);
+        const int nsub = (valid_rows + 15) >> 4;       // active 16-row sub-tiles
+
+        const uint8_t* Ag = args.A + arow0 * K;
+        const float* sag = args.sa + (int64_t)g * nkb * args.rows + m0;   // sa is [group][K/128][rows]
+        const float* sbg = args.sb + (int64_t)g * nnb * nkb;
+        const int nb_first = n0 >> 7;
+        const int nb_count = min(nnb, (n0 + T::BN + 127) >> 7) - nb_first;
+        // this wave's scale block of B, relative to the tile's first
+        const int nbi_w = min(((n0 + wave * JN * 16) >> 7) - nb_first, nb_count - 1);
+
+        // ---- B: per-lane offsets of the JN fragments (rows past N read row N-1) -------------
+        const uint8_t* Bt = uniform_ptr(args.B + ((int64_t)g * N + n0) * K);
+        const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(Bt), 0, 0x7FFFFFFF, kBufferFlags);
+        uint32_t b_off[JN];
+#pragma unroll
+        for (int f = 0; f < JN; ++f) {
+            const int r = min(wave * JN * 16 + 16 * f + r16, N - 1 - n0);
+            b_off[f] = (uint32_t)r * (uint32_t)K + (uint32_t)(16 * q) + (uint32_t)kb0 * 128u;
+        }
+        v8i ring[PF][JN];
+        auto issue_b = [&](int kb, v8i (&dst)[JN]) {
+#pragma unroll
+            for (int f = 0; f < JN; ++f) {
+                const uint32_t o = b_off[f] + (uint32_t)kb * 128u;
+                const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, (int)o, 0, 0));
+                const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, (int)(o + 64), 0, 0));
+                dst[f] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            }
+        };
+
+        // ---- A and scales of phase ph (K blocks [ph*KP, ph*KP + tp)): global -> registers, one
+        // phase ahead, then registers -> LDS buffer ph&1 at the phase start.  Every load of the K
+        // loop is unconditional (a K block or row past the end re-reads the last valid one, a cache
+        // hit), so the compiler's memory-counter waits before each use stay exact and leave the
+        // later loads in flight.
+        // rows of A loaded: the active sub-tiles, clamped to the array (rows past the count are
+        // never read; a clamped row re-reads the last one, a cache hit)
+        const int rows_needed = min(nsub * 16, row_limit);
+        v4i a_reg[T::NA4];
+        float sa_reg[T::NSA];
+        float sb_reg = 0.f;
+        auto load_a = [&](int ph) {
+            const int kbp = ph * KP;
+#pragma unroll
+            for (int i = 0; i < T::NA4; ++i) {
+                const int cid = tid + T::NT * i;          // chunk: 8 per row, MT rows per K block
+                const int kb = min(kbp + cid / (MT * 8), nks - 1);
+                const int r = min((cid >> 3) % MT, rows_needed - 1);
+                a_reg[i] = *reinterpret_cast<const v4i*>(Ag + (int64_t)r * K + (int64_t)(kb0 + kb) * 128 + (cid & 7) * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < T::NSA; ++i) {
+                const int sid = tid + T::NT * i;
+                const int kb = min(kbp + sid / MT, nks - 1);
+                const int r = min(sid % MT, rows_needed - 1);
+                sa_reg[i] = sag[(int64_t)(kb0 + kb) * args.rows + r];
+            }
+            {
+                const int x = min(tid, T::NBW * KP - 1);
+                const int nbi = min(x / KP, nb_count - 1);
+                const int kb = min(kbp + x % KP, nks - 1);
+                sb_reg = sbg[(int64_t)(nb_first + nbi) * nkb + kb0 + kb];
+            }
+        };
+        auto store_a = [&](int ph) {
+            const int kbp = ph * KP;
+            const int tp = min(KP, nks - kbp);
+            uint8_t* dst = smem + (ph & 1) * T::PHASE_BYTES;
+#pragma unroll
+            for (int i = 0; i < T::NA4; ++i) {
+                const int cid = tid + T::NT * i;
+                const int t = cid / (MT * 8);
+                const int r = (cid >> 3) % MT;
+                if (t < tp && r < rows_needed)
+                    *reinterpret_cast<v4i*>(dst + (t * MT + r) * 128 + (((cid & 7) ^ ((r >> 1) & 7)) << 4)) = a_reg[i];
+            }
+#pragma unroll
+            for (int i = 0; i < T::NSA; ++i) {
+                const int sid = tid + T::NT * i;
+                const int t = sid / MT;
+                const int r = sid % MT;
+                if (t < tp && r < rows_needed)
+                    reinterpret_cast<float*>(dst + T::SA_OFF)[t * MT + r] = sa_reg[i];
+            }
+            if (tid < T::NBW * KP) reinterpret_cast<float*>(dst + T::SB_OFF)[tid] = sb_reg;
+        };
+
+        // ---- accumulators -------------------------------------------------------------------
+        v4f acc[JN][T::MSUB];
+#pragma unroll
+        for (int f = 0; f < JN; ++f)
+#pragma unroll
+            for (int j = 0; j < T::MSUB; ++j) acc[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+        // one K block: MFMA partials of the active sub-tiles, promoted into acc
+        auto compute = [&](int kb, const v8i (&bf)[JN]) {
+            const int t = kb % KP;
+            const uint8_t* ph = smem + ((kb / KP) & 1) * T::PHASE_BYTES;
+            const uint8_t* ab = ph + t * MT * 128;
+            const float* sal = reinterpret_cast<const float*>(ph + T::SA_OFF) + t * MT;
+            const float sbv = reinterpret_cast<const float*>(ph + T::SB_OFF)[nbi_w * KP + t];
+#pragma unroll
+            for (int j = 0; j < T::MSUB; ++j) {
+                if (j < nsub) {
+                    const uint8_t* rp = ab + (16 * j + r16) * 128;
+                    const v4i lo = *reinterpret_cast<const v4i*>(rp + frag_lo);
+                    const v4i hi = *reinterpret_cast<const v4i*>(rp + frag_hi);
+                    const v8i af = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                    const float s = sal[16 * j + r16] * sbv;
+#pragma unroll
+                    for (int f = 0; f < JN; ++f) {
+                        const v4f p = mfma16x16x128(bf[f], af);
+                        acc[f][j] += p * s;
+                    }
+                }
+            }
+        };
+
+        // ---- K loop: B PF-1 blocks ahead in registers, A one phase ahead in LDS ----------------
+        // the same issue order as in the loop (A of a phase, then B), so the memory-counter state
+        // the compiler merges at the loop head does not force a full drain
+        load_a(0);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int u2 = 0; u2 < PF - 1; ++u2) issue_b(min(u2, nks - 1), ring[u2]);
+        for (int base = 0; base < nks; base += T::U) {
+            // U = lcm(KP, PF) K blocks: every trip starts a phase and a ring cycle
+#pragma unroll
+            for (int u2 = 0; u2 < T::U; ++u2) {
+                const int kb = base + u2;
+                if (u2 % KP == 0) {
+                    // phase start: this phase's A into LDS, visible to every wave, then the
+                    // next phase's loads (the buffer they go to was last read two phases ago)
+                    store_a(kb / KP);
+                    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                    load_a(kb / KP + 1);
+                }
+                issue_b(min(kb + PF - 1, nks - 1), ring[(u2 + PF - 1) % PF]);
+                if (kb < nks) compute(kb, ring[u2 % PF]);
+            }
+        }
+
+        // ---- epilogue: split-K exchange (agent-coherent partials), then bf16 stores ---------
+        bool store_direct = true;
+        if (args.splits > 1) {
+            const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                uniform_ptr(args.ws + (int64_t)tile_id * args.splits * (MT * T::BN)), 0,
+                (int)(args.splits * MT * T::BN * 4), kBufferFlags);
+            const int lane_off = (wave * JN * T::MSUB * 256 + lane * 4) * 4;
+            // every sub-tile is written and read (those past the valid rows carry unused values),
+            // so no access sits behind a branch and the reads below stay in flight together
+#pragma unroll
+            for (int f = 0; f < JN; ++f)
+#pragma unroll
+                for (int j = 0; j < T::MSUB; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        acc[f][j], ws_rsrc, lane_off + ((split * MT * T::BN) + (f * T::MSUB + j) * 256) * 4, 0,
+                        kSc1);
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (tid == 0) {
+                const int old = __hip_atomic_fetch_add(args.counters + tile_id, 1, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+                const int last = (old == args.splits - 1);
+                if (last)
+                    __hip_atomic_store(args.counters + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_flag = last;
+            }
+            __syncthreads();
+            store_direct = s_flag != 0;
+            if (store_direct) {
+                // sum every split's partial (this one's included) in split order, CH splits' reads
+                // in flight at a time
+                constexpr int CH = (JN * T::MSUB >= 16) ? 1 : 16 / (JN * T::MSUB);
+                for (int s0 = 0; s0 < args.splits; s0 += CH) {
+                    v4f x[CH][JN][T::MSUB];
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) {
+                        const int s2 = min(s0 + c, args.splits - 1);
+#pragma unroll
+                        for (int f = 0; f < JN; ++f)
+#pragma unroll
+                            for (int j = 0; j < T::MSUB; ++j)
+                                x[c][f][j] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                    ws_rsrc, lane_off + ((s2 * MT * T::BN) + (f * T::MSUB + j) * 256) * 4, 0, kSc1));
+                    }
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) {
+                        if (s0 + c < args.splits) {
+#pragma unroll
+                            for (int f = 0; f < JN; ++f)
+#pragma unroll
+                                for (int j = 0; j < T::MSUB; ++j)
+                                    acc[f][j] = (s0 + c == 0) ? x[c][f][j] : acc[f][j] + x[c][f][j];
+                        }
+                    }
+                }
+            }
+        }
+        if (store_direct) {
+#pragma unroll
+            for (int j = 0; j < T::MSUB; ++j) {
+                const int rm = 16 * j + r16;
+                if (j >= nsub || rm >= valid_rows) continue;
+                uint16_t* drow = args.D + (arow0 + rm) * (int64_t)N;
+#pragma unroll
+                for (int f = 0; f < JN; ++f) {
+                    const int n = n0 + wave * JN * 16 + 16 * f + 4 * q;
+                    const v4f x = acc[f][j];
+                    if (n + 3 < N && (N & 3) == 0) {
+                        uint2 pk;
+                        pk.x = pack_bf16x2(x.x, x.y);
+                        pk.y = pack_bf16x2(x.z, x.w);
+                        *reinterpret_cast<uint2*>(drow + n) = pk;
+                    } else {
+                        const float e[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            if (n + r < N) {
+                                __bf16 h = (__bf16)e[r];
+                                uint16_t hb;
+                                __builtin_memcpy(&hb, &h, 2);
+                                drow[n + r] = hb;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        // the next unit's first phase rewrites LDS other waves may still be reading
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// instantiation table
+// ------------------------------------------------------------------------------------------
+
+template <int MT, int W, int JN, int KP, int PF>
+static void launch_stream(dim3 grid, const KernelArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((fp8gemm_masked_decode_kernel<MT, W, JN, KP, PF>), grid, dim3(W * 64), 0, s, a);
+}
+
+template <int MT, int W, int JN, int KP, int PF>
+static KernelEntry stream_entry(const char* name) {
+    using T = Stream<MT, W, JN, KP, PF>;
+    KernelEntry e;
+    e.name = name;
+    e.kind = kKindStream;
+    e.layout = kMasked;
+    e.bm = MT;
+    e.bn = T::BN;
+    e.waves_m = 1;
+    e.waves_n = W;
+    e.stages = PF;
+    e.jn = JN;
+    e.kp = KP;
+    e.threads = T::NT;
+    e.splitk = true;
+    e.lds_bytes = T::LDS_BYTES;
+    e.func = reinterpret_cast<const void*>(&fp8gemm_masked_decode_kernel<MT, W, JN, KP, PF>);
+    e.launch = &launch_stream<MT, W, JN, KP, PF>;
+    return e;
+}
+
+#define STREAM_ENTRY(MT, W, JN, KP, PF) \
+    stream_entry<MT, W, JN, KP, PF>("masked decode " #MT " rows, " #W " waves x " #JN " fragments, phase " #KP ", depth " #PF)
+
+// Masked groups of at most 128 valid rows (one tile per group and N tile, B streamed once per
+// group).  Measured on the 16-group x 4096 x 7168 decode configuration (about 64 valid rows per
+// group): 4 waves x 2 fragments, 2-block phases: 129 us; 8 waves x 1 fragment: 135 us; the tiled
+// kernel with 64-row tiles (B streamed twice for groups past 64 rows): 240 us.
+const KernelEntry* stream_table(int* count) {
+    static const KernelEntry table[] = {
+        STREAM_ENTRY(128, 4, 2, 2, 4),
+        STREAM_ENTRY(128, 8, 1, 4, 4),
+    };
+    *count = (int)(sizeof(table) / sizeof(table[0]));
+    return table;
+}
+
+}  // namespace fp8gemm

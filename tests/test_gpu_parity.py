@@ -55,6 +55,17 @@ def kernel_table():
             re.findall(r"FP8GEMM_ENTRY\((\d+), (\d+), (\d+), (\d+), (\d+), (k\w+)\)", src)]
 
 
+def stream_table():
+    """Configurations of the masked decode kernel: (rows, waves, fragments, phase, depth)."""
+    src = open(os.path.join(ROOT, "fp8_block_scaled_x128_amd", "csrc", "stream_kernels.hip")).read()
+    return [tuple(int(x) for x in t) for t in
+            re.findall(r"STREAM_ENTRY\((\d+), (\d+), (\d+), (\d+), (\d+)\)", src)]
+
+
+def stream_id(e):
+    return "mt%d_w%d_jn%d_kp%d_pf%d" % e[:5]
+
+
 class forced:
     """Force the launch configuration of the calls inside the block (FP8GEMM_FORCE_CONFIG)."""
 
@@ -66,6 +77,13 @@ class forced:
 
     def __exit__(self, *exc):
         os.environ.pop("FP8GEMM_FORCE_CONFIG", None)
+
+
+class forced_stream(forced):
+    """Force a configuration of the masked decode kernel."""
+
+    def __init__(self, mt, w, jn, kp, pf, split):
+        self.v = "stream:%d:%d:%d:%d:%d:%d" % (mt, w, jn, kp, pf, split)
 
 
 def int_codes(rng, shape, lo=-4, hi=4):
@@ -311,6 +329,52 @@ def test_every_masked_kernel_config(entry, split):
     assert "tile=%dx%d" % (bm, bn) in cfg, cfg
     got = gpu_bits(D)
     assert_close(got, ref, mask=np.broadcast_to(valid.astype(bool)[:, :, None], got.shape), what=cfg)
+
+
+@pytest.mark.parametrize("entry", stream_table(), ids=stream_id)
+@pytest.mark.parametrize("split", [1, 3])
+def test_every_masked_decode_config(entry, split):
+    """The masked decode kernel: counts past one tile (a second M tile), zero, a ragged last
+    sub-tile and a full group; N off the tile and scale-block grid; K = 6 blocks (a short last
+    A phase for 4-block phases); integer inputs bit-exact; one CU (several units per workgroup)."""
+    mt, w, jn, kp, pf = entry
+    bn = 16 * jn * w
+    M_max = 2 * mt
+    w_ = W.masked(np.array([mt + 3, 0, 17, M_max], np.int32), M_max, 2 * bn + 24, 768, seed=mt * 3 + split + bn)
+    ref, valid = oracle.grouped_masked(w_.A, w_.sa, w_.B, w_.sb, w_.masked_m)
+    out = sentinel_tensor((4, M_max, 2 * bn + 24))
+    with forced_stream(mt, w, jn, kp, pf, split):
+        D = run_masked(w_, 64, out=out)
+        cfg = fg.last_config()
+    assert "stream tile=%dx%d" % (mt, bn) in cfg, cfg
+    got = gpu_bits(D)
+    v = np.broadcast_to(valid.astype(bool)[:, :, None], got.shape)
+    assert_close(got, ref, mask=v, what=cfg)
+    assert np.all(got[~v] == SENTINEL), "rows past the count were written"
+    # integer codes with power-of-two scales: exact, so bit-exact; rows past the counts hold
+    # other codes (they must not leak into valid rows)
+    rng = np.random.default_rng(mt + split)
+    G, K, N = 4, 768, 2 * bn + 24
+    A = int_codes(rng, (G, M_max, K))
+    Bq = int_codes(rng, (G, N, K))
+    sa = (2.0 ** rng.integers(-1, 2, size=(G, M_max, K // 128))).astype(np.float32)
+    sb = (2.0 ** rng.integers(-1, 2, size=(G, (N + 127) // 128, K // 128))).astype(np.float32)
+    mm = np.array([mt - 5, 1, mt + 17, 0], np.int32)
+    ref2, valid2 = oracle.grouped_masked(A, sa, Bq, sb, mm)
+    v2 = np.broadcast_to(valid2.astype(bool)[:, :, None], ref2.shape)
+    fg.set_num_cus(1)
+    try:
+        with forced_stream(mt, w, jn, kp, pf, split):
+            D2 = run_masked(W.Masked(A, sa, Bq, sb, mm, 64), 64, out=sentinel_tensor((G, M_max, N)))
+            cfg2 = fg.last_config()
+    finally:
+        fg.set_num_cus(0)
+    got2 = gpu_bits(D2)
+    assert np.array_equal(got2[v2], ref2[v2]), cfg2
+    assert np.all(got2[~v2] == SENTINEL)
+    units, grid = (int(x) for x in re.search(r"units=(\d+) grid=(\d+)", cfg2).groups())
+    assert units > grid, cfg2
+    say("masked decode", cfg, cfg2)
 
 
 def test_masked_count_out_of_range_clamps_and_flags():
