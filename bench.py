@@ -23,6 +23,9 @@ Prints ONE JSON line:
   quantize_1x128  the bf16 -> E4M3 1x128 activation quantiser on the contiguous configuration's
                activations (32768 x 7168) and the masked decode configuration's, with its own
                HBM roofline (context, not part of value)
+  moe_expert_chain  one DeepSeek-V3-sized MoE expert layer on the masked decode configuration's
+               groups: first grouped GEMM, SwiGLU + requantisation, second grouped GEMM
+               (context, not part of value)
   cpu_baseline the CPU oracle on a bounded sample of the same workload on this host's cores
 """
 from __future__ import annotations
@@ -54,7 +57,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-grouped", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
+    p.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU-oracle sample time")
     p.add_argument("--counters", action="store_true",
                    help="launch each M=4096 sweep GEMM and a 1 GiB copy a few times, eagerly (run under "
                         "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)")
@@ -256,6 +259,7 @@ def main():
         del flush
         grouped = bench_grouped(fg, W, torch, dev, stream)
     quantize = bench_quantize(fg, W, torch, dev, stream)
+    moe = {} if args.no_grouped else bench_moe_chain(fg, W, torch, dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -285,6 +289,7 @@ def main():
         "per_shape": per,
         "grouped": grouped,
         "quantize_1x128": quantize,
+        "moe_expert_chain": moe,
     }
     print(json.dumps(line), flush=True)
 
@@ -441,6 +446,76 @@ def bench_grouped(fg, W, torch, dev, stream, reps=10):
     return out
 
 
+def bench_moe_chain(fg, W, torch, dev, stream, reps=5):
+    """One DeepSeek-V3-sized MoE expert layer on the masked decode configuration's groups (16
+    groups, M_max 256, about 64 valid rows each, H = 7168, I = 2048): the first grouped GEMM
+    (N = 4096, K = 7168), SwiGLU + requantisation, the second grouped GEMM (N = 7168, K = 2048),
+    through the single chain entry point.  HIP events on the launch stream around a graph of the
+    chain (and of each step alone), after a read-only 1 GiB buffer read; HBM roofline on the
+    algorithmic bytes (both layers' weights dominate)."""
+    t0 = time.time()
+    e = W.moe_config4()
+    G, M_max, H = e.A.shape
+    I = e.W2.shape[2]
+    A, W1, s1, W2, s2 = (torch.from_numpy(x).to(dev) for x in (e.A, e.W1, e.s1, e.W2, e.s2))
+    sa = torch.from_numpy(np.ascontiguousarray(np.swapaxes(e.sa, -1, -2))).to(dev)
+    mm = torch.from_numpy(e.masked_m).to(dev)
+    Y1 = torch.empty((G, M_max, 2 * I), dtype=torch.bfloat16, device=dev)
+    Hq = torch.empty((G, M_max, I), dtype=torch.float8_e4m3fn, device=dev)
+    sh = torch.empty((G, I // 128, M_max), dtype=torch.float32, device=dev)
+    out = torch.empty((G, M_max, H), dtype=torch.bfloat16, device=dev)
+    counts = [int(x) for x in e.masked_m]
+    rows = sum(counts)
+    steps = {
+        "chain": lambda: fg.moe_expert_masked(A, sa, W1, s1, W2, s2, mm, e.expected_m, out=out,
+                                              workspace=(Y1, Hq, sh), stream=stream),
+        "first_layer": lambda: fg.grouped_masked(A, sa, W1, s1, mm, e.expected_m, out=Y1, stream=stream),
+        "swiglu_quantize": lambda: fg.swiglu_quantize_1x128_masked(Y1, mm, codes=Hq, scales=sh, stream=stream),
+        "second_layer": lambda: fg.grouped_masked(Hq, sh, W2, s2, mm, e.expected_m, out=out, stream=stream),
+    }
+    work = {"chain": W.moe_expert_work(counts, H, I, G),
+            "first_layer": W.grouped_work(counts, 2 * I, H, index_bytes=4 * G),
+            "swiglu_quantize": (0, W.swiglu_quantize_work(rows, I)),
+            "second_layer": W.grouped_work(counts, H, I, index_bytes=4 * G)}
+    flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1, device=dev)
+    res = {}
+    for name, call in steps.items():
+        with torch.cuda.stream(stream):
+            call()
+        stream.synchronize()
+        cfg = fg.last_config()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            call()
+        ts = []
+        for _ in range(reps):
+            with torch.cuda.stream(stream):
+                sink.add_(flush.sum())
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+            stream.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.mean(ts))
+        flop, byts = work[name]
+        gbs = byts / (ms * 1e-3) / 1e9
+        res[name] = dict(us=round(ms * 1e3, 1), bytes=byts, gbs=round(gbs, 1),
+                         frac_hbm=round(gbs / PEAK_HBM_GBS, 4), config=cfg)
+        if flop:
+            res[name]["tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+        log("moe %s: %.1f us, %.1f GB/s (%s)" % (name, ms * 1e3, gbs, cfg))
+        del g
+    res["chain"]["valid_rows"] = rows
+    res["chain"]["shape"] = "G=%d M_max=%d H=%d I=%d" % (G, M_max, H, I)
+    log("moe chain leg done in %.1f s" % (time.time() - t0))
+    del A, W1, s1, W2, s2, sa, mm, Y1, Hq, sh, out, flush
+    torch.cuda.empty_cache()
+    return res
+
+
 QUANT_LAUNCHES = 16    # launches per timed graph of the quantiser (two operand copies alternate)
 
 
@@ -546,13 +621,22 @@ def cpu_baseline(cases, target_s):
     t_probe = (time.perf_counter() - t0) / pr
     per_row_all = t_probe * sum(c["N"] * c["K"] for c in cases) / (probe["N"] * probe["K"])
     rows = int(max(1, min(4096, target_s / max(per_row_all, 1e-9))))
-    flop = 0
-    t0 = time.perf_counter()
-    for c in cases:
-        r = min(rows, c["M"])
-        oracle.gemm_nt(c["hostA"][:r], c["hostsa"][:r], c["hostB"], c["hostsb"])
-        flop += 2 * r * c["N"] * c["K"]
-    dt = time.perf_counter() - t0
+
+    def run(rows):
+        flop = 0
+        t0 = time.perf_counter()
+        for c in cases:
+            r = min(rows, c["M"])
+            oracle.gemm_nt(c["hostA"][:r], c["hostsa"][:r], c["hostB"], c["hostsb"])
+            flop += 2 * r * c["N"] * c["K"]
+        return flop, time.perf_counter() - t0
+
+    flop, dt = run(rows)
+    # the probe also pays the per-call decode of B, so the first sample can fall short of the
+    # target: resize once from the measured time (the reported sample is the second)
+    if dt < 0.6 * target_s and rows < 4096:
+        rows = int(max(1, min(4096, rows * target_s / dt)))
+        flop, dt = run(rows)
     log("cpu oracle: %d rows of each case, %.1f GFLOP in %.1f s on %d threads" % (rows, flop / 1e9, dt, nth))
     return dict(value=round(flop / dt / 1e12, 6), unit="TFLOP/s", cores=nth, kind="oracle",
                 sample="first %d rows (at most M) of each of the 18 sweep GEMMs, all N and K: %.1f GFLOP in %.1f s"

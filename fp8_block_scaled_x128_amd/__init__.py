@@ -8,6 +8,8 @@ C ABI declared in include/fp8gemm.h.  torch supplies device memory and the curre
     D = grouped_masked(A, sa, B, sb, masked_m, expected_m) # MoE, fixed per-group capacity
     A, sa = quantize_1x128(X)                              # bf16 activations -> codes + scales
     A, sa = quantize_1x128_masked(X, masked_m)             # the same, masked layout
+    H, sh = swiglu_quantize_1x128(Y)                       # silu(gate) * up -> codes + scales
+    out = moe_expert_masked(A, sa, W1, s1, W2, s2, masked_m, expected_m)  # one MoE expert layer
 
 A and B are E4M3 codes (torch.float8_e4m3fn or uint8), sa one fp32 scale per 1x128 block of a
 row of A stored K-block-major (sa[kb, m], shape [K/128, M]), sb one per 128x128 block of B (page "DeepSeek開源第三彈：V3/R1訓練推理關鍵秘籍，核心代碼僅
@@ -20,7 +22,8 @@ import ctypes
 import os
 
 __all__ = ["gemm_nt", "grouped_contiguous", "grouped_masked", "quantize_1x128",
-           "quantize_1x128_masked", "init", "set_num_cus",
+           "quantize_1x128_masked", "swiglu_quantize_1x128", "swiglu_quantize_1x128_masked",
+           "moe_expert_masked", "init", "set_num_cus",
            "last_config", "read_device_error", "status_string", "lib", "library_path",
            "Fp8GemmError", "STATUS", "DEVERR_BAD_INDEX", "DEVERR_BAD_COUNT"]
 
@@ -42,6 +45,10 @@ SIGNATURES = {
     "fp8gemm_grouped_masked": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _P]),
     "fp8gemm_quantize_1x128": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "fp8gemm_quantize_1x128_masked": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _P]),
+    "fp8gemm_swiglu_quantize_1x128": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "fp8gemm_swiglu_quantize_1x128_masked": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _P]),
+    "fp8gemm_moe_expert_masked": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                 _I32, _I64, _I64, _I64, _I64, _P]),
     "fp8gemm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fp8gemm_init": (ctypes.c_int, []),
     "fp8gemm_set_num_cus": (ctypes.c_int, [ctypes.c_int]),
@@ -284,3 +291,80 @@ def quantize_1x128_masked(X, masked_m, codes=None, scales=None, stream=None):
                                                  _stream(stream, X.device))
     _check(st, "fp8gemm_quantize_1x128_masked")
     return codes, scales
+
+
+def swiglu_quantize_1x128(Y, codes=None, scales=None, stream=None):
+    """SwiGLU + requantisation: Y bf16 [M,2I] (gate | up) -> (codes [M,I], scales fp32 [I/128,M]) of
+    h = silu(gate) * up, one scale per 1x128 block (the second expert layer's A and sa)."""
+    torch = _torch()
+    Y = _bf16(Y, "Y")
+    _shape_check(Y.dim() == 2 and Y.shape[1] % 2 == 0, "Y [M,2I]")
+    M, I = Y.shape[0], Y.shape[1] // 2
+    codes, scales = _quant_outputs(codes, scales, (M, I), (I // 128, M), Y.device)
+    with torch.cuda.device(Y.device):
+        st = lib().fp8gemm_swiglu_quantize_1x128(Y.data_ptr(), codes.data_ptr(), scales.data_ptr(), M, I,
+                                                 _stream(stream, Y.device))
+    _check(st, "fp8gemm_swiglu_quantize_1x128")
+    return codes, scales
+
+
+def swiglu_quantize_1x128_masked(Y, masked_m, codes=None, scales=None, stream=None):
+    """Masked layout: Y bf16 [G,M_max,2I] -> (codes [G,M_max,I], scales [G,I/128,M_max]); rows at or
+    past masked_m[g] are not written (zeros when the outputs are allocated here)."""
+    torch = _torch()
+    Y = _bf16(Y, "Y")
+    masked_m = _i32(masked_m, "masked_m")
+    _shape_check(Y.dim() == 3 and Y.shape[2] % 2 == 0 and tuple(masked_m.shape) == (Y.shape[0],),
+                 "Y [G,M_max,2I], masked_m [G]")
+    G, M_max, I = Y.shape[0], Y.shape[1], Y.shape[2] // 2
+    if codes is None:
+        codes = torch.zeros((G, M_max, I), dtype=torch.uint8, device=Y.device).view(torch.float8_e4m3fn)
+    if scales is None:
+        scales = torch.zeros((G, I // 128, M_max), dtype=torch.float32, device=Y.device)
+    codes, scales = _quant_outputs(codes, scales, (G, M_max, I), (G, I // 128, M_max), Y.device)
+    with torch.cuda.device(Y.device):
+        st = lib().fp8gemm_swiglu_quantize_1x128_masked(Y.data_ptr(), codes.data_ptr(), scales.data_ptr(),
+                                                        masked_m.data_ptr(), G, M_max, I,
+                                                        _stream(stream, Y.device))
+    _check(st, "fp8gemm_swiglu_quantize_1x128_masked")
+    return codes, scales
+
+
+def moe_expert_masked(A, sa, W1, s1, W2, s2, masked_m, expected_m: int, out=None, workspace=None,
+                      stream=None):
+    """One MoE expert layer per group, masked layout: out = (swiglu(A . W1^T) requantised) . W2^T.
+    A [G,M_max,H] codes, sa [G,H/128,M_max], W1 [G,2I,H], s1 [G,2I/128,H/128], W2 [G,H,I],
+    s2 [G,H/128,I/128], masked_m int32 [G].  ``workspace``: optional (Y1 bf16 [G,M_max,2I],
+    Hq codes [G,M_max,I], sh fp32 [G,I/128,M_max]), allocated here when None.  Returns out bf16
+    [G,M_max,H] (rows past masked_m[g] untouched: zeros when allocated here)."""
+    torch = _torch()
+    A, W1, W2 = _codes(A, "A"), _codes(W1, "W1"), _codes(W2, "W2")
+    sa, s1, s2 = _f32(sa, "sa"), _f32(s1, "s1"), _f32(s2, "s2")
+    masked_m = _i32(masked_m, "masked_m")
+    _shape_check(A.dim() == 3 and W1.dim() == 3 and W2.dim() == 3, "A [G,M_max,H], W1 [G,2I,H], W2 [G,H,I]")
+    G, M_max, H = A.shape
+    I = W2.shape[2]
+    _shape_check(tuple(W1.shape) == (G, 2 * I, H) and tuple(W2.shape) == (G, H, I)
+                 and tuple(sa.shape) == (G, H // 128, M_max)
+                 and tuple(s1.shape) == (G, (2 * I + 127) // 128, H // 128)
+                 and tuple(s2.shape) == (G, (H + 127) // 128, I // 128) and tuple(masked_m.shape) == (G,),
+                 "A [G,M_max,H], sa [G,H/128,M_max], W1 [G,2I,H], s1 [G,2I/128,H/128], W2 [G,H,I], "
+                 "s2 [G,H/128,I/128], masked_m [G]")
+    if workspace is None:
+        workspace = (torch.empty((G, M_max, 2 * I), dtype=torch.bfloat16, device=A.device),
+                     torch.empty((G, M_max, I), dtype=torch.float8_e4m3fn, device=A.device),
+                     torch.empty((G, I // 128, M_max), dtype=torch.float32, device=A.device))
+    Y1, Hq, sh = workspace
+    Y1, Hq, sh = _bf16(Y1, "Y1"), _codes(Hq, "Hq"), _f32(sh, "sh")
+    _shape_check(tuple(Y1.shape) == (G, M_max, 2 * I) and tuple(Hq.shape) == (G, M_max, I)
+                 and tuple(sh.shape) == (G, I // 128, M_max), "workspace shapes")
+    if out is None:
+        out = torch.zeros((G, M_max, H), dtype=torch.bfloat16, device=A.device)
+    D = _out(out, (G, M_max, H), A.device)
+    with torch.cuda.device(A.device):
+        st = lib().fp8gemm_moe_expert_masked(A.data_ptr(), sa.data_ptr(), W1.data_ptr(), s1.data_ptr(),
+                                             W2.data_ptr(), s2.data_ptr(), masked_m.data_ptr(),
+                                             Y1.data_ptr(), Hq.data_ptr(), sh.data_ptr(), D.data_ptr(),
+                                             G, M_max, H, I, int(expected_m), _stream(stream, A.device))
+    _check(st, "fp8gemm_moe_expert_masked")
+    return D

@@ -181,10 +181,11 @@ int pick_split(int64_t tiles, int nkb, int cus) {
 // times N tiles leave CUs idle.  Returns -1 when the kernel's 32-bit per-lane offsets cannot
 // address K (then the tiled kernel serves the call).
 Choice choose_masked_decode(int64_t N, int nkb, int64_t groups, int cus) {
-    Choice c{find_stream(kMasked, 128, 4, 2, 2, 4), 1};
+    const int64_t K = (int64_t)nkb * 128;
+    // short K (few blocks per unit): narrower N tiles, so more units overlap their start-up
+    Choice c{K <= 2048 ? find_stream(kMasked, 128, 4, 1, 2, 4) : find_stream(kMasked, 128, 4, 2, 2, 4), 1};
     if (c.entry < 0) return c;
     const KernelEntry& e = kernels()[c.entry];
-    const int64_t K = (int64_t)nkb * 128;
     if ((int64_t)std::max(e.bm, e.bn + 1) * K >= (int64_t(1) << 31)) return Choice{-1, 1};
     c.split = pick_split(groups * ((N + e.bn - 1) / e.bn), nkb, cus);
     return c;
@@ -328,9 +329,10 @@ int check_k(int64_t K) {
     return FP8GEMM_OK;
 }
 
-// Shared launch of the activation quantiser over G groups of `rows` rows.
+// Shared launch of the activation quantiser over G groups of `rows` rows; with `swiglu` the
+// input rows hold 2K values (gate | up) and the quantised values are silu(gate) * up.
 int quantize(const void* X, void* A, float* sa, const int32_t* masked_m, int32_t G, int64_t rows,
-             int64_t K, hipStream_t stream) {
+             int64_t K, bool swiglu, hipStream_t stream) {
     const int64_t nkb = K / 128;
     const int64_t blocks = (int64_t)G * rows * nkb;
     if (blocks >= (int64_t(1) << 31)) return FP8GEMM_ERR_UNSUPPORTED;  // block ids stay below 2^31
@@ -352,9 +354,10 @@ int quantize(const void* X, void* A, float* sa, const int32_t* masked_m, int32_t
     q.div_rows = make_fastdiv((uint32_t)rows);
     const int64_t wgs = (blocks + kQuantBlocksPerWG - 1) / kQuantBlocksPerWG;
     const int64_t grid = (wgs + 7) / 8 * 8;
-    std::snprintf(g_last_config, sizeof g_last_config, "quantize_1x128 blocks_per_wg=%d grid=%lld",
-                  kQuantBlocksPerWG, (long long)grid);
-    launch_quantize_1x128(q, dim3((unsigned)grid), stream);
+    std::snprintf(g_last_config, sizeof g_last_config, "%s blocks_per_wg=%d grid=%lld",
+                  swiglu ? "swiglu_quantize_1x128" : "quantize_1x128", kQuantBlocksPerWG, (long long)grid);
+    if (swiglu) launch_swiglu_quantize(q, dim3((unsigned)grid), stream);
+    else launch_quantize_1x128(q, dim3((unsigned)grid), stream);
     if (hipGetLastError() != hipSuccess) return FP8GEMM_ERR_LAUNCH;
     return FP8GEMM_OK;
 }
@@ -371,7 +374,7 @@ int fp8gemm_quantize_1x128(const void* X, void* A, float* sa, int64_t M, int64_t
     if (M == 0) return FP8GEMM_OK;
     if (!X || !A || !sa) return FP8GEMM_ERR_NULL_PTR;
     if (!aligned(X, 16) || !aligned(A, 16) || !aligned(sa, 4)) return FP8GEMM_ERR_MISALIGNED;
-    return quantize(X, A, sa, nullptr, 1, M, K, static_cast<hipStream_t>(stream));
+    return quantize(X, A, sa, nullptr, 1, M, K, false, static_cast<hipStream_t>(stream));
 }
 
 int fp8gemm_quantize_1x128_masked(const void* X, void* A, float* sa, const int32_t* masked_m,
@@ -385,7 +388,58 @@ int fp8gemm_quantize_1x128_masked(const void* X, void* A, float* sa, const int32
     if (!X || !A || !sa || !masked_m) return FP8GEMM_ERR_NULL_PTR;
     if (!aligned(X, 16) || !aligned(A, 16) || !aligned(sa, 4) || !aligned(masked_m, 4))
         return FP8GEMM_ERR_MISALIGNED;
-    return quantize(X, A, sa, masked_m, G, M_max, K, static_cast<hipStream_t>(stream));
+    return quantize(X, A, sa, masked_m, G, M_max, K, false, static_cast<hipStream_t>(stream));
+}
+
+int fp8gemm_swiglu_quantize_1x128(const void* X, void* A, float* sa, int64_t M, int64_t I, void* stream) {
+    if (M < 0) return FP8GEMM_ERR_BAD_SHAPE;
+    int st = check_k(I);
+    if (st != FP8GEMM_OK) return st;
+    if (M > kMaxRows || 4 * M * I >= kMaxBytes) return FP8GEMM_ERR_UNSUPPORTED;
+    if (M == 0) return FP8GEMM_OK;
+    if (!X || !A || !sa) return FP8GEMM_ERR_NULL_PTR;
+    if (!aligned(X, 16) || !aligned(A, 16) || !aligned(sa, 4)) return FP8GEMM_ERR_MISALIGNED;
+    return quantize(X, A, sa, nullptr, 1, M, I, true, static_cast<hipStream_t>(stream));
+}
+
+int fp8gemm_swiglu_quantize_1x128_masked(const void* X, void* A, float* sa, const int32_t* masked_m,
+                                         int32_t G, int64_t M_max, int64_t I, void* stream) {
+    if (G <= 0 || M_max < 0) return FP8GEMM_ERR_BAD_SHAPE;
+    int st = check_k(I);
+    if (st != FP8GEMM_OK) return st;
+    if ((int64_t)G * M_max > kMaxRows || 4 * (int64_t)G * M_max * I >= kMaxBytes) return FP8GEMM_ERR_UNSUPPORTED;
+    if (M_max == 0) return FP8GEMM_OK;
+    if (!X || !A || !sa || !masked_m) return FP8GEMM_ERR_NULL_PTR;
+    if (!aligned(X, 16) || !aligned(A, 16) || !aligned(sa, 4) || !aligned(masked_m, 4))
+        return FP8GEMM_ERR_MISALIGNED;
+    return quantize(X, A, sa, masked_m, G, M_max, I, true, static_cast<hipStream_t>(stream));
+}
+
+int fp8gemm_moe_expert_masked(const void* A, const float* sa, const void* W1, const float* s1,
+                              const void* W2, const float* s2, const int32_t* masked_m, void* Y1,
+                              void* Hq, float* sh, void* out, int32_t G, int64_t M_max, int64_t H,
+                              int64_t I, int64_t expected_m, void* stream) {
+    // every check of the three steps before anything is enqueued
+    if (G <= 0 || M_max < 0 || expected_m < 0) return FP8GEMM_ERR_BAD_SHAPE;
+    int st = check_k(H);
+    if (st == FP8GEMM_OK) st = check_k(I);
+    if (st != FP8GEMM_OK) return st;
+    const int64_t rows = (int64_t)G * M_max;
+    if (rows > kMaxRows || 2 * I > kMaxRows || rows * H >= kMaxBytes || 4 * rows * I >= kMaxBytes ||
+        2 * (int64_t)G * I * H >= kMaxBytes || 2 * rows * H >= kMaxBytes)
+        return FP8GEMM_ERR_UNSUPPORTED;
+    if (M_max == 0) return FP8GEMM_OK;
+    if (!A || !sa || !W1 || !s1 || !W2 || !s2 || !masked_m || !Y1 || !Hq || !sh || !out)
+        return FP8GEMM_ERR_NULL_PTR;
+    if (!aligned(A, 16) || !aligned(W1, 16) || !aligned(W2, 16) || !aligned(Y1, 16) || !aligned(Hq, 16) ||
+        !aligned(out, 16) || !aligned(sa, 4) || !aligned(s1, 4) || !aligned(s2, 4) || !aligned(sh, 4) ||
+        !aligned(masked_m, 4))
+        return FP8GEMM_ERR_MISALIGNED;
+    st = fp8gemm_grouped_masked(A, sa, W1, s1, masked_m, Y1, G, M_max, 2 * I, H, expected_m, stream);
+    if (st != FP8GEMM_OK) return st;
+    st = fp8gemm_swiglu_quantize_1x128_masked(Y1, Hq, sh, masked_m, G, M_max, I, stream);
+    if (st != FP8GEMM_OK) return st;
+    return fp8gemm_grouped_masked(Hq, sh, W2, s2, masked_m, out, G, M_max, H, I, expected_m, stream);
 }
 
 int fp8gemm_nt(const void* A, const float* sa, const void* B, const float* sb, void* D, int64_t M,

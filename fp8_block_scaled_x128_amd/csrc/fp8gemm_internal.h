@@ -91,7 +91,7 @@ const KernelEntry* stream_table(int* count);
 constexpr int kQuantBlocksPerWG = 16;
 
 struct QuantArgs {
-    const uint16_t* X;          // [G][rows][K] bf16 bits
+    const uint16_t* X;          // [G][rows][K] bf16 bits ([G][rows][2K] for the SwiGLU variant)
     uint8_t* A;                 // [G][rows][K] E4M3 codes
     float* sa;                  // [G][nkb][rows]
     const int32_t* masked_m;    // [G] valid rows per group, or null (all rows)
@@ -104,5 +104,8 @@ struct QuantArgs {
 };
 
 void launch_quantize_1x128(const QuantArgs& a, dim3 grid, hipStream_t stream);
+
+// SwiGLU + 1x128 quantiser: the same arguments, with X rows of 2K bf16 values (gate | up).
+void launch_swiglu_quantize(const QuantArgs& a, dim3 grid, hipStream_t stream);
 
 }  // namespace fp8gemm

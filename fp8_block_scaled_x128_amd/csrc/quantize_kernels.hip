@@ -17,6 +17,12 @@
 // rows (adjacent words of the K-block-major scale array) then meet in the same L2.  Contiguous
 // per-workgroup spans sustain about 6 TB/s for this read/write mix on MI355X, against about
 // 5 TB/s for tiles of 16 rows x 4 blocks.
+//
+// The same file holds the SwiGLU variant used between the two linear layers of an MoE expert
+// (page "Perpustakaan operator GPU sumber terbuka DeepSeek DeepGEMM memperbarui versi besar,
+// menambahkan Mega MoE…": first linear layer, SwiGLU activation, second linear layer): it reads
+// a row's gate and up halves, forms silu(gate) * up in fp32 and quantises those values with the
+// same block quantiser, fused, so the activation never makes a round trip through HBM.
 
 #include "fp8gemm_internal.h"
 
@@ -78,6 +84,39 @@ __device__ inline uint2 quantize_chunk(const Chunk& c, float* scale) {
     return make_uint2((uint32_t)lo, (uint32_t)hi);
 }
 
+// The same block quantiser on 8 fp32 values (a lane's share of a 128-value block): |x| bit
+// patterns of finite fp32 values order like the values, so the block maximum is again an integer
+// reduction; then s = amax / 448, the correctly rounded quotients, saturation and the RNE
+// conversion, as above.
+__device__ inline uint2 quantize_f32x8(const float (&x)[8], float* scale) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+    m = row16_max(m);
+    const float amax = fmaxf(__uint_as_float(m), 1e-4f);
+    const float s = amax / 448.0f;
+    const float r = 1.0f / s;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __builtin_amdgcn_fmed3f(div_rn(x[i], s, r), -448.0f, 448.0f);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], hi, true);
+    *scale = s;
+    return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+// SwiGLU of one element in fp32: silu(g) * u = (g * sigmoid(g)) * u, sigmoid(g) = 1 / (1 + e^-g).
+// e^-g is the hardware base-2 exponential of -g * log2(e) and the reciprocal the hardware one
+// (each within about one unit in the last place; the result feeds a 3-bit-mantissa code).  For
+// g below about -88, e^-g is infinite, sigmoid 0 and the product a signed zero.
+__device__ inline float swiglu1(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+    const float sig = __builtin_amdgcn_rcpf(1.0f + e);
+    return (g * sig) * u;
+}
+
 __global__ __launch_bounds__(256) void quantize_1x128_kernel(QuantArgs a) {
     // XCD-aware order: dispatch sends consecutive workgroups to consecutive XCDs, so workgroup
     // i works on logical span (i % 8) * (P / 8) + i / 8 (the grid size P is a multiple of 8).
@@ -104,10 +143,50 @@ __global__ __launch_bounds__(256) void quantize_1x128_kernel(QuantArgs a) {
     if (chunk == 0) a.sa[((int64_t)g * a.nkb + kb) * a.rows + r] = s;
 }
 
+// SwiGLU activation and requantisation between the two GEMMs of an MoE expert: X rows hold 2K
+// bf16 values, the gate in columns [0, K) and the up projection in [K, 2K); the K activations
+// silu(gate) * up of a row are quantised per 1x128 block exactly as quantize_1x128_kernel does
+// (codes [G][rows][K], scales [G][K/128][rows]).  Same mapping: 16 lanes per block, 16 blocks
+// per workgroup, XCD-aware order; a lane reads 16 bytes of gate and 16 of up.
+__global__ __launch_bounds__(256) void swiglu_quantize_kernel(QuantArgs a) {
+    const uint32_t P = gridDim.x;
+    const uint32_t wg = (blockIdx.x & 7u) * (P >> 3) + (blockIdx.x >> 3);
+    const uint32_t b = wg * kQuantBlocksPerWG + (threadIdx.x >> 4);
+    if (b >= a.blocks) return;
+    const uint32_t row = fast_div(b, a.div_nkb);
+    const uint32_t kb = b - row * (uint32_t)a.nkb;
+    const uint32_t g = fast_div(row, a.div_rows);
+    const uint32_t r = row - g * (uint32_t)a.rows;
+    if (a.masked_m) {
+        const int32_t c = a.masked_m[g];
+        if ((c < 0 || c > a.rows) && r == 0 && kb == 0 && (threadIdx.x & 15) == 0)
+            atomicOr(a.err, (int32_t)kDevErrBadCount);
+        if ((int32_t)r >= c) return;
+    }
+    const int chunk = threadIdx.x & 15;
+    const uint16_t* xr = a.X + (int64_t)row * (2 * (int64_t)a.K) + kb * 128 + chunk * 8;
+    const Chunk gc = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(xr));
+    const Chunk uc = __builtin_nontemporal_load(reinterpret_cast<const Chunk*>(xr + a.K));
+    float h[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h[2 * i] = swiglu1(__uint_as_float(gc[i] << 16), __uint_as_float(uc[i] << 16));
+        h[2 * i + 1] = swiglu1(__uint_as_float(gc[i] & 0xFFFF0000u), __uint_as_float(uc[i] & 0xFFFF0000u));
+    }
+    float s;
+    const uint2 q = quantize_f32x8(h, &s);
+    *reinterpret_cast<uint2*>(a.A + (int64_t)row * a.K + kb * 128 + chunk * 8) = q;
+    if (chunk == 0) a.sa[((int64_t)g * a.nkb + kb) * a.rows + r] = s;
+}
+
 }  // namespace
 
 void launch_quantize_1x128(const QuantArgs& a, dim3 grid, hipStream_t stream) {
     hipLaunchKernelGGL(quantize_1x128_kernel, grid, dim3(256), 0, stream, a);
+}
+
+void launch_swiglu_quantize(const QuantArgs& a, dim3 grid, hipStream_t stream) {
+    hipLaunchKernelGGL(swiglu_quantize_kernel, grid, dim3(256), 0, stream, a);
 }
 
 }  // namespace fp8gemm

@@ -382,12 +382,15 @@ static KernelEntry stream_entry(const char* name) {
     stream_entry<MT, W, JN, KP, PF>("masked decode " #MT " rows, " #W " waves x " #JN " fragments, phase " #KP ", depth " #PF)
 
 // Masked groups of at most 128 valid rows (one tile per group and N tile, B streamed once per
-// group).  Measured on the 16-group x 4096 x 7168 decode configuration (about 64 valid rows per
-// group): 4 waves x 2 fragments, 2-block phases: 129 us; 8 waves x 1 fragment: 135 us; the tiled
-// kernel with 64-row tiles (B streamed twice for groups past 64 rows): 240 us.
+// group).  Measured on 16 groups x 256 rows (about 64 valid each), graphs of 3 launches:
+//   N = 4096, K = 7168: 4 waves x 2 fragments, 2-block phases 108 us (4.5 TB/s); 8 waves x 1
+//     fragment 113 us; 4 waves x 1 fragment 125 us; the tiled kernel's 128x128 tile 168 us;
+//   N = 7168, K = 2048: 4 waves x 1 fragment 64 us (3.9 TB/s); 8 x 1: 67 us; 4 x 2: 69 us.
+// Splitting K was slower everywhere (the groups times N tiles already fill the CUs).
 const KernelEntry* stream_table(int* count) {
     static const KernelEntry table[] = {
         STREAM_ENTRY(128, 4, 2, 2, 4),
+        STREAM_ENTRY(128, 4, 1, 2, 4),
         STREAM_ENTRY(128, 8, 1, 4, 4),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));

@@ -115,6 +115,41 @@ int fp8gemm_quantize_1x128(const void* X, void* A, float* sa, int64_t M, int64_t
 int fp8gemm_quantize_1x128_masked(const void* X, void* A, float* sa, const int32_t* masked_m,
                                   int32_t G, int64_t M_max, int64_t K, void* stream);
 
+/* SwiGLU activation and requantisation: the step between the two linear layers of an MoE
+ * expert (page "Perpustakaan operator GPU sumber terbuka DeepSeek DeepGEMM memperbarui versi
+ * besar, menambahkan Mega MoE…": an MoE layer at inference is EP dispatch, first linear layer,
+ * SwiGLU activation, second linear layer, EP combine).  The pages do not spell SwiGLU out; the
+ * reading taken is the usual one:
+ *   X [M][2I] bfloat16 (device): the first layer's output, gate in columns [0, I), up projection
+ *   in columns [I, 2I);  h = silu(gate) * up with silu(x) = x / (1 + e^-x), formed in fp32;
+ * then the 1x128 quantiser above on h (fp32 values instead of bf16):
+ *   A [M][I] e4m3 codes (device, written), sa [I/128][M] fp32 (device, written) -- the left
+ *   operand of the second layer.  I: positive multiple of 128 (else FP8GEMM_ERR_BAD_SHAPE).
+ *   X and A 16-byte aligned, sa 4-byte aligned.  Inputs must be finite, with silu(gate) * up
+ *   inside the fp32 range; otherwise the codes and scale of that block are unspecified. */
+int fp8gemm_swiglu_quantize_1x128(const void* X, void* A, float* sa, int64_t M, int64_t I, void* stream);
+
+/* The same for the masked layout: X [G][M_max][2I], A [G][M_max][I], sa [G][I/128][M_max],
+ * masked_m [G] int32 (device); rows at or past masked_m[g] are left untouched; a count outside
+ * [0, M_max] is clamped and flags FP8GEMM_DEVERR_BAD_COUNT. */
+int fp8gemm_swiglu_quantize_1x128_masked(const void* X, void* A, float* sa, const int32_t* masked_m,
+                                         int32_t G, int64_t M_max, int64_t I, void* stream);
+
+/* One MoE expert layer per group on the masked layout (same page: the first linear layer,
+ * SwiGLU and the second linear layer; dispatch and combine are not part of it):
+ *   Y1  = grouped_masked(A, sa, W1, s1)            Y1 [G][M_max][2I] bf16   (first layer)
+ *   Hq, sh = swiglu_quantize_1x128_masked(Y1)      Hq [G][M_max][I] e4m3, sh [G][I/128][M_max]
+ *   out = grouped_masked(Hq, sh, W2, s2)           out [G][M_max][H] bf16   (second layer)
+ * with A [G][M_max][H], sa [G][H/128][M_max], W1 [G][2I][H], s1 [G][2I/128][H/128],
+ * W2 [G][H][I], s2 [G][H/128][I/128].  Y1, Hq and sh are caller-owned workspaces (device),
+ * nothing is allocated.  H and I: positive multiples of 128.  Every argument of the three steps
+ * is checked before anything is enqueued; the three launches follow each other on `stream`.
+ * Rows at or past masked_m[g] of Y1, Hq, sh and out are left untouched. */
+int fp8gemm_moe_expert_masked(const void* A, const float* sa, const void* W1, const float* s1,
+                              const void* W2, const float* s2, const int32_t* masked_m, void* Y1,
+                              void* Hq, float* sh, void* out, int32_t G, int64_t M_max, int64_t H,
+                              int64_t I, int64_t expected_m, void* stream);
+
 /* Device-side precondition flags (bits of the device error word). */
 #define FP8GEMM_DEVERR_BAD_INDEX 1 /* contiguous: an m_indices entry outside [-1, G) or off its block's group */
 #define FP8GEMM_DEVERR_BAD_COUNT 2 /* masked GEMM or quantiser: a masked_m entry outside [0, M_max] */

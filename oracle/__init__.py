@@ -45,6 +45,7 @@ def _load():
         lib.oracle_e4m3_code.argtypes = [ctypes.c_double]
         lib.oracle_quantize_1x128.restype = ctypes.c_int
         lib.oracle_quantize_1x128.argtypes = [P, I64, I64, P, P, ctypes.c_int]
+        lib.oracle_swiglu_quantize_1x128.argtypes = [P, I64, I64, P, P, P, ctypes.c_int]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = [ctypes.c_int]
         lib.oracle_gemm_nt.restype = ctypes.c_int
@@ -179,3 +180,18 @@ def quantize_1x128(X_bits, nthreads: int = 0):
     sa = np.empty((M, -(-K // 128)), dtype=np.float32)
     _load().oracle_quantize_1x128(_ptr(X), M, K, _ptr(codes), _ptr(sa), nthreads)
     return codes, sa
+
+
+def swiglu_quantize_1x128(X_bits, nthreads: int = 0):
+    """SwiGLU + requantisation: X bf16 bit patterns (uint16 [M, 2I], gate | up) -> (codes uint8
+    [M, I], sa float32 [M, ceil(I/128)], h float64 [M, I]) with h = silu(gate) * up (definition
+    in ``oracle.c``)."""
+    X = _c(X_bits, np.uint16)
+    M, I2 = X.shape
+    assert I2 % 2 == 0
+    I = I2 // 2
+    codes = np.empty((M, I), dtype=np.uint8)
+    sa = np.empty((M, -(-I // 128)), dtype=np.float32)
+    h = np.empty((M, I), dtype=np.float64)
+    _load().oracle_swiglu_quantize_1x128(_ptr(X), M, I, _ptr(codes), _ptr(sa), _ptr(h), nthreads)
+    return codes, sa, h

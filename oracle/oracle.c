@@ -302,21 +302,38 @@ ORACLE_API int oracle_elements(const uint8_t* A, const float* sa, const uint8_t*
 
 /* ---- activation quantiser, 1x128 blocks ---------------------------------------------------- */
 
-/* X [M][K] bfloat16 bit patterns -> codes [M][K] (E4M3) and sa [M][ceil(K/128)] (fp32), one scale
- * per block of 128 consecutive K values of a row (a shorter last block when K is not a multiple
- * of 128).  Per block:
- *   amax = max |x|                         (exact: |x| of a bf16 value is a bf16 value)
+/* One block of n <= 128 fp32 values xs -> n codes and the block's scale:
+ *   amax = max |x|
  *   amax = max(amax, fp32(1e-4))           (an all-zero or tiny block keeps a finite scale)
  *   s    = fp32(amax / 448)                (the scale stored in sa)
  *   v    = fp32(x / s)                     (the value to encode)
  *   code = E4M3_rne(v), saturating at +-448
  * Both quotients are formed in fp64 and rounded once to fp32; for a quotient of two fp32 values
  * fp64 carries more than 2*24+2 bits, so that double rounding equals the correctly rounded fp32
- * quotient.  Inputs must be finite (a NaN or infinity gives unspecified codes).  Returns 0. */
+ * quotient. */
+static float quantize_block(const float* xs, int64_t n, uint8_t* codes) {
+    const float floor_amax = 1e-4f;
+    float amax = 0.0f;
+    for (int64_t k = 0; k < n; ++k) {
+        float a = fabsf(xs[k]);
+        if (a > amax) amax = a;
+    }
+    if (amax < floor_amax) amax = floor_amax;
+    float s = (float)((double)amax / 448.0);
+    for (int64_t k = 0; k < n; ++k) {
+        float v = (float)((double)xs[k] / (double)s);
+        codes[k] = oracle_e4m3_code((double)v);
+    }
+    return s;
+}
+
+/* X [M][K] bfloat16 bit patterns -> codes [M][K] (E4M3) and sa [M][ceil(K/128)] (fp32), one scale
+ * per block of 128 consecutive K values of a row (a shorter last block when K is not a multiple
+ * of 128), by quantize_block on the bf16 values (|x| of a bf16 value is a bf16 value, so amax is
+ * exact).  Inputs must be finite (a NaN or infinity gives unspecified codes).  Returns 0. */
 ORACLE_API int oracle_quantize_1x128(const uint16_t* X, int64_t M, int64_t K, uint8_t* codes,
                                      float* sa, int nthreads) {
     int64_t nkb = (K + 127) / 128;
-    const float floor_amax = 1e-4f;
     int nt = pick_threads(nthreads);
     (void)nt;
 #pragma omp parallel for schedule(static) num_threads(nt)
@@ -324,20 +341,53 @@ ORACLE_API int oracle_quantize_1x128(const uint16_t* X, int64_t M, int64_t K, ui
         for (int64_t kb = 0; kb < nkb; ++kb) {
             int64_t k0 = kb * 128, k1 = k0 + 128 < K ? k0 + 128 : K;
             float xs[128];
-            float amax = 0.0f;
             for (int64_t k = k0; k < k1; ++k) {
                 uint32_t bits = (uint32_t)X[m * K + k] << 16;   /* bf16 is the top half of fp32 */
                 memcpy(&xs[k - k0], &bits, sizeof bits);
-                float a = fabsf(xs[k - k0]);
-                if (a > amax) amax = a;
             }
-            if (amax < floor_amax) amax = floor_amax;
-            float s = (float)((double)amax / 448.0);
+            float s = quantize_block(xs, k1 - k0, codes + m * K + k0);
             sa[m * nkb + kb] = s;
+        }
+    }
+    return 0;
+}
+
+/* ---- SwiGLU and requantisation (the step between an MoE expert's two linear layers) -------- */
+
+/* Page "Perpustakaan operator GPU sumber terbuka DeepSeek DeepGEMM memperbarui versi besar,
+ * menambahkan Mega MoE…" (the Mega MoE news item): an MoE layer at inference is EP dispatch, a
+ * first linear layer, SwiGLU activation, a second linear layer and EP combine.  SwiGLU is not
+ * spelled out there; the reading taken is the usual one, with the first layer's output row split
+ * into halves, gate = columns [0, I), up = columns [I, 2I):
+ *   h = silu(gate) * up,  silu(x) = x * sigmoid(x) = x / (1 + e^-x)
+ * formed in fp64 from the bf16 inputs and rounded once to fp32 (the activation handed on), then
+ * quantised per block of 128 consecutive columns with quantize_block (the left operand of the
+ * second layer).  X [M][2I] bf16 bit patterns -> codes [M][I], sa [M][ceil(I/128)], and the fp64
+ * activations h [M][I] when h is not NULL.  Inputs must be finite with h inside the fp32 range.
+ * Returns 0. */
+ORACLE_API int oracle_swiglu_quantize_1x128(const uint16_t* X, int64_t M, int64_t I, uint8_t* codes,
+                                            float* sa, double* h, int nthreads) {
+    int64_t nkb = (I + 127) / 128;
+    int nt = pick_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* gate = X + m * 2 * I;
+        const uint16_t* up = gate + I;
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+            int64_t k0 = kb * 128, k1 = k0 + 128 < I ? k0 + 128 : I;
+            float xs[128];
             for (int64_t k = k0; k < k1; ++k) {
-                float v = (float)((double)xs[k - k0] / (double)s);
-                codes[m * K + k] = oracle_e4m3_code((double)v);
+                uint32_t gb = (uint32_t)gate[k] << 16, ub = (uint32_t)up[k] << 16;
+                float g, u;
+                memcpy(&g, &gb, sizeof g);
+                memcpy(&u, &ub, sizeof u);
+                double silu = (double)g / (1.0 + exp(-(double)g));
+                double v = silu * (double)u;
+                if (h) h[m * I + k] = v;
+                xs[k - k0] = (float)v;
             }
+            sa[m * nkb + kb] = quantize_block(xs, k1 - k0, codes + m * I + k0);
         }
     }
     return 0;

@@ -25,9 +25,15 @@ MUTANTS = {
     "quant_floor_dropped": ("if (amax < floor_amax) amax = floor_amax;", ""),
     "quant_scale_divisor": ("float s = (float)((double)amax / 448.0);", "float s = (float)((double)amax / 240.0);"),
     "quant_sa_transposed": ("sa[m * nkb + kb] = s;", "sa[kb * M + m] = s;"),
-    "quant_multiplies_by_reciprocal": ("float v = (float)((double)xs[k - k0] / (double)s);",
-                                       "float v = xs[k - k0] * (1.0f / s);"),
-    "quant_amax_skips_last": ("if (a > amax) amax = a;", "if (a > amax && k + 1 < k1) amax = a;"),
+    "quant_multiplies_by_reciprocal": ("float v = (float)((double)xs[k] / (double)s);",
+                                       "float v = xs[k] * (1.0f / s);"),
+    "quant_amax_skips_last": ("if (a > amax) amax = a;", "if (a > amax && k + 1 < n) amax = a;"),
+    "swiglu_halves_swapped": ("const uint16_t* up = gate + I;\n", "const uint16_t* up = gate; gate += I;\n"),
+    "swiglu_sigmoid_not_silu": ("double silu = (double)g / (1.0 + exp(-(double)g));",
+                                "double silu = 1.0 / (1.0 + exp(-(double)g));"),
+    "swiglu_sign_of_exponent": ("double silu = (double)g / (1.0 + exp(-(double)g));",
+                                "double silu = (double)g / (1.0 + exp((double)g));"),
+    "swiglu_activation_perturbed": ("xs[k - k0] = (float)v;", "xs[k - k0] = (float)v * 1.0000001f;"),
 }
 
 

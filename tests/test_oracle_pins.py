@@ -509,3 +509,81 @@ def test_quantiser_matches_library_composition():
     codes, sa = oracle.quantize_1x128(bits)
     c2, s2 = W.quantize_1x128(widen(bits))
     assert np.array_equal(codes, c2) and np.array_equal(sa, s2)
+
+
+# ------------------------------------------------------------------------------------------
+# SwiGLU and requantisation (between an MoE expert's two linear layers)
+# ------------------------------------------------------------------------------------------
+
+def _swiglu_input(seed, M, I, gate_scale=3.0):
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((M, I)).astype(np.float32) * np.float32(gate_scale)
+    u = rng.standard_normal((M, I)).astype(np.float32)
+    return W.bf16_bits(np.concatenate([g, u], axis=1))
+
+
+def test_swiglu_matches_library_silu_and_quantiser():
+    """h against torch's fp64 silu of the first half times the second half; codes and scales
+    against the input recipe's quantiser (torch's fp32 division and float8 cast) on fp32(h)."""
+    I = 640
+    bits = _swiglu_input(51, 24, I)
+    codes, sa, h = oracle.swiglu_quantize_1x128(bits)
+    x = torch.from_numpy(widen(bits).astype(np.float64))
+    ref = (torch.nn.functional.silu(x[:, :I]) * x[:, I:]).numpy()
+    assert np.allclose(h, ref, rtol=1e-14, atol=0)
+    c2, s2 = W.quantize_1x128(ref.astype(np.float32))
+    assert np.array_equal(codes, c2) and np.array_equal(sa, s2)
+
+
+def test_swiglu_closed_forms():
+    """silu(0) = 0 and a zero up half gives 0; silu(x) - silu(-x) = x (sigmoid(x) + sigmoid(-x)
+    = 1); silu(x) / silu(-x) = -e^x (sigmoid(x) / sigmoid(-x) = e^x); silu(x) -> x for large x."""
+    gates = np.array([0.0, 1.1015625, -1.1015625, 1.5, -1.5, 7.0, -7.0, 2.0, 40.0], np.float32)
+    ups = np.array([5.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 0.0, 1.0], np.float32)
+    I = 128
+    x = np.zeros((1, 2 * I), np.float32)
+    x[0, :9], x[0, I:I + 9] = gates, ups
+    _, _, h = oracle.swiglu_quantize_1x128(W.bf16_bits(x))
+    h = h[0]
+    assert h[0] == 0.0 and h[7] == 0.0
+    for i in (1, 3, 5):
+        t = float(gates[i])
+        assert abs((h[i] - h[i + 1]) - t) <= 1e-15 * t
+        assert abs(h[i] / h[i + 1] + math.exp(t)) <= 1e-14 * math.exp(t)
+    assert abs(h[8] - 40.0) <= 40.0 * 1e-16 + 40.0 * math.exp(-40.0) * 1.01
+    assert np.all(h[9:] == 0.0)
+
+
+def test_swiglu_large_gate_is_the_quantiser_of_the_product():
+    """gate = 32: sigmoid(32) = 1 - 1.3e-14, so fp32(h) = 32 * up exactly (a bf16 value), and the
+    codes and scales equal the 1x128 quantiser's on 32 * up; gate = -120: h is a signed zero."""
+    rng = np.random.default_rng(52)
+    I = 384
+    up = widen(W.bf16_bits(rng.standard_normal((6, I)).astype(np.float32)))
+    x = np.concatenate([np.full((6, I), 32.0, np.float32), up], axis=1)
+    codes, sa, h = oracle.swiglu_quantize_1x128(W.bf16_bits(x))
+    c2, s2 = oracle.quantize_1x128(bf16_bits_exact(up * np.float32(32.0)))
+    assert np.array_equal(codes, c2) and np.array_equal(sa, s2)
+    x[:, :I] = -120.0
+    codes, sa, h = oracle.swiglu_quantize_1x128(W.bf16_bits(x))
+    assert np.all(np.abs(h) < 1e-40)
+    assert np.all(sa == np.float32(FLOOR / np.float32(448)))
+    assert np.all((codes & 0x7F) == 0)
+
+
+def test_swiglu_quantiser_invariants():
+    """Every block's largest code is +-448 (no floored block here); code * s is within half an
+    E4M3 unit of fp32(h); flipping the sign of the up half flips every code's sign bit."""
+    I = 512
+    bits = _swiglu_input(53, 16, I, gate_scale=6.0)
+    codes, sa, h = oracle.swiglu_quantize_1x128(bits)
+    dec = _DEC[codes].astype(np.float64)
+    assert np.all(np.abs(dec).reshape(16, -1, 128).max(axis=2) == 448)
+    h32 = h.astype(np.float32).astype(np.float64)
+    s = np.repeat(sa.astype(np.float64), 128, axis=1)
+    err = np.abs(dec * s - h32)
+    assert np.all(err <= ((2.0 ** -4 + 2.0 ** -23) * np.abs(h32) + 2.0 ** -10 * s) * (1 + 1e-12))
+    flipped = bits.copy()
+    flipped[:, I:] ^= np.uint16(0x8000)
+    c2, s2, _ = oracle.swiglu_quantize_1x128(flipped)
+    assert np.array_equal(c2, codes ^ np.uint8(0x80)) and np.array_equal(s2, sa)

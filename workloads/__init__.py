@@ -67,6 +67,19 @@ class Masked:
     expected_m: int = 0
 
 
+@dataclass
+class MoeExpert:
+    """One MoE expert layer per group on the masked layout: out = swiglu(A W1^T) W2^T."""
+    A: np.ndarray          # uint8 [G, M_max, H]
+    sa: np.ndarray         # float32 [G, M_max, H/128]
+    W1: np.ndarray         # uint8 [G, 2I, H]     (gate rows [0, I), up rows [I, 2I))
+    s1: np.ndarray         # float32 [G, 2I/128, H/128]
+    W2: np.ndarray         # uint8 [G, H, I]
+    s2: np.ndarray         # float32 [G, ceil(H/128), I/128]
+    masked_m: np.ndarray   # int32 [G]
+    expected_m: int = 0
+
+
 # ---------------------------------------------------------------------------------------------
 # Random draws and quantisation
 # ---------------------------------------------------------------------------------------------
@@ -218,6 +231,36 @@ def masked(masked_m, M_max: int, N: int, K: int, seed: int, expected_m: int = 0)
                   expected_m)
 
 
+def moe_expert(masked_m, M_max: int, H: int, I: int, seed: int, expected_m: int = 0) -> MoeExpert:
+    """Activations as in ``masked`` (hidden size H); both layers' weights N(0,1) quantised per
+    128x128 block with their scales divided by sqrt(fan-in), so the first layer's outputs (the
+    SwiGLU inputs) and the second layer's outputs are of order one."""
+    first = masked(masked_m, M_max, 2 * I, H, seed, expected_m)
+    rng = np.random.default_rng(seed + 7)
+    W2, s2 = zip(*(_weights(rng, H, I) for _ in range(len(masked_m))))
+    s1 = (first.sb / np.float32(np.sqrt(H))).astype(np.float32)
+    s2 = (np.stack(s2) / np.float32(np.sqrt(I))).astype(np.float32)
+    return MoeExpert(first.A, first.sa, first.B, s1, np.stack(W2), s2, first.masked_m, expected_m)
+
+
+def moe_config4() -> MoeExpert:
+    """The masked decode configuration as a whole DeepSeek-V3-sized expert layer: 16 groups,
+    M_max=256, masked_m ~ Poisson(64), hidden size H=7168, expert intermediate size I=2048 (the
+    first layer is the configuration's N=4096 x K=7168 GEMM, the second N=7168 x K=2048)."""
+    return moe_expert(config4_masked_m(), 256, 7168, 2048, seed=40, expected_m=64)
+
+
+def swiglu_input_bf16(M: int, I: int, seed: int) -> np.ndarray:
+    """bf16 [M, 2I] first-layer outputs (gate | up): N(0,1) gates times 2 (over the curved part of
+    silu, both signs), N(0,1) ups with 1% outlier channels of gain 16."""
+    rng = np.random.default_rng(seed)
+    gain = np.ones(I, dtype=np.float32)
+    gain[rng.choice(I, size=max(1, I // 100), replace=False)] = 16.0
+    g = normal(rng, (M, I)) * np.float32(2.0)
+    u = normal(rng, (M, I)) * gain
+    return bf16_bits(np.concatenate([g, u], axis=1))
+
+
 # --- the five configurations -----------------------------------------------------------------
 
 def config0() -> Dense:
@@ -309,6 +352,21 @@ def dense_work(M, N, K):
     """(flop, bytes): 2MNK and A + sa + B + sb + D bytes."""
     nkb, nnb = -(-K // BLOCK), -(-N // BLOCK)
     return 2 * M * N * K, M * K + 4 * M * nkb + N * K + 4 * nnb * nkb + 2 * M * N
+
+
+def swiglu_quantize_work(rows: int, I: int):
+    """Bytes of the SwiGLU + requantisation step: bf16 gate and up in, E4M3 codes and fp32 scales
+    out."""
+    return rows * 2 * I * 2 + rows * I + 4 * rows * (-(-I // BLOCK))
+
+
+def moe_expert_work(valid_rows_per_group, H, I, G):
+    """(flop, bytes) of one masked expert layer: the first layer (N = 2I, K = H), the SwiGLU step
+    and the second layer (N = H, K = I); masked counts as index bytes of both GEMMs."""
+    f1, b1 = grouped_work(valid_rows_per_group, 2 * I, H, index_bytes=4 * G)
+    f2, b2 = grouped_work(valid_rows_per_group, H, I, index_bytes=4 * G)
+    rows = int(sum(valid_rows_per_group))
+    return f1 + f2, b1 + swiglu_quantize_work(rows, I) + b2
 
 
 def grouped_work(valid_rows_per_group, N, K, index_bytes):
