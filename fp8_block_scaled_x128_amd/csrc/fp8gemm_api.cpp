@@ -234,7 +234,7 @@ Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_row
             }
         }
     } else if (m >= 1024 && N >= 256 && layout == kContiguous) {
-        c.entry = find_entry(layout, 128, 256, 2, 4, 2);
+        c.entry = find_entry(layout, 256, 256, 4, 2, 2);
     } else {
         c.entry = find_entry(layout, 128, 128, 2, 2, 4);
     }
@@ -267,7 +267,8 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream)
     a.div_groups = make_fastdiv((uint32_t)groups);
     if (units >= (int64_t(1) << 30)) return FP8GEMM_ERR_UNSUPPORTED;   // unit ids stay far below 2^31
     a.units = (int32_t)units;
-    a.group_m = (layout != kMasked && a.tiles_m >= 8) ? (layout == kDense ? 4 : 8) : 1;
+    // bands of M tiles in the unit order: 4 for 256-row tiles, 8 for 128-row contiguous tiles
+    a.group_m = (layout != kMasked && a.tiles_m >= 8) ? (layout == kDense || e.bm >= 256 ? 4 : 8) : 1;
     a.div_splits = make_fastdiv((uint32_t)a.splits);
     a.div_tiles_m = make_fastdiv((uint32_t)a.tiles_m);
     a.div_tiles_n = make_fastdiv((uint32_t)a.tiles_n);

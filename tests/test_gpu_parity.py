@@ -259,6 +259,41 @@ def test_every_contiguous_kernel_config(entry, split):
     assert_close(gpu_bits(D), ref, mask=v[:, None].repeat(D.shape[1], 1), what=cfg)
 
 
+@pytest.mark.parametrize("split", [1, 2])
+def test_contiguous_256_row_tiles_spanning_two_groups(split):
+    """256-row tiles whose two 128-row blocks belong to different groups run one pass per group
+    (rows of the other group not stored); tiles of one group, padding-only blocks, a ragged
+    end; a 2-CU cap (several tiles per workgroup, passes reusing the LDS ring)."""
+    c = W.contiguous([100, 0, 3, 128, 60, 250, 7], 0, 520, 640, seed=97 + split, packed=True)
+    M, N = c.A.shape[0], 520
+    ref, valid = oracle.grouped_contiguous(c.A, c.sa, c.B, c.sb, c.m_indices)
+    v = valid.astype(bool)
+    for cap in (0, 2):
+        fg.set_num_cus(cap)
+        try:
+            with forced(256, 256, 4, 2, 2, split):
+                D = run_contig(c, out=sentinel_tensor((M, N)))
+                cfg = fg.last_config()
+        finally:
+            fg.set_num_cus(0)
+        assert "tile=256x256" in cfg, cfg
+        got = gpu_bits(D)
+        assert_close(got, ref, mask=v[:, None].repeat(N, 1), what=cfg)
+        assert np.all(got[~v] == SENTINEL), "padding rows were written"
+    # integer codes, power-of-two scales: bit-exact through the two-pass tiles
+    rng = np.random.default_rng(11)
+    A, B = int_codes(rng, c.A.shape), int_codes(rng, c.B.shape)
+    sa = (2.0 ** rng.integers(-1, 2, size=c.sa.shape)).astype(np.float32)
+    sb = (2.0 ** rng.integers(-1, 2, size=c.sb.shape)).astype(np.float32)
+    c2 = W.Contiguous(A, sa, B, sb, c.m_indices)
+    ref2, _ = oracle.grouped_contiguous(A, sa, B, sb, c.m_indices)
+    with forced(256, 256, 4, 2, 2, split):
+        D2 = run_contig(c2)
+    assert_bit_exact(gpu_bits(D2)[v], ref2[v], what="contiguous 256-row tiles, integer inputs")
+    assert fg.read_device_error() == 0
+    say("contiguous 256-row tiles", cfg)
+
+
 def test_contiguous_equals_per_group_dense():
     c = W.contiguous([256, 384], 0, 512, 1024, seed=91, packed=True)
     D = gpu_bits(run_contig(c))
