@@ -399,7 +399,7 @@ GROUPED_CALLS = 3      # calls per timed graph of the grouped configurations
 def bench_grouped(fg, W, torch, dev, stream, reps=10):
     out = {}
     for name, make in (("contiguous_cfg2", W.config2), ("contiguous_cfg3", W.config3),
-                       ("masked_cfg4", W.config4)):
+                       ("masked_cfg4", W.config4), ("masked_fp8xfp4_cfg4", W.config4_fp4)):
         t0 = time.time()
         w = make()
         A, B, sb = (torch.from_numpy(x).to(dev) for x in (w.A, w.B, w.sb))
@@ -411,6 +411,13 @@ def bench_grouped(fg, W, torch, dev, stream, reps=10):
             call = lambda: fg.grouped_contiguous(A, sa, B, sb, idx, out=D, stream=stream)
             counts = [int(np.sum(w.m_indices == g)) for g in range(w.B.shape[0])]
             flop, byts = W.grouped_work(counts, N, K, index_bytes=4 * w.A.shape[0])
+        elif "fp4" in name:
+            K = w.A.shape[2]
+            mm = torch.from_numpy(w.masked_m).to(dev)
+            D = torch.empty((w.A.shape[0], w.A.shape[1], N), dtype=torch.bfloat16, device=dev)
+            call = lambda: fg.fp8fp4_grouped_masked(A, sa, B, sb, mm, w.expected_m, out=D, stream=stream)
+            counts = [int(x) for x in w.masked_m]
+            flop, byts = W.grouped_fp4_work(counts, N, K, index_bytes=4 * len(counts))
         else:
             mm = torch.from_numpy(w.masked_m).to(dev)
             D = torch.empty((w.A.shape[0], w.A.shape[1], N), dtype=torch.bfloat16, device=dev)

@@ -6,6 +6,7 @@ C ABI declared in include/fp8gemm.h.  torch supplies device memory and the curre
     D = gemm_nt(A, sa, B, sb)                              # dense NT, bf16 out
     D = grouped_contiguous(A, sa, B, sb, m_indices)        # MoE, groups concatenated along M
     D = grouped_masked(A, sa, B, sb, masked_m, expected_m) # MoE, fixed per-group capacity
+    D = fp8fp4_grouped_masked(A, sa, B4, sb4, masked_m, expected_m)  # the same, B in E2M1 + E8M0
     A, sa = quantize_1x128(X)                              # bf16 activations -> codes + scales
     A, sa = quantize_1x128_masked(X, masked_m)             # the same, masked layout
     H, sh = swiglu_quantize_1x128(Y)                       # silu(gate) * up -> codes + scales
@@ -22,7 +23,7 @@ import ctypes
 import os
 
 __all__ = ["gemm_nt", "grouped_contiguous", "grouped_masked", "quantize_1x128",
-           "quantize_1x128_masked", "swiglu_quantize_1x128", "swiglu_quantize_1x128_masked",
+           "quantize_1x128_masked", "fp8fp4_grouped_masked", "swiglu_quantize_1x128", "swiglu_quantize_1x128_masked",
            "moe_expert_masked", "init", "set_num_cus",
            "last_config", "read_device_error", "status_string", "lib", "library_path",
            "Fp8GemmError", "STATUS", "DEVERR_BAD_INDEX", "DEVERR_BAD_COUNT"]
@@ -45,6 +46,7 @@ SIGNATURES = {
     "fp8gemm_grouped_masked": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _P]),
     "fp8gemm_quantize_1x128": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "fp8gemm_quantize_1x128_masked": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _P]),
+    "fp8gemm_fp8fp4_grouped_masked": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _P]),
     "fp8gemm_swiglu_quantize_1x128": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "fp8gemm_swiglu_quantize_1x128_masked": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _P]),
     "fp8gemm_moe_expert_masked": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -235,6 +237,40 @@ def grouped_masked(A, sa, B, sb, masked_m, expected_m: int, out=None, stream=Non
                                           masked_m.data_ptr(), D.data_ptr(), G, M_max, N, K,
                                           int(expected_m), _stream(stream, A.device))
     _check(st, "fp8gemm_grouped_masked")
+    return D
+
+
+def _u8(t, name):
+    torch = _torch()
+    if t.dtype != torch.uint8:
+        raise TypeError("%s must be uint8, got %s" % (name, t.dtype))
+    return _dev_contig(t, name)
+
+
+def fp8fp4_grouped_masked(A, sa, B, sb, masked_m, expected_m: int, out=None, stream=None):
+    """Masked layout with B in E2M1: A [G,M_max,K] e4m3 codes, sa [G,K/128,M_max], B uint8
+    [G,N,K/2] (two E2M1 codes per byte, even element in the low nibble), sb uint8 [G,N,K/32]
+    (E8M0 scales per 32 K), masked_m int32 [G].  Rows past masked_m[g] of ``out`` are left
+    untouched (zeros when ``out`` is allocated here)."""
+    torch = _torch()
+    A = _codes(A, "A")
+    B, sb = _u8(B, "B"), _u8(sb, "sb")
+    sa = _f32(sa, "sa")
+    masked_m = _i32(masked_m, "masked_m")
+    _shape_check(A.dim() == 3 and B.dim() == 3 and A.shape[0] == B.shape[0] and 2 * B.shape[2] == A.shape[2],
+                 "A [G,M_max,K] and B [G,N,K/2]")
+    G, M_max, K = A.shape
+    N = B.shape[1]
+    _shape_check(tuple(sa.shape) == (G, K // 128, M_max) and tuple(sb.shape) == (G, N, K // 32)
+                 and tuple(masked_m.shape) == (G,), "sa [G,K/128,M_max], sb [G,N,K/32], masked_m [G]")
+    if out is None:
+        out = torch.zeros((G, M_max, N), dtype=torch.bfloat16, device=A.device)
+    D = _out(out, (G, M_max, N), A.device)
+    with torch.cuda.device(A.device):
+        st = lib().fp8gemm_fp8fp4_grouped_masked(A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(),
+                                                 masked_m.data_ptr(), D.data_ptr(), G, M_max, N, K,
+                                                 int(expected_m), _stream(stream, A.device))
+    _check(st, "fp8gemm_fp8fp4_grouped_masked")
     return D
 
 

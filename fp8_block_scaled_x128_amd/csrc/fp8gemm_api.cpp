@@ -131,27 +131,29 @@ int find_entry(int layout, int bm, int bn, int wm, int wn, int stages) {
     return -1;
 }
 
-int find_stream(int layout, int mt, int w, int jn, int kp, int pf) {
+int find_stream(int layout, int mt, int w, int jn, int kp, int pf, bool fp4 = false) {
     const std::vector<KernelEntry>& tab = kernels();
     for (size_t i = 0; i < tab.size(); ++i)
-        if (tab[i].kind == kKindStream && tab[i].layout == layout && tab[i].bm == mt && tab[i].waves_n == w &&
-            tab[i].jn == jn && tab[i].kp == kp && tab[i].stages == pf)
+        if (tab[i].kind == kKindStream && tab[i].layout == layout && tab[i].fp4 == fp4 && tab[i].bm == mt &&
+            tab[i].waves_n == w && tab[i].jn == jn && tab[i].kp == kp && tab[i].stages == pf)
             return (int)i;
     return -1;
 }
 
 // Optional override for experiments:
 //   FP8GEMM_FORCE_CONFIG=BMxBN:WMxWN:STAGES:SPLIT            (tiled kernel)
-//   FP8GEMM_FORCE_CONFIG=stream:MT:W:JN:KP:PF:SPLIT           (masked decode kernel)
-bool forced_config(int layout, int* idx, int* split) {
+//   FP8GEMM_FORCE_CONFIG=stream:MT:W:JN:KP:PF:SPLIT           (masked decode kernel; with an
+//                                                             E2M1 B, its E2M1 configuration)
+bool forced_config(int layout, bool fp4, int* idx, int* split) {
     const char* s = std::getenv("FP8GEMM_FORCE_CONFIG");
     if (!s || !*s) return false;
     int i = -1, sp = 1;
     if (std::strncmp(s, "stream:", 7) == 0) {
         int mt, w, jn, kp, pf;
         if (std::sscanf(s + 7, "%d:%d:%d:%d:%d:%d", &mt, &w, &jn, &kp, &pf, &sp) < 6) return false;
-        i = find_stream(layout, mt, w, jn, kp, pf);
+        i = find_stream(layout, mt, w, jn, kp, pf, fp4);
     } else {
+        if (fp4) return false;
         int bm, bn, wm, wn, st;
         if (std::sscanf(s, "%dx%d:%dx%d:%d:%d", &bm, &bn, &wm, &wn, &st, &sp) < 6) return false;
         i = find_entry(layout, bm, bn, wm, wn, st);
@@ -180,10 +182,10 @@ int pick_split(int64_t tiles, int nkb, int cus) {
 // tile per group and N tile, B read once straight into registers.  K splits only when the groups
 // times N tiles leave CUs idle.  Returns -1 when the kernel's 32-bit per-lane offsets cannot
 // address K (then the tiled kernel serves the call).
-Choice choose_masked_decode(int64_t N, int nkb, int64_t groups, int cus) {
+Choice choose_masked_decode(int64_t N, int nkb, int64_t groups, int cus, bool fp4) {
     const int64_t K = (int64_t)nkb * 128;
     // short K (few blocks per unit): narrower N tiles, so more units overlap their start-up
-    Choice c{K <= 2048 ? find_stream(kMasked, 128, 4, 1, 2, 4) : find_stream(kMasked, 128, 4, 2, 2, 4), 1};
+    Choice c{K <= 2048 ? find_stream(kMasked, 128, 4, 1, 2, 4, fp4) : find_stream(kMasked, 128, 4, 2, 2, 4, fp4), 1};
     if (c.entry < 0) return c;
     const KernelEntry& e = kernels()[c.entry];
     if ((int64_t)std::max(e.bm, e.bn + 1) * K >= (int64_t(1) << 31)) return Choice{-1, 1};
@@ -198,14 +200,16 @@ Choice choose_masked_decode(int64_t N, int nkb, int64_t groups, int cus) {
 //    and split-K to reach that count on narrow N.
 //  - >= 1024 rows (prefill): MFMA-bound; 256x256 tiles, 8 waves.
 //  - in between: 128x128 tiles.
-Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_rows, int G, int cus) {
+Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_rows, int G, int cus, bool fp4) {
     Choice c{-1, 1};
     int forced = -1, fsplit = 1;
-    if (forced_config(layout, &forced, &fsplit)) return Choice{forced, fsplit};
+    if (forced_config(layout, fp4, &forced, &fsplit)) return Choice{forced, fsplit};
     const int64_t m = (layout == kMasked) ? std::max<int64_t>(1, std::min(expected_rows, rows)) : rows;
     const int64_t groups = (layout == kMasked) ? G : 1;
+    // an E2M1 B runs only on the masked decode kernel (groups past 128 rows take several M tiles)
+    if (fp4) return choose_masked_decode(N, nkb, groups, cus, true);
     if (layout == kMasked && m <= 128) {
-        c = choose_masked_decode(N, nkb, groups, cus);
+        c = choose_masked_decode(N, nkb, groups, cus, false);
         if (c.entry >= 0) return c;
     }
     if (m <= 64) {
@@ -245,13 +249,13 @@ Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_row
     return c;
 }
 
-int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream) {
+int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream, bool fp4 = false) {
     DeviceState* d = nullptr;
     int st = device_state(&d);
     if (st != FP8GEMM_OK) return st;
     int cap = g_cu_cap.load();
     int cus = (cap > 0 && cap < d->cus) ? cap : d->cus;
-    Choice c = choose(layout, a.rows, a.N, a.nkb, expected_rows, a.G, cus);
+    Choice c = choose(layout, a.rows, a.N, a.nkb, expected_rows, a.G, cus, fp4);
     if (c.entry < 0) return FP8GEMM_ERR_UNSUPPORTED;
     const KernelEntry& e = kernels()[c.entry];
     if (e.kind == kKindStream && (int64_t)std::max(e.bm, e.bn + 1) * a.K >= (int64_t(1) << 31))
@@ -291,7 +295,7 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream)
     int64_t slots = (int64_t)cus * d->occupancy[c.entry];
     int64_t grid = std::min<int64_t>(a.units, slots);
     if (grid <= 0) return FP8GEMM_OK;
-    const char* lname = layout == kDense ? "nt" : (layout == kContiguous ? "contiguous" : "masked");
+    const char* lname = layout == kDense ? "nt" : (layout == kContiguous ? "contiguous" : (fp4 ? "masked fp8xfp4" : "masked"));
     if (e.kind == kKindStream)
         std::snprintf(g_last_config, sizeof g_last_config,
                       "%s stream tile=%dx%d waves=%d jn=%d phase=%d depth=%d split=%d kb_per_split=%d "
@@ -526,6 +530,37 @@ int fp8gemm_grouped_masked(const void* A, const float* sa, const void* B, const 
     a.nnb = (int32_t)((N + 127) / 128);
     int64_t hint = expected_m > 0 ? std::min(expected_m, M_max) : M_max;
     return launch(kMasked, a, hint, static_cast<hipStream_t>(stream));
+}
+
+int fp8gemm_fp8fp4_grouped_masked(const void* A, const float* sa, const void* B, const uint8_t* sb,
+                                  const int32_t* masked_m, void* D, int32_t G, int64_t M_max, int64_t N,
+                                  int64_t K, int64_t expected_m, void* stream) {
+    if (G <= 0 || M_max < 0 || N < 0 || expected_m < 0) return FP8GEMM_ERR_BAD_SHAPE;
+    int st = check_k(K);
+    if (st != FP8GEMM_OK) return st;
+    if ((int64_t)G * M_max > kMaxRows || N > kMaxRows || (int64_t)G * M_max * K >= kMaxBytes ||
+        (int64_t)G * N * K >= kMaxBytes || 257 * K / 2 >= (int64_t(1) << 31))
+        return FP8GEMM_ERR_UNSUPPORTED;
+    if (M_max == 0 || N == 0) return FP8GEMM_OK;
+    if (!A || !sa || !B || !sb || !D || !masked_m) return FP8GEMM_ERR_NULL_PTR;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
+        !aligned(masked_m, 4))
+        return FP8GEMM_ERR_MISALIGNED;
+    KernelArgs a{};
+    a.A = static_cast<const uint8_t*>(A);
+    a.sa = sa;
+    a.B = static_cast<const uint8_t*>(B);
+    a.sbe = sb;
+    a.D = static_cast<uint16_t*>(D);
+    a.masked_m = masked_m;
+    a.rows = M_max;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.G = G;
+    a.nkb = (int32_t)(K / 128);
+    a.nnb = (int32_t)((N + 127) / 128);
+    int64_t hint = expected_m > 0 ? std::min(expected_m, M_max) : M_max;
+    return launch(kMasked, a, hint, static_cast<hipStream_t>(stream), true);
 }
 
 const char* fp8gemm_status_string(int status) {

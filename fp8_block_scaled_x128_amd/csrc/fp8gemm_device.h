@@ -73,6 +73,15 @@ __device__ __forceinline__ v4f mfma16x16x128(const v8i& x, const v8i& y) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// E2M1 x E4M3 partial: X = 16 rows of E2M1 codes (16 bytes per lane, the upper half of the
+// operand unused), Y = 16 rows of E4M3 codes, with the E8M0 scale `scale_x` (one byte, 127 = 1)
+// applied to this lane's 32 X elements; the Y operand is unscaled (127).
+__device__ __forceinline__ v4f mfma16x16x128_fp4_fp8(const v8i& x, const v8i& y, int scale_x) {
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    // format codes: 4 = E2M1 for X, 0 = E4M3 for Y
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, zero, 4, 0, 0, scale_x, 0, 127);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even (v_cvt_pk_bf16_f32)
     uint16_t ua, ub;

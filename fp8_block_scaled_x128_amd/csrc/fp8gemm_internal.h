@@ -47,6 +47,7 @@ struct KernelArgs {
     const float* sa;            // [rows_total][nkb]
     const uint8_t* B;           // [G][N][K]
     const float* sb;            // [G][nnb][nkb]
+    const uint8_t* sbe;         // E2M1 B: E8M0 scales [G][N][K/32] (B is then [G][N][K/2])
     uint16_t* D;                // [rows_total][N] bf16 bits
     const int32_t* m_indices;   // contiguous layout: [rows], -1 = padding
     const int32_t* masked_m;    // masked layout: [G]
@@ -73,6 +74,7 @@ struct KernelEntry {
     const char* name;
     int kind;                   // KernelKind
     int layout;
+    bool fp4;                   // B in E2M1 with E8M0 scales per 32 K (masked decode kernel only)
     int bm, bn, waves_m, waves_n, stages;
     int jn, kp;                 // stream kernel: B fragments per wave, K blocks per A phase
     int threads;

@@ -496,6 +496,7 @@ static KernelEntry entry(const char* name) {
     e.name = name;
     e.kind = kKindTiled;
     e.layout = LAYOUT;
+    e.fp4 = false;
     e.bm = BM;
     e.bn = BN;
     e.waves_m = WMW;

@@ -65,9 +65,11 @@ struct Stream {
     static_assert(PF >= 2, "at least one K block in flight");
 };
 
-template <int MT, int W, int JN, int KP, int PF>
+template <int MT, int W, int JN, int KP, int PF, bool FP4>
 __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const KernelArgs args) {
     using T = Stream<MT, W, JN, KP, PF>;
+    // bytes of one 128-wide K block of a B row: E4M3 codes, or E2M1 codes two to a byte
+    constexpr int KBB = FP4 ? 64 : 128;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
     __shared__ int s_flag;
 
@@ -116,30 +118,51 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
 
         const uint8_t* Ag = args.A + arow0 * K;
         const float* sag = args.sa + (int64_t)g * nkb * args.rows + m0;   // sa is [group][K/128][rows]
-        const float* sbg = args.sb + (int64_t)g * nnb * nkb;
+        const float* sbg = FP4 ? nullptr : args.sb + (int64_t)g * nnb * nkb;
         const int nb_first = n0 >> 7;
         const int nb_count = min(nnb, (n0 + T::BN + 127) >> 7) - nb_first;
         // this wave's scale block of B, relative to the tile's first
         const int nbi_w = min(((n0 + wave * JN * 16) >> 7) - nb_first, nb_count - 1);
 
         // ---- B: per-lane offsets of the JN fragments (rows past N read row N-1) -------------
-        const uint8_t* Bt = uniform_ptr(args.B + ((int64_t)g * N + n0) * K);
+        // E4M3: lane q takes bytes [16q, +16) and [64+16q, +16) of its row's K block.
+        // E2M1: lane q takes bytes [16q, +16) -- elements 32q .. 32q+31, one 32-element scale
+        // block, whose E8M0 scale (byte q of the row's 4 scale bytes of the block) the MFMA applies;
+        // with the A lanes' chunks q and 4+q this pairs equal K (mapped on gfx950: the E2M1
+        // operand's nibbles 0-15 of lane group q meet E4M3 lane group 2(q%2) bytes 16(q/2)..+15,
+        // nibbles 16-31 lane group 2(q%2)+1).
+        const int64_t brow = FP4 ? K / 2 : K;
+        const uint8_t* Bt = uniform_ptr(args.B + ((int64_t)g * N + n0) * brow);
         const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(Bt), 0, 0x7FFFFFFF, kBufferFlags);
         uint32_t b_off[JN];
+        uint32_t s_off[JN];
 #pragma unroll
         for (int f = 0; f < JN; ++f) {
             const int r = min(wave * JN * 16 + 16 * f + r16, N - 1 - n0);
-            b_off[f] = (uint32_t)r * (uint32_t)K + (uint32_t)(16 * q) + (uint32_t)kb0 * 128u;
+            b_off[f] = (uint32_t)r * (uint32_t)brow + (uint32_t)(16 * q) + (uint32_t)kb0 * KBB;
+            s_off[f] = (uint32_t)r * (uint32_t)(nkb * 4) + (uint32_t)kb0 * 4u;
         }
+        __amdgpu_buffer_rsrc_t s_rsrc = b_rsrc;
+        if constexpr (FP4)
+            s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t*>(uniform_ptr(args.sbe + ((int64_t)g * N + n0) * nkb * 4)), 0, 0x7FFFFFFF,
+                kBufferFlags);
         v8i ring[PF][JN];
-        auto issue_b = [&](int kb, v8i (&dst)[JN]) {
+        uint32_t sring[PF][JN];      // E2M1: the 4 E8M0 scale bytes of the row's K block
+        auto issue_b = [&](int kb, v8i (&dst)[JN], uint32_t (&sdst)[JN]) {
 #pragma unroll
             for (int f = 0; f < JN; ++f) {
-                const uint32_t o = b_off[f] + (uint32_t)kb * 128u;
+                const uint32_t o = b_off[f] + (uint32_t)kb * KBB;
                 const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, (int)o, 0, 0));
-                const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, (int)(o + 64), 0, 0));
-                dst[f] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                if constexpr (FP4) {
+                    dst[f] = (v8i){lo.x, lo.y, lo.z, lo.w, 0, 0, 0, 0};
+                    sdst[f] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, (int)(s_off[f] + (uint32_t)kb * 4u), 0, 0);
+                } else {
+                    const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, (int)(o + 64), 0, 0));
+                    dst[f] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                    sdst[f] = 0;
+                }
             }
         };
 
@@ -170,7 +193,7 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
                 const int r = min(sid % MT, rows_needed - 1);
                 sa_reg[i] = sag[(int64_t)(kb0 + kb) * args.rows + r];
             }
-            {
+            if constexpr (!FP4) {
                 const int x = min(tid, T::NBW * KP - 1);
                 const int nbi = min(x / KP, nb_count - 1);
                 const int kb = min(kbp + x % KP, nks - 1);
@@ -197,7 +220,7 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
                 if (t < tp && r < rows_needed)
                     reinterpret_cast<float*>(dst + T::SA_OFF)[t * MT + r] = sa_reg[i];
             }
-            if (tid < T::NBW * KP) reinterpret_cast<float*>(dst + T::SB_OFF)[tid] = sb_reg;
+            if (!FP4 && tid < T::NBW * KP) reinterpret_cast<float*>(dst + T::SB_OFF)[tid] = sb_reg;
         };
 
         // ---- accumulators -------------------------------------------------------------------
@@ -208,12 +231,13 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
             for (int j = 0; j < T::MSUB; ++j) acc[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
         // one K block: MFMA partials of the active sub-tiles, promoted into acc
-        auto compute = [&](int kb, const v8i (&bf)[JN]) {
+        auto compute = [&](int kb, const v8i (&bf)[JN], const uint32_t (&sw)[JN]) {
             const int t = kb % KP;
             const uint8_t* ph = smem + ((kb / KP) & 1) * T::PHASE_BYTES;
             const uint8_t* ab = ph + t * MT * 128;
             const float* sal = reinterpret_cast<const float*>(ph + T::SA_OFF) + t * MT;
-            const float sbv = reinterpret_cast<const float*>(ph + T::SB_OFF)[nbi_w * KP + t];
+            // E4M3 B: the 128x128 block scale, applied with sa; E2M1 B: scales inside the MFMA
+            const float sbv = FP4 ? 1.0f : reinterpret_cast<const float*>(ph + T::SB_OFF)[nbi_w * KP + t];
 #pragma unroll
             for (int j = 0; j < T::MSUB; ++j) {
                 if (j < nsub) {
@@ -224,7 +248,9 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
                     const float s = sal[16 * j + r16] * sbv;
 #pragma unroll
                     for (int f = 0; f < JN; ++f) {
-                        const v4f p = mfma16x16x128(bf[f], af);
+                        v4f p;
+                        if constexpr (FP4) p = mfma16x16x128_fp4_fp8(bf[f], af, (int)((sw[f] >> (8 * q)) & 0xFFu));
+                        else p = mfma16x16x128(bf[f], af);
                         acc[f][j] += p * s;
                     }
                 }
@@ -237,7 +263,7 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
         load_a(0);
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int u2 = 0; u2 < PF - 1; ++u2) issue_b(min(u2, nks - 1), ring[u2]);
+        for (int u2 = 0; u2 < PF - 1; ++u2) issue_b(min(u2, nks - 1), ring[u2], sring[u2]);
         for (int base = 0; base < nks; base += T::U) {
             // U = lcm(KP, PF) K blocks: every trip starts a phase and a ring cycle
 #pragma unroll
@@ -250,8 +276,8 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
                     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
                     load_a(kb / KP + 1);
                 }
-                issue_b(min(kb + PF - 1, nks - 1), ring[(u2 + PF - 1) % PF]);
-                if (kb < nks) compute(kb, ring[u2 % PF]);
+                issue_b(min(kb + PF - 1, nks - 1), ring[(u2 + PF - 1) % PF], sring[(u2 + PF - 1) % PF]);
+                if (kb < nks) compute(kb, ring[u2 % PF], sring[u2 % PF]);
             }
         }
 
@@ -351,18 +377,19 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
 // instantiation table
 // ------------------------------------------------------------------------------------------
 
-template <int MT, int W, int JN, int KP, int PF>
+template <int MT, int W, int JN, int KP, int PF, bool FP4>
 static void launch_stream(dim3 grid, const KernelArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((fp8gemm_masked_decode_kernel<MT, W, JN, KP, PF>), grid, dim3(W * 64), 0, s, a);
+    hipLaunchKernelGGL((fp8gemm_masked_decode_kernel<MT, W, JN, KP, PF, FP4>), grid, dim3(W * 64), 0, s, a);
 }
 
-template <int MT, int W, int JN, int KP, int PF>
+template <int MT, int W, int JN, int KP, int PF, bool FP4>
 static KernelEntry stream_entry(const char* name) {
     using T = Stream<MT, W, JN, KP, PF>;
     KernelEntry e;
     e.name = name;
     e.kind = kKindStream;
     e.layout = kMasked;
+    e.fp4 = FP4;
     e.bm = MT;
     e.bn = T::BN;
     e.waves_m = 1;
@@ -373,13 +400,15 @@ static KernelEntry stream_entry(const char* name) {
     e.threads = T::NT;
     e.splitk = true;
     e.lds_bytes = T::LDS_BYTES;
-    e.func = reinterpret_cast<const void*>(&fp8gemm_masked_decode_kernel<MT, W, JN, KP, PF>);
-    e.launch = &launch_stream<MT, W, JN, KP, PF>;
+    e.func = reinterpret_cast<const void*>(&fp8gemm_masked_decode_kernel<MT, W, JN, KP, PF, FP4>);
+    e.launch = &launch_stream<MT, W, JN, KP, PF, FP4>;
     return e;
 }
 
 #define STREAM_ENTRY(MT, W, JN, KP, PF) \
-    stream_entry<MT, W, JN, KP, PF>("masked decode " #MT " rows, " #W " waves x " #JN " fragments, phase " #KP ", depth " #PF)
+    stream_entry<MT, W, JN, KP, PF, false>("masked decode " #MT " rows, " #W " waves x " #JN " fragments, phase " #KP ", depth " #PF)
+#define STREAM_ENTRY_FP4(MT, W, JN, KP, PF) \
+    stream_entry<MT, W, JN, KP, PF, true>("masked decode FP8xFP4 " #MT " rows, " #W " waves x " #JN " fragments, phase " #KP ", depth " #PF)
 
 // Masked groups of at most 128 valid rows (one tile per group and N tile, B streamed once per
 // group).  Measured on 16 groups x 256 rows (about 64 valid each), graphs of 3 launches:
@@ -392,6 +421,10 @@ const KernelEntry* stream_table(int* count) {
         STREAM_ENTRY(128, 4, 2, 2, 4),
         STREAM_ENTRY(128, 4, 1, 2, 4),
         STREAM_ENTRY(128, 8, 1, 4, 4),
+        // E4M3 x E2M1 (B with one E8M0 scale per 32 K): half the B bytes per K block
+        STREAM_ENTRY_FP4(128, 4, 2, 2, 4),
+        STREAM_ENTRY_FP4(128, 4, 4, 2, 4),
+        STREAM_ENTRY_FP4(128, 4, 1, 2, 4),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

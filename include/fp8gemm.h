@@ -93,6 +93,26 @@ int fp8gemm_grouped_masked(const void* A, const float* sa, const void* B, const 
                            const int32_t* masked_m, void* D, int32_t G, int64_t M_max, int64_t N,
                            int64_t K, int64_t expected_m, void* stream);
 
+/* M-grouped GEMM, masked layout, with B in 4-bit floating point: the FP8 x FP4 mixed precision of
+ * page "Perpustakaan operator GPU sumber terbuka DeepSeek DeepGEMM memperbarui versi besar,
+ * menambahkan Mega MoE…" (Mega MoE supports only the FP8 x FP4 combination; FP8 x FP4 matrix
+ * multiplication is listed among the additions).  The pages give no FP4 element or scale format;
+ * the reading taken is OCP MXFP4 for B and the FP8 left operand of fp8gemm_grouped_masked:
+ *   A [G][M_max][K] e4m3 codes, sa [G][K/128][M_max] fp32 (as fp8gemm_grouped_masked),
+ *   B [G][N][K/2] bytes: E2M1 codes (1 sign, 2 exponent bits with bias 1, 1 mantissa bit:
+ *     0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives), two per byte, element k of a row in byte
+ *     k/2, the even element in the low nibble,
+ *   sb [G][N][K/32] uint8: E8M0 scales (value 2^(s - 127); 255 is NaN and gives unspecified
+ *     results), one per 32 consecutive K values of a row of B,
+ *   D[g][m][n] = bf16( sum_kb sa[g][kb][m] * sum_{k in block kb} e4m3(A) * e2m1(B) * 2^(sb - 127) ),
+ *   masked_m, expected_m and D as fp8gemm_grouped_masked.  K: a positive multiple of 128; B, A
+ *   and D 16-byte aligned, sa, sb and masked_m 4-byte aligned.  The 32-value scales are applied
+ *   inside the matrix-core instruction; the fresh fp32 partial of each 128-wide K block is then
+ *   scaled by sa and accumulated in fp32 (the two-level accumulation). */
+int fp8gemm_fp8fp4_grouped_masked(const void* A, const float* sa, const void* B, const uint8_t* sb,
+                                  const int32_t* masked_m, void* D, int32_t G, int64_t M_max, int64_t N,
+                                  int64_t K, int64_t expected_m, void* stream);
+
 /* Activation quantiser, 1x128 blocks: the step that produces the left operand and its scales.
  * The pages take fine-grained scaling from DeepSeek V3 (page "DeepSeek開源第三彈…", section
  * 深入了解DeepGEMM) and give no quantiser; this one is the plain reading of a 1x128 block scale.

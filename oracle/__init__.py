@@ -46,6 +46,13 @@ def _load():
         lib.oracle_quantize_1x128.restype = ctypes.c_int
         lib.oracle_quantize_1x128.argtypes = [P, I64, I64, P, P, ctypes.c_int]
         lib.oracle_swiglu_quantize_1x128.argtypes = [P, I64, I64, P, P, P, ctypes.c_int]
+        lib.oracle_e2m1_value.restype = ctypes.c_double
+        lib.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e8m0_value.restype = ctypes.c_double
+        lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_grouped_masked_fp4.restype = ctypes.c_int
+        lib.oracle_grouped_masked_fp4.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, I64,
+                                                  P, P, P, ctypes.c_int]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = [ctypes.c_int]
         lib.oracle_gemm_nt.restype = ctypes.c_int
@@ -195,3 +202,31 @@ def swiglu_quantize_1x128(X_bits, nthreads: int = 0):
     h = np.empty((M, I), dtype=np.float64)
     _load().oracle_swiglu_quantize_1x128(_ptr(X), M, I, _ptr(codes), _ptr(sa), _ptr(h), nthreads)
     return codes, sa, h
+
+
+def e2m1_value(code: int) -> float:
+    return _load().oracle_e2m1_value(int(code))
+
+
+def e8m0_value(s: int) -> float:
+    return _load().oracle_e8m0_value(int(s))
+
+
+def grouped_masked_fp4(A, sa, B, sb, masked_m, with_acc: bool = False, nthreads: int = 0):
+    """Masked layout with an E2M1 right operand: A uint8 [G,M_max,K] (E4M3), sa float32
+    [G,M_max,K/128], B uint8 [G,N,K/2] (two E2M1 codes per byte, even element low), sb uint8
+    [G,N,K/32] (E8M0), masked_m int32 [G] -> (D bf16 bits [G,M_max,N], valid [G,M_max])."""
+    A, sa, B = _c(A, np.uint8), _c(sa, np.float32), _c(B, np.uint8)
+    sb, mm = _c(sb, np.uint8), _c(masked_m, np.int32)
+    G, M_max, K = A.shape
+    N = B.shape[1]
+    assert B.shape == (G, N, K // 2) and sb.shape == (G, N, K // 32) and K % 32 == 0
+    assert sa.shape == (G, M_max, -(-K // 128)) and mm.shape == (G,)
+    D = np.empty((G, M_max, N), dtype=np.uint16)
+    valid = np.empty((G, M_max), dtype=np.uint8)
+    acc = np.empty((G, M_max, N), dtype=np.float64) if with_acc else None
+    rc = _load().oracle_grouped_masked_fp4(_ptr(A), _ptr(sa), _ptr(B), _ptr(sb), _ptr(mm), G, M_max, N, K,
+                                           _ptr(D), _ptr(valid), _ptr(acc), nthreads)
+    if rc:
+        raise MemoryError("oracle_grouped_masked_fp4")
+    return (D, valid, acc) if with_acc else (D, valid)

@@ -257,6 +257,82 @@ ORACLE_API int oracle_grouped_masked(const uint8_t* A, const float* sa, const ui
     return 0;
 }
 
+/* ---- M-grouped, masked layout, B in E2M1 with E8M0 scales per 32 K ------------------------ */
+
+/* OCP MX 4-bit float E2M1: 1 sign, 2 exponent bits (bias 1), 1 mantissa bit.  Exponent field 0
+ * is subnormal: m * 2^-1.  There is no infinity or NaN; the values are 0, 0.5, 1, 1.5, 2, 3, 4, 6
+ * and their negatives. */
+ORACLE_API double oracle_e2m1_value(uint8_t code) {
+    int sign = (code >> 3) & 1;
+    int e = (code >> 1) & 3;
+    int m = code & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -v : v;
+}
+
+/* OCP MX scale E8M0: an unsigned 8-bit exponent, value 2^(s - 127); 0xFF is NaN. */
+ORACLE_API double oracle_e8m0_value(uint8_t s) { return s == 0xFF ? NAN : ldexp(1.0, (int)s - 127); }
+
+/* The masked grouped product with an FP4 right operand (page "Perpustakaan operator GPU sumber
+ * terbuka DeepSeek DeepGEMM memperbarui versi besar, menambahkan Mega MoE…": FP8 x FP4 matrix
+ * multiplication, the precision combination of Mega MoE; the pages give no FP4 format, the
+ * reading taken is OCP MXFP4).  B[g][n] holds K E2M1 codes, two per byte (element k in byte k/2,
+ * the even element in the low nibble): B is [G][N][K/2] bytes.  sb[g][n][k/32] is the E8M0 scale
+ * of the 32 consecutive values k/32*32 .. +31 of that row.  A, sa (row-major [G*M_max][K/128]),
+ * masked_m, D, valid and acc as oracle_grouped_masked.  Per valid output:
+ *   D = bf16_rne( sum_kb sa[kb] * sum_{k in block kb} e4m3(A[k]) * e2m1(B[k]) * 2^(sb[k/32] - 127) )
+ * Each 32-value sum is exact in fp64 (products are multiples of 2^-10 below 2^12); scaling by a
+ * power of two is exact; the four scaled sums of a 128-value block are added in fp64, then the
+ * blocks are accumulated as in the FP8 product.  K must be a multiple of 32. */
+ORACLE_API int oracle_grouped_masked_fp4(const uint8_t* A, const float* sa, const uint8_t* B,
+                                         const uint8_t* sb, const int32_t* masked_m, int32_t G,
+                                         int64_t M_max, int64_t N, int64_t K, uint16_t* D,
+                                         uint8_t* valid, double* acc, int nthreads) {
+    int64_t nkb = (K + 127) / 128, nsb = K / 32;
+    int64_t rows = (int64_t)G * M_max;
+    double* Ad = (double*)malloc(sizeof(double) * (size_t)(rows * K + 1));
+    double* Bd = (double*)malloc(sizeof(double) * (size_t)((int64_t)G * N * K + 1));
+    if (!Ad || !Bd) { free(Ad); free(Bd); return -1; }
+    decode_rows(A, rows, K, Ad);
+    double e2m1[16];
+    for (int c = 0; c < 16; ++c) e2m1[c] = oracle_e2m1_value((uint8_t)c);
+    for (int64_t i = 0; i < (int64_t)G * N * K; ++i) {
+        uint8_t byte = B[i / 2];
+        Bd[i] = e2m1[(i & 1) ? (byte >> 4) : (byte & 0xF)];
+    }
+    int nt = pick_threads(nthreads);
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t gr = 0; gr < rows; ++gr) {
+        int64_t g = gr / (M_max > 0 ? M_max : 1), r = gr % (M_max > 0 ? M_max : 1);
+        int64_t count = masked_m[g] < 0 ? 0 : (masked_m[g] > M_max ? M_max : masked_m[g]);
+        int ok = r < count;
+        if (valid) valid[gr] = (uint8_t)ok;
+        for (int64_t n = 0; n < N; ++n) {
+            double v = 0.0;
+            if (ok) {
+                const double* a = Ad + gr * K;
+                const double* b = Bd + (g * N + n) * K;
+                const uint8_t* srow = sb + (g * N + n) * nsb;
+                for (int64_t kb = 0; kb < nkb; ++kb) {
+                    double block = 0.0;
+                    for (int64_t k0 = kb * 128; k0 < kb * 128 + 128 && k0 < K; k0 += 32) {
+                        double sub = 0.0;
+                        for (int64_t k = k0; k < k0 + 32; ++k) sub += a[k] * b[k];
+                        block += oracle_e8m0_value(srow[k0 / 32]) * sub;
+                    }
+                    v = fma((double)sa[gr * nkb + kb], block, v);
+                }
+            }
+            D[gr * N + n] = ok ? oracle_bf16_bits(v) : 0;
+            if (acc) acc[gr * N + n] = v;
+        }
+    }
+    free(Ad);
+    free(Bd);
+    return 0;
+}
+
 /* ---- selected elements ------------------------------------------------------------------- */
 
 /* The same element computation for `count` chosen outputs, for full-size problems where the

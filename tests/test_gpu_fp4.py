@@ -1,0 +1,216 @@
+"""GPU parity of the masked grouped GEMM with an FP4 right operand (E2M1 elements, one E8M0 scale
+per 32 values of K), through the C ABI, against the CPU oracle.
+
+The matrix-core instruction applies the E8M0 scales and sums each 128-wide K block; its internal
+sum keeps about 12 bits below the block's largest product (the same as for E4M3 x E4M3), so the
+general cases use the GEMM tolerance |gpu - ref| <= 2^-7 |ref| + 1e-3 rms(ref).  Integer A codes
+with small B values and power-of-two scales keep every partial sum exact, and those outputs must
+match bit for bit."""
+import os
+import re
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from parity import assert_close, gpu_bits
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU runs deselect these with -m "not gpu"
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import fp8_block_scaled_x128_amd as fg  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SENTINEL = 0x7FC1   # a NaN pattern the library never writes
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def sentinel_tensor(shape):
+    return torch.full(shape, SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+
+def fp4_table():
+    """Configurations of the FP8 x FP4 decode kernel: (rows, waves, fragments, phase, depth)."""
+    src = open(os.path.join(ROOT, "fp8_block_scaled_x128_amd", "csrc", "stream_kernels.hip")).read()
+    return [tuple(int(x) for x in t) for t in
+            re.findall(r"STREAM_ENTRY_FP4\((\d+), (\d+), (\d+), (\d+), (\d+)\)", src)]
+
+
+class forced_stream:
+    def __init__(self, mt, w, jn, kp, pf, split):
+        self.v = "stream:%d:%d:%d:%d:%d:%d" % (mt, w, jn, kp, pf, split)
+
+    def __enter__(self):
+        os.environ["FP8GEMM_FORCE_CONFIG"] = self.v
+
+    def __exit__(self, *exc):
+        os.environ.pop("FP8GEMM_FORCE_CONFIG", None)
+
+
+def run(w, expected_m, out=None):
+    D = fg.fp8fp4_grouped_masked(dev(w.A), dev(np.swapaxes(w.sa, -1, -2)), dev(w.B), dev(w.sb),
+                                 dev(w.masked_m), expected_m, out=out)
+    torch.cuda.synchronize()
+    return D
+
+
+def valid_mask(w, N):
+    M_max = w.A.shape[1]
+    v = np.arange(M_max)[None, :] < np.clip(w.masked_m, 0, M_max)[:, None]
+    return np.broadcast_to(v[:, :, None], (len(w.masked_m), M_max, N))
+
+
+def integer_case(rng, mm, M_max, N, K):
+    """A: integer E4M3 codes in [-4, 4]; B: random E2M1 codes; scales powers of two near 1."""
+    G = len(mm)
+    vals = rng.integers(-4, 5, size=(G, M_max, K)).astype(np.float32)
+    A = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    B = rng.integers(0, 256, size=(G, N, K // 2), dtype=np.uint8)
+    sa = (2.0 ** rng.integers(-1, 2, size=(G, M_max, K // 128))).astype(np.float32)
+    sb = rng.integers(126, 129, size=(G, N, K // 32)).astype(np.uint8)
+    return W.MaskedFp4(A, sa, B, sb, np.asarray(mm, np.int32), 64)
+
+
+@pytest.mark.parametrize("mm,M_max,N,K", [([0, 1, 64, 200, 130], 200, 192, 384),
+                                          ([64, 64], 64, 4096, 256), ([3], 256, 100, 128),
+                                          ([37, 90, 5], 128, 640, 1152)])
+def test_fp4_parity_rows_past_count_untouched(mm, M_max, N, K):
+    w = W.masked_fp4(np.array(mm, np.int32), M_max, N, K, seed=sum(mm) + N + 5)
+    ref, _ = oracle.grouped_masked_fp4(w.A, w.sa, w.B, w.sb, w.masked_m)
+    v = valid_mask(w, N)
+    for em in (1, 64, M_max):
+        D = run(w, em, out=sentinel_tensor((len(mm), M_max, N)))
+        got = gpu_bits(D)
+        assert_close(got, ref, mask=v, what="fp4 em=%d %s" % (em, fg.last_config()))
+        assert np.all(got[~v] == SENTINEL), "rows past the count were written"
+    assert fg.read_device_error() == 0
+    say("fp4", mm, N, K, fg.last_config())
+
+
+@pytest.mark.parametrize("entry", fp4_table(), ids=lambda e: "mt%d_w%d_jn%d_kp%d_pf%d" % e)
+@pytest.mark.parametrize("split", [1, 3])
+def test_every_fp4_config(entry, split):
+    """Each FP4 kernel configuration: counts past one tile, zero, ragged sub-tiles and a full
+    group; N off the tile grid; K = 6 blocks (a short last phase); random MXFP4 weights within
+    tolerance, then integer inputs bit-exact on one CU (several units per workgroup)."""
+    mt, wv, jn, kp, pf = entry
+    bn = 16 * jn * wv
+    M_max, N, K = 2 * mt, 2 * bn + 24, 768
+    w = W.masked_fp4(np.array([mt + 3, 0, 17, M_max], np.int32), M_max, N, K, seed=mt + bn + split)
+    ref, _ = oracle.grouped_masked_fp4(w.A, w.sa, w.B, w.sb, w.masked_m)
+    with forced_stream(mt, wv, jn, kp, pf, split):
+        D = run(w, 64, out=sentinel_tensor((4, M_max, N)))
+        cfg = fg.last_config()
+    assert "stream tile=%dx%d" % (mt, bn) in cfg, cfg
+    got = gpu_bits(D)
+    v = valid_mask(w, N)
+    assert_close(got, ref, mask=v, what=cfg)
+    assert np.all(got[~v] == SENTINEL)
+
+    wi = integer_case(np.random.default_rng(bn + split), [mt - 5, 1, mt + 17, 0], M_max, N, K)
+    ref2, _ = oracle.grouped_masked_fp4(wi.A, wi.sa, wi.B, wi.sb, wi.masked_m)
+    v2 = valid_mask(wi, N)
+    fg.set_num_cus(1)
+    try:
+        with forced_stream(mt, wv, jn, kp, pf, split):
+            D2 = run(wi, 64, out=sentinel_tensor((4, M_max, N)))
+            cfg2 = fg.last_config()
+    finally:
+        fg.set_num_cus(0)
+    got2 = gpu_bits(D2)
+    assert np.array_equal(got2[v2], ref2[v2]), "%s: %d outputs differ" % (cfg2, int((got2[v2] != ref2[v2]).sum()))
+    assert np.all(got2[~v2] == SENTINEL)
+    units, grid = (int(x) for x in re.search(r"units=(\d+) grid=(\d+)", cfg2).groups())
+    assert units > grid, cfg2
+    say("fp4 config", cfg, cfg2)
+
+
+def test_fp4_scales_over_the_whole_e8m0_range_that_stays_finite():
+    """Scales far from 1 in both directions (products down to 2^-40 and up to 2^+40): the scale
+    is applied exactly inside the instruction, so results stay within tolerance."""
+    rng = np.random.default_rng(5)
+    G, M_max, N, K = 2, 32, 160, 512
+    w = W.masked_fp4(np.array([32, 20], np.int32), M_max, N, K, seed=77)
+    sb = rng.integers(127 - 40, 127 + 41, size=(G, N, K // 32)).astype(np.uint8)
+    w = W.MaskedFp4(w.A, w.sa, w.B, sb, w.masked_m, 32)
+    ref, _ = oracle.grouped_masked_fp4(w.A, w.sa, w.B, w.sb, w.masked_m)
+    got = gpu_bits(run(w, 32, out=sentinel_tensor((G, M_max, N))))
+    v = valid_mask(w, N)
+    for g in range(G):
+        assert_close(got[g], ref[g], mask=v[g], what="wide scales group %d" % g)
+
+
+def test_fp4_count_out_of_range_clamps_and_flags():
+    w = W.masked_fp4(np.array([64, 10], np.int32), 64, 128, 256, seed=93)
+    bad = W.MaskedFp4(w.A, w.sa, w.B, w.sb, np.array([1000, -5], np.int32), 64)
+    fg.read_device_error()                     # clear
+    D = run(bad, 64, out=sentinel_tensor((2, 64, 128)))
+    assert fg.read_device_error() & fg.DEVERR_BAD_COUNT
+    ref, _ = oracle.grouped_masked_fp4(bad.A, bad.sa, bad.B, bad.sb, bad.masked_m)
+    got = gpu_bits(D)
+    assert np.all(got[1] == SENTINEL)
+    assert_close(got[0], ref[0], what="clamped count")
+
+
+def test_fp4_argument_errors():
+    w = W.masked_fp4(np.array([4], np.int32), 16, 64, 256, seed=3)
+    A, sa = dev(w.A), dev(np.swapaxes(w.sa, -1, -2))
+    B, sb, mm = dev(w.B), dev(w.sb), dev(w.masked_m)
+    lib = fg.lib()
+    code = {v: k for k, v in fg.STATUS.items()}
+    D = torch.empty((1, 16, 64), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    args = [A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(), mm.data_ptr(), D.data_ptr()]
+    assert lib.fp8gemm_fp8fp4_grouped_masked(*args, 1, 16, 64, 200, 0, s) == code["FP8GEMM_ERR_BAD_SHAPE"]
+    assert lib.fp8gemm_fp8fp4_grouped_masked(*args, 0, 16, 64, 256, 0, s) == code["FP8GEMM_ERR_BAD_SHAPE"]
+    nul = list(args)
+    nul[3] = None
+    assert lib.fp8gemm_fp8fp4_grouped_masked(*nul, 1, 16, 64, 256, 0, s) == code["FP8GEMM_ERR_NULL_PTR"]
+    mis = list(args)
+    mis[3] = sb.data_ptr() + 1
+    assert lib.fp8gemm_fp8fp4_grouped_masked(*mis, 1, 16, 64, 256, 0, s) == code["FP8GEMM_ERR_MISALIGNED"]
+    assert lib.fp8gemm_fp8fp4_grouped_masked(*args, 1, 0, 64, 256, 0, s) == code["FP8GEMM_OK"]
+    with pytest.raises(TypeError):
+        fg.fp8fp4_grouped_masked(A, sa, B.view(torch.int8), sb, mm, 4)
+    with pytest.raises(ValueError):
+        fg.fp8fp4_grouped_masked(A, sa, B[:, :, :64], sb, mm, 4)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.slow
+def test_fp4_config4_full_size_sampled():
+    """The masked decode workload (16 groups x 256 rows, Poisson(64) counts, N=4096, K=7168) with
+    MXFP4 weights, at full size in the launch shape the benchmark times.  Each output depends only
+    on its row of A and its row of B, so the oracle runs on 3 groups' sampled rows and columns."""
+    say("fp4 config 4")
+    w = W.config4_fp4()
+    G, M_max, K = w.A.shape
+    N = w.B.shape[1]
+    D = run(w, w.expected_m, out=sentinel_tensor((G, M_max, N)))
+    got = gpu_bits(D)
+    v = valid_mask(w, N)
+    assert np.all(got[~v] == SENTINEL)
+    assert fg.read_device_error() == 0
+    rng = np.random.default_rng(4)
+    for g in rng.choice(G, 3, replace=False):
+        c = int(w.masked_m[g])
+        rows = np.unique(np.concatenate([[0, c - 1], rng.integers(0, c, 30)]))
+        cols = np.unique(np.concatenate([np.arange(64), np.arange(N - 64, N), rng.integers(0, N, 128)]))
+        sub = W.MaskedFp4(w.A[g:g + 1, rows], w.sa[g:g + 1, rows], w.B[g:g + 1, cols], w.sb[g:g + 1, cols],
+                          np.array([rows.size], np.int32), 0)
+        ref, _ = oracle.grouped_masked_fp4(sub.A, sub.sa, sub.B, sub.sb, sub.masked_m)
+        rep = assert_close(got[g][np.ix_(rows, cols)], ref[0], what="config 4 fp4 group %d" % g)
+        say("fp4 config 4 group", g, fg.last_config(), rep["bit_equal"])

@@ -33,6 +33,13 @@ MUTANTS = {
                                 "double silu = 1.0 / (1.0 + exp(-(double)g));"),
     "swiglu_sign_of_exponent": ("double silu = (double)g / (1.0 + exp(-(double)g));",
                                 "double silu = (double)g / (1.0 + exp((double)g));"),
+    "fp4_nibble_order_swapped": ("Bd[i] = e2m1[(i & 1) ? (byte >> 4) : (byte & 0xF)];",
+                                 "Bd[i] = e2m1[(i & 1) ? (byte & 0xF) : (byte >> 4)];"),
+    "fp4_scale_per_64_values": ("block += oracle_e8m0_value(srow[k0 / 32]) * sub;",
+                                "block += oracle_e8m0_value(srow[k0 / 64]) * sub;"),
+    "e2m1_subnormal_quantum": ("double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);",
+                               "double v = (e == 0) ? 0.25 * m : ldexp(1.0 + 0.5 * m, e - 1);"),
+    "e8m0_bias": ("ldexp(1.0, (int)s - 127)", "ldexp(1.0, (int)s - 128)"),
     "swiglu_activation_perturbed": ("xs[k - k0] = (float)v;", "xs[k - k0] = (float)v * 1.0000001f;"),
 }
 

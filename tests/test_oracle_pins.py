@@ -587,3 +587,87 @@ def test_swiglu_quantiser_invariants():
     flipped[:, I:] ^= np.uint16(0x8000)
     c2, s2, _ = oracle.swiglu_quantize_1x128(flipped)
     assert np.array_equal(c2, codes ^ np.uint8(0x80)) and np.array_equal(s2, sa)
+
+
+# ------------------------------------------------------------------------------------------
+# FP8 x FP4 (E2M1 elements, E8M0 scales per 32 values)
+# ------------------------------------------------------------------------------------------
+
+def test_e2m1_and_e8m0_values(golden_dir):
+    """Every E2M1 code and E8M0 anchors against the published OCP MX definition."""
+    n = 0
+    for line in _read_golden(os.path.join(golden_dir, "e2m1_e8m0_values.txt")):
+        kind, code, val = line.split()
+        c = int(code, 16)
+        if kind == "e2m1":
+            got = oracle.e2m1_value(c)
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), (code, got)
+        else:
+            assert oracle.e8m0_value(c) == 2.0 ** int(val), (code, oracle.e8m0_value(c))
+        n += 1
+    assert n == 21
+    assert math.isnan(oracle.e8m0_value(0xFF))
+
+
+def _fp4_operands(seed, G=3, M_max=9, N=40, K=384, lo=123, hi=131):
+    rng = np.random.default_rng(seed)
+    A = W.random_codes(rng, (G, M_max, K))
+    sa = np.exp(rng.standard_normal((G, M_max, K // 128))).astype(np.float32)
+    B = rng.integers(0, 256, size=(G, N, K // 2), dtype=np.uint8)
+    sb = rng.integers(lo, hi + 1, size=(G, N, K // 32)).astype(np.uint8)
+    return A, sa, B, sb
+
+
+def _fp4_values(B, sb):
+    """Exact values e2m1(B) * 2^(sb - 127) as float32 [G, N, K] (independent of the oracle)."""
+    table = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6], np.float32)
+    codes = np.stack([B & 15, B >> 4], axis=-1).reshape(B.shape[0], B.shape[1], -1)
+    scale = np.ldexp(np.float32(1), sb.astype(np.int32) - 127).astype(np.float32)
+    return table[codes] * np.repeat(scale, 32, axis=-1)
+
+
+def test_fp4_product_equals_fp8_product_of_the_same_values():
+    """With E8M0 scales in [2^-4, 2^4] every scaled E2M1 value is an E4M3 value, so the FP4 product
+    must equal the (pinned) FP8 product of those values with unit 128x128 scales, bit for bit."""
+    A, sa, B, sb = _fp4_operands(71)
+    G, M_max, K = A.shape
+    N = B.shape[1]
+    vals = _fp4_values(B, sb)
+    B8 = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(_DEC[B8], vals)                         # exact in E4M3
+    mm = np.array([9, 0, 4], np.int32)
+    d4, v4 = oracle.grouped_masked_fp4(A, sa, B, sb, mm)
+    d8, v8 = oracle.grouped_masked(A, sa, B8, np.ones((G, -(-N // 128), K // 128), np.float32), mm)
+    assert np.array_equal(v4, v8)
+    assert np.array_equal(d4[v4.astype(bool)], d8[v8.astype(bool)])
+
+
+def test_fp4_brute_force_exact_rationals():
+    """Tiny shapes with scales over a wide range: the exact rational sum, rounded once to bf16."""
+    A, sa, B, sb = _fp4_operands(72, G=2, M_max=3, N=5, K=256, lo=100, hi=160)
+    G, M_max, K = A.shape
+    N = B.shape[1]
+    vals = _fp4_values(B, sb).astype(np.float64)
+    mm = np.array([3, 2], np.int32)
+    d4, valid = oracle.grouped_masked_fp4(A, sa, B, sb, mm)
+    for g in range(G):
+        for m in range(mm[g]):
+            for n in range(N):
+                s = Fraction(0)
+                for k in range(K):
+                    s += Fraction(float(sa[g, m, k // 128])) * frac_of_code(A[g, m, k]) * Fraction(float(vals[g, n, k]))
+                assert d4[g, m, n] == exact_bf16_bits(s), (g, m, n)
+
+
+def test_fp4_rows_past_count_do_not_matter():
+    A, sa, B, sb = _fp4_operands(73)
+    mm = np.array([5, 9, 1], np.int32)
+    d1, v = oracle.grouped_masked_fp4(A, sa, B, sb, mm)
+    rng = np.random.default_rng(3)
+    A2, sa2 = A.copy(), sa.copy()
+    for g, c in enumerate(mm):
+        A2[g, c:] = W.random_codes(rng, A2[g, c:].shape)
+        sa2[g, c:] = 7.0
+    d2, _ = oracle.grouped_masked_fp4(A2, sa2, B, sb, mm)
+    vb = v.astype(bool)
+    assert np.array_equal(d1[vb], d2[vb]) and np.all(d1[~vb] == 0)

@@ -231,6 +231,67 @@ def masked(masked_m, M_max: int, N: int, K: int, seed: int, expected_m: int = 0)
                   expected_m)
 
 
+# --- 4-bit weights: OCP MXFP4 (E2M1 elements, one E8M0 scale per 32 consecutive values) -------
+
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+# Rounding thresholds on |x| / 2^e for E2M1 codes 1..7: the midpoints between neighbouring grid
+# values; at a midpoint the even code (mantissa bit 0) wins, so a threshold that leads to an odd
+# code is passed only strictly (">") and one that leads to an even code inclusively (">=").
+_E2M1_UP = ((0.25, False), (0.75, True), (1.25, False), (1.75, True), (2.5, False), (3.5, True), (5.0, False))
+
+
+def quantize_mxfp4(x: np.ndarray, chunk_rows: int = 1024):
+    """x: float32 [R, K] (K a multiple of 32) -> (packed uint8 [R, K/2], scales uint8 [R, K/32]).
+    Per 32-value block the shared exponent is floor(log2(amax)) - 2 (E2M1's largest exponent is
+    2), so amax / 2^e lies in [4, 8); elements round to the nearest E2M1 value (ties to the even
+    code), saturating at 6.  An all-zero block gets scale 2^0."""
+    R, K = x.shape
+    assert K % 32 == 0
+    packed = np.empty((R, K // 2), dtype=np.uint8)
+    scales = np.empty((R, K // 32), dtype=np.uint8)
+    for r0 in range(0, R, chunk_rows):
+        r1 = min(R, r0 + chunk_rows)
+        xb = x[r0:r1].astype(np.float64).reshape(r1 - r0, K // 32, 32)
+        amax = np.abs(xb).max(axis=2)
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, 0).astype(np.int64)
+        e = np.clip(e, -127, 127)
+        y = np.abs(xb) / np.ldexp(1.0, e)[:, :, None]
+        code = np.zeros(y.shape, dtype=np.uint8)
+        for t, inclusive in _E2M1_UP:
+            code += (y >= t) if inclusive else (y > t)
+        code |= np.where(xb < 0, 8, 0).astype(np.uint8)
+        code = code.reshape(r1 - r0, K)
+        packed[r0:r1] = code[:, 0::2] | (code[:, 1::2] << 4)
+        scales[r0:r1] = (e + 127).astype(np.uint8)
+    return packed, scales
+
+
+@dataclass
+class MaskedFp4:
+    A: np.ndarray          # uint8 [G, M_max, K] E4M3
+    sa: np.ndarray         # float32 [G, M_max, K/128]
+    B: np.ndarray          # uint8 [G, N, K/2] E2M1 pairs
+    sb: np.ndarray         # uint8 [G, N, K/32] E8M0
+    masked_m: np.ndarray   # int32 [G]
+    expected_m: int = 0
+
+
+def masked_fp4(masked_m, M_max: int, N: int, K: int, seed: int, expected_m: int = 0) -> MaskedFp4:
+    """As ``masked`` with the right operand N(0,1) quantised to MXFP4."""
+    first = masked(masked_m, M_max, 128, K, seed, expected_m)      # A, sa and rows past the counts
+    rng = np.random.default_rng(seed + 11)
+    Bs, sbs = zip(*(quantize_mxfp4(normal(rng, (N, K))) for _ in range(len(masked_m))))
+    return MaskedFp4(first.A, first.sa, np.stack(Bs), np.stack(sbs), first.masked_m, expected_m)
+
+
+def config4_fp4() -> MaskedFp4:
+    """The masked decode configuration with its weights in MXFP4: 16 groups, M_max=256,
+    masked_m ~ Poisson(64), N=4096, K=7168."""
+    return masked_fp4(config4_masked_m(), 256, 4096, 7168, seed=44, expected_m=64)
+
+
 def moe_expert(masked_m, M_max: int, H: int, I: int, seed: int, expected_m: int = 0) -> MoeExpert:
     """Activations as in ``masked`` (hidden size H); both layers' weights N(0,1) quantised per
     128x128 block with their scales divided by sqrt(fan-in), so the first layer's outputs (the
@@ -367,6 +428,17 @@ def moe_expert_work(valid_rows_per_group, H, I, G):
     f2, b2 = grouped_work(valid_rows_per_group, H, I, index_bytes=4 * G)
     rows = int(sum(valid_rows_per_group))
     return f1 + f2, b1 + swiglu_quantize_work(rows, I) + b2
+
+
+def grouped_fp4_work(valid_rows_per_group, N, K, index_bytes):
+    """(flop, bytes) of the masked GEMM with MXFP4 weights: B is K/2 bytes per row plus one E8M0
+    byte per 32 values; A, its scales, D and the counts as in ``grouped_work``."""
+    nkb = -(-K // BLOCK)
+    rows = int(sum(valid_rows_per_group))
+    groups = sum(1 for c in valid_rows_per_group if c > 0)
+    flop = 2 * rows * N * K
+    byts = rows * K + 4 * rows * nkb + groups * (N * K // 2 + N * K // 32) + 2 * rows * N + index_bytes
+    return flop, byts
 
 
 def grouped_work(valid_rows_per_group, N, K, index_bytes):
