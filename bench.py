@@ -254,6 +254,8 @@ def main():
                     flop_per_launch=kern_flop[dom] // kern_launch[dom],
                     share_of_step=round(kern_time[dom] / sum(kern_time.values()), 3))
 
+    specialized = bench_specialized(fg, torch, stream, cases, per, replay, read_flush, reps)
+
     grouped = {}
     if not args.no_grouped:
         del flush
@@ -290,6 +292,7 @@ def main():
         "grouped": grouped,
         "quantize_1x128": quantize,
         "moe_expert_chain": moe,
+        "specialized": specialized,
     }
     print(json.dumps(line), flush=True)
 
@@ -391,6 +394,52 @@ def traffic_summary(fetch_dir, write_dir):
         f.write("traffic_bytes_per_launch: %d   (mean over the %d shapes run by %s)\n"
                 % (per_launch, len(dom), DOMINANT_KERNEL))
     print(open(path).read())
+
+
+def bench_specialized(fg, torch, stream, cases, per, replay, read_flush, reps):
+    """The 18 sweep shapes with the tiled kernel built at run time for each (N, K): compile + load
+    time of each kernel, then the same per-shape timing as the table kernels (HIP events around
+    a graph of COPIES launches after a read-only 1 GiB buffer read), outputs checked bit for bit
+    against the table kernel's."""
+    t0 = time.time()
+    rows = []
+    for i, case in enumerate(cases):
+        compile_ms = fg.specialize_nt(case["M"], case["N"], case["K"])
+        ref = case["copies"][0]["D"].clone()
+
+        def call(r, case=case):
+            c = case["copies"][r]
+            fg.gemm_nt_specialized(c["A"], c["sa"], c["B"], c["sb"], out=c["D"], stream=stream)
+
+        with torch.cuda.stream(stream):
+            call(0)
+        stream.synchronize()
+        if not torch.equal(case["copies"][0]["D"], ref):
+            raise RuntimeError("specialized kernel differs from the table kernel (case %d)" % i)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(COPIES):
+                call(r)
+        ts = []
+        for _ in range(reps):
+            read_flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            replay(g)
+            e1.record(stream)
+            stream.synchronize()
+            ts.append(e0.elapsed_time(e1) / COPIES)
+        us = float(np.mean(ts)) * 1e3
+        rows.append(dict(M=case["M"], N=case["N"], K=case["K"], us_table=per[i]["us"], us_specialized=round(us, 2),
+                         speedup=round(per[i]["us"] / us, 4), compile_ms=round(compile_ms, 1)))
+        del g
+    sp = [r["speedup"] for r in rows]
+    geo = float(np.exp(np.mean(np.log(sp))))
+    log("specialized kernels: geomean speedup %.3f over the table kernels, compile %.0f ms total (%.1f s)" % (
+        geo, sum(r["compile_ms"] for r in rows), time.time() - t0))
+    return dict(geomean_speedup=round(geo, 4), compile_ms_total=round(sum(r["compile_ms"] for r in rows), 1),
+                per_shape=rows)
 
 
 GROUPED_CALLS = 3      # calls per timed graph of the grouped configurations

@@ -4,6 +4,7 @@ Argument marshalling only -- every step of the computation runs in the HIP kerne
 C ABI declared in include/fp8gemm.h.  torch supplies device memory and the current stream.
 
     D = gemm_nt(A, sa, B, sb)                              # dense NT, bf16 out
+    D = gemm_nt_specialized(A, sa, B, sb)                  # the same, kernel built at run time for N, K
     D = grouped_contiguous(A, sa, B, sb, m_indices)        # MoE, groups concatenated along M
     D = grouped_masked(A, sa, B, sb, masked_m, expected_m) # MoE, fixed per-group capacity
     D = fp8fp4_grouped_masked(A, sa, B4, sb4, masked_m, expected_m)  # the same, B in E2M1 + E8M0
@@ -22,7 +23,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gemm_nt", "grouped_contiguous", "grouped_masked", "quantize_1x128",
+__all__ = ["gemm_nt", "gemm_nt_specialized", "specialize_nt", "specialized_code_object", "specialized_count",
+           "grouped_contiguous", "grouped_masked", "quantize_1x128",
            "quantize_1x128_masked", "fp8fp4_grouped_masked", "swiglu_quantize_1x128", "swiglu_quantize_1x128_masked",
            "moe_expert_masked", "init", "set_num_cus",
            "last_config", "read_device_error", "status_string", "lib", "library_path",
@@ -42,6 +44,12 @@ DEVERR_BAD_COUNT = 2
 _P, _I64, _I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
 SIGNATURES = {
     "fp8gemm_nt": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "fp8gemm_nt_specialized": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "fp8gemm_specialize_nt": (ctypes.c_int, [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_double)]),
+    "fp8gemm_specialized_code_object": (ctypes.c_int, [ctypes.c_int] * 6 + [_I64, _I64, _P,
+                                                       ctypes.POINTER(ctypes.c_size_t), ctypes.c_char_p,
+                                                       ctypes.c_int]),
+    "fp8gemm_specialized_count": (ctypes.c_int, []),
     "fp8gemm_grouped_contiguous": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P]),
     "fp8gemm_grouped_masked": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _P]),
     "fp8gemm_quantize_1x128": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
@@ -176,6 +184,43 @@ def _shape_check(cond, msg):
 
 def gemm_nt(A, sa, B, sb, out=None, stream=None):
     """D[M,N] (bf16) = A[M,K] . B[N,K]^T with sa [K/128, M] and sb [ceil(N/128), K/128]."""
+    return _dense("fp8gemm_nt", A, sa, B, sb, out, stream)
+
+
+def gemm_nt_specialized(A, sa, B, sb, out=None, stream=None):
+    """gemm_nt with the tiled kernel compiled at run time for this N and K (cached per device);
+    the same results, bit for bit."""
+    return _dense("fp8gemm_nt_specialized", A, sa, B, sb, out, stream)
+
+
+def specialize_nt(M: int, N: int, K: int) -> float:
+    """Build (or find cached) the kernel gemm_nt_specialized runs for (M, N, K) on the current
+    device; returns the compile + load time in ms (0.0 when it was cached)."""
+    ms = ctypes.c_double(0.0)
+    _check(lib().fp8gemm_specialize_nt(int(M), int(N), int(K), ctypes.byref(ms)), "fp8gemm_specialize_nt")
+    return ms.value
+
+
+def specialized_code_object(layout: int, bm: int, bn: int, waves_m: int, waves_n: int, stages: int,
+                            N: int, K: int):
+    """(code object bytes, kernel symbol) of a tiled table entry specialised to (N, K); no GPU."""
+    size = ctypes.c_size_t(0)
+    log = ctypes.create_string_buffer(65536)
+    args = [int(layout), int(bm), int(bn), int(waves_m), int(waves_n), int(stages), int(N), int(K)]
+    _check(lib().fp8gemm_specialized_code_object(*args, None, ctypes.byref(size), log, len(log)),
+           "fp8gemm_specialized_code_object: " + log.value.decode(errors="replace")[:2000])
+    buf = ctypes.create_string_buffer(size.value)
+    _check(lib().fp8gemm_specialized_code_object(*args, buf, ctypes.byref(size), log, len(log)),
+           "fp8gemm_specialized_code_object")
+    return buf.raw[:size.value], log.value.decode()
+
+
+def specialized_count() -> int:
+    """Number of run-time specialised kernels cached in this process."""
+    return int(lib().fp8gemm_specialized_count())
+
+
+def _dense(fn, A, sa, B, sb, out, stream):
     torch = _torch()
     A, B = _codes(A, "A"), _codes(B, "B")
     sa, sb = _f32(sa, "sa"), _f32(sb, "sb")
@@ -186,9 +231,9 @@ def gemm_nt(A, sa, B, sb, out=None, stream=None):
                  "sa [K/128,M], sb [ceil(N/128),K/128]")
     D = _out(out, (M, N), A.device)
     with torch.cuda.device(A.device):
-        st = lib().fp8gemm_nt(A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(), D.data_ptr(),
-                              M, N, K, _stream(stream, A.device))
-    _check(st, "fp8gemm_nt")
+        st = getattr(lib(), fn)(A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(), D.data_ptr(),
+                                M, N, K, _stream(stream, A.device))
+    _check(st, fn)
     return D
 
 

@@ -37,6 +37,7 @@ struct Workspace {
 struct DeviceState {
     std::mutex mu;
     bool ready = false;
+    int id = 0;
     int cus = 0;
     int32_t* err = nullptr;                              // device error word
     std::vector<int> occupancy;                          // per kernel-table entry
@@ -71,6 +72,7 @@ int device_state(DeviceState** out) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8GEMM_ERR_HIP;
         d.cus = prop.multiProcessorCount;
+        d.id = dev;
         const std::vector<KernelEntry>& tab = kernels();
         d.occupancy.assign(tab.size(), 1);
         for (size_t i = 0; i < tab.size(); ++i) {
@@ -184,8 +186,11 @@ int pick_split(int64_t tiles, int nkb, int cus) {
 // address K (then the tiled kernel serves the call).
 Choice choose_masked_decode(int64_t N, int nkb, int64_t groups, int cus, bool fp4) {
     const int64_t K = (int64_t)nkb * 128;
-    // short K (few blocks per unit): narrower N tiles, so more units overlap their start-up
-    Choice c{K <= 2048 ? find_stream(kMasked, 128, 4, 1, 2, 4, fp4) : find_stream(kMasked, 128, 4, 2, 2, 4, fp4), 1};
+    // short K (few blocks per unit): narrower N tiles, so more units overlap their start-up; an
+    // E2M1 B (half the bytes per K block) takes 256-row N tiles, so the A tile staged per
+    // workgroup serves twice the B bytes
+    Choice c{K <= 2048 ? find_stream(kMasked, 128, 4, 1, 2, 4, fp4)
+                       : find_stream(kMasked, 128, 4, fp4 ? 4 : 2, 2, 4, fp4), 1};
     if (c.entry < 0) return c;
     const KernelEntry& e = kernels()[c.entry];
     if ((int64_t)std::max(e.bm, e.bn + 1) * K >= (int64_t(1) << 31)) return Choice{-1, 1};
@@ -249,7 +254,10 @@ Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_row
     return c;
 }
 
-int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream, bool fp4 = false) {
+// specialize: run the tiled kernel compiled at run time with this call's N and K (the launch
+// shape is the table's choice either way).
+int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream, bool fp4 = false,
+           bool specialize = false) {
     DeviceState* d = nullptr;
     int st = device_state(&d);
     if (st != FP8GEMM_OK) return st;
@@ -258,6 +266,12 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream,
     Choice c = choose(layout, a.rows, a.N, a.nkb, expected_rows, a.G, cus, fp4);
     if (c.entry < 0) return FP8GEMM_ERR_UNSUPPORTED;
     const KernelEntry& e = kernels()[c.entry];
+    const JitKernel* jk = nullptr;
+    if (specialize) {
+        if (e.kind != kKindTiled) return FP8GEMM_ERR_UNSUPPORTED;
+        st = jit_kernel(d->id, e, c.entry, a.N, a.K, &jk);
+        if (st != FP8GEMM_OK) return st;
+    }
     if (e.kind == kKindStream && (int64_t)std::max(e.bm, e.bn + 1) * a.K >= (int64_t(1) << 31))
         return FP8GEMM_ERR_UNSUPPORTED;     // a forced stream configuration beyond its offsets
 
@@ -292,7 +306,7 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream,
         a.ws = w->partials;
         a.counters = w->counters;
     }
-    int64_t slots = (int64_t)cus * d->occupancy[c.entry];
+    int64_t slots = (int64_t)cus * (jk ? jk->occupancy : d->occupancy[c.entry]);
     int64_t grid = std::min<int64_t>(a.units, slots);
     if (grid <= 0) return FP8GEMM_OK;
     const char* lname = layout == kDense ? "nt" : (layout == kContiguous ? "contiguous" : (fp4 ? "masked fp8xfp4" : "masked"));
@@ -304,10 +318,17 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream,
                       (long long)a.units, (long long)grid);
     else
         std::snprintf(g_last_config, sizeof g_last_config,
-                      "%s tile=%dx%d waves=%dx%d stages=%d split=%d kb_per_split=%d units=%lld grid=%lld",
-                      lname, e.bm, e.bn, e.waves_m, e.waves_n, e.stages, a.splits, a.kb_per_split,
-                      (long long)a.units, (long long)grid);
+                      "%s%s tile=%dx%d waves=%dx%d stages=%d split=%d kb_per_split=%d units=%lld grid=%lld",
+                      lname, jk ? " specialized" : "", e.bm, e.bn, e.waves_m, e.waves_n, e.stages, a.splits,
+                      a.kb_per_split, (long long)a.units, (long long)grid);
     if (std::getenv("FP8GEMM_LOG")) std::fprintf(stderr, "[fp8gemm] %s\n", g_last_config);
+    if (jk) {
+        void* params[] = {&a};
+        if (hipModuleLaunchKernel(jk->fn, (unsigned)grid, 1, 1, (unsigned)e.threads, 1, 1, 0, stream, params,
+                                  nullptr) != hipSuccess)
+            return FP8GEMM_ERR_LAUNCH;
+        return FP8GEMM_OK;
+    }
     e.launch(dim3((unsigned)grid), a, stream);
     if (hipGetLastError() != hipSuccess) return FP8GEMM_ERR_LAUNCH;
     return FP8GEMM_OK;
@@ -365,6 +386,32 @@ int quantize(const void* X, void* A, float* sa, const int32_t* masked_m, int32_t
     else launch_quantize_1x128(q, dim3((unsigned)grid), stream);
     if (hipGetLastError() != hipSuccess) return FP8GEMM_ERR_LAUNCH;
     return FP8GEMM_OK;
+}
+
+// Dense NT GEMM, from the table's kernel or its run-time specialisation.
+int dense(const void* A, const float* sa, const void* B, const float* sb, void* D, int64_t M, int64_t N,
+          int64_t K, void* stream, bool specialize) {
+    if (M < 0 || N < 0) return FP8GEMM_ERR_BAD_SHAPE;
+    int st = check_k(K);
+    if (st != FP8GEMM_OK) return st;
+    if (M > kMaxRows || N > kMaxRows || M * K >= kMaxBytes || N * K >= kMaxBytes)
+        return FP8GEMM_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return FP8GEMM_OK;
+    st = check_ptrs(A, sa, B, sb, D);
+    if (st != FP8GEMM_OK) return st;
+    KernelArgs a{};
+    a.A = static_cast<const uint8_t*>(A);
+    a.sa = sa;
+    a.B = static_cast<const uint8_t*>(B);
+    a.sb = sb;
+    a.D = static_cast<uint16_t*>(D);
+    a.rows = M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.G = 1;
+    a.nkb = (int32_t)(K / 128);
+    a.nnb = (int32_t)((N + 127) / 128);
+    return launch(kDense, a, M, static_cast<hipStream_t>(stream), false, specialize);
 }
 
 }  // namespace
@@ -449,28 +496,56 @@ int fp8gemm_moe_expert_masked(const void* A, const float* sa, const void* W1, co
 
 int fp8gemm_nt(const void* A, const float* sa, const void* B, const float* sb, void* D, int64_t M,
                int64_t N, int64_t K, void* stream) {
-    if (M < 0 || N < 0) return FP8GEMM_ERR_BAD_SHAPE;
+    return dense(A, sa, B, sb, D, M, N, K, stream, false);
+}
+
+int fp8gemm_nt_specialized(const void* A, const float* sa, const void* B, const float* sb, void* D, int64_t M,
+                           int64_t N, int64_t K, void* stream) {
+    return dense(A, sa, B, sb, D, M, N, K, stream, true);
+}
+
+int fp8gemm_specialize_nt(int64_t M, int64_t N, int64_t K, double* compile_ms) {
+    if (M <= 0 || N <= 0) return FP8GEMM_ERR_BAD_SHAPE;
     int st = check_k(K);
     if (st != FP8GEMM_OK) return st;
-    if (M > kMaxRows || N > kMaxRows || M * K >= kMaxBytes || N * K >= kMaxBytes)
-        return FP8GEMM_ERR_UNSUPPORTED;
-    if (M == 0 || N == 0) return FP8GEMM_OK;
-    st = check_ptrs(A, sa, B, sb, D);
+    if (M > kMaxRows || N > kMaxRows || M * K >= kMaxBytes || N * K >= kMaxBytes) return FP8GEMM_ERR_UNSUPPORTED;
+    DeviceState* d = nullptr;
+    st = device_state(&d);
     if (st != FP8GEMM_OK) return st;
-    KernelArgs a{};
-    a.A = static_cast<const uint8_t*>(A);
-    a.sa = sa;
-    a.B = static_cast<const uint8_t*>(B);
-    a.sb = sb;
-    a.D = static_cast<uint16_t*>(D);
-    a.rows = M;
-    a.N = (int32_t)N;
-    a.K = (int32_t)K;
-    a.G = 1;
-    a.nkb = (int32_t)(K / 128);
-    a.nnb = (int32_t)((N + 127) / 128);
-    return launch(kDense, a, M, static_cast<hipStream_t>(stream));
+    int cap = g_cu_cap.load();
+    int cus = (cap > 0 && cap < d->cus) ? cap : d->cus;
+    Choice c = choose(kDense, M, N, (int)(K / 128), M, 1, cus, false);
+    if (c.entry < 0) return FP8GEMM_ERR_UNSUPPORTED;
+    const int before = jit_cache_size();
+    const JitKernel* jk = nullptr;
+    st = jit_kernel(d->id, kernels()[c.entry], c.entry, (int)N, (int)K, &jk);
+    if (st != FP8GEMM_OK) return st;
+    if (compile_ms) *compile_ms = jit_cache_size() > before ? jk->compile_ms : 0.0;
+    return FP8GEMM_OK;
 }
+
+int fp8gemm_specialized_code_object(int layout, int bm, int bn, int waves_m, int waves_n, int stages, int64_t N,
+                                    int64_t K, void* buf, size_t* size, char* log, int log_len) {
+    if (!size) return FP8GEMM_ERR_NULL_PTR;
+    if (N <= 0 || N > kMaxRows) return FP8GEMM_ERR_BAD_SHAPE;
+    int st = check_k(K);
+    if (st != FP8GEMM_OK) return st;
+    const int idx = find_entry(layout, bm, bn, waves_m, waves_n, stages);
+    if (idx < 0) return FP8GEMM_ERR_BAD_SHAPE;
+    std::vector<char> code;
+    std::string lowered, text;
+    st = jit_compile(kernels()[idx], (int)N, (int)K, &code, &lowered, &text);
+    if (log && log_len > 0) std::snprintf(log, (size_t)log_len, "%s", st == FP8GEMM_OK ? lowered.c_str() : text.c_str());
+    if (st != FP8GEMM_OK) return st;
+    const size_t cap = *size;
+    *size = code.size();
+    if (!buf) return FP8GEMM_OK;
+    if (cap < code.size()) return FP8GEMM_ERR_BAD_SHAPE;
+    std::memcpy(buf, code.data(), code.size());
+    return FP8GEMM_OK;
+}
+
+int fp8gemm_specialized_count(void) { return jit_cache_size(); }
 
 int fp8gemm_grouped_contiguous(const void* A, const float* sa, const void* B, const float* sb,
                                const int32_t* m_indices, void* D, int64_t M_total, int64_t N,

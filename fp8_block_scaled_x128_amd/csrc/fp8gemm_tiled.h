@@ -1,0 +1,489 @@
+// fp8gemm_tiled.h -- the tiled gfx950 kernel body of the FP8 block-scaled GEMM.  Included by the
+// ahead-of-time build (fp8gemm_kernels.hip, N and K as arguments) and compiled at run time with
+// N and K fixed (fp8gemm_jit.cpp).
+//
+// One kernel body serves the dense NT GEMM and the two M-grouped MoE layouts (page
+// "DeepSeek開源第三彈：V3/R1訓練推理關鍵秘籍，核心代碼僅300行", sections 深入了解DeepGEMM and
+// 如何使用？: a single core kernel, fine-grained scaling, two-level accumulation; NT layout;
+// contiguous and masked grouped variants).
+//
+// Per work unit (an output tile, for one K range) a workgroup
+//   1. streams 128-wide K slices of the B tile, the A tile and their scales from HBM into an
+//      LDS ring with direct-to-LDS DMA loads (global_load_lds_dword[x4]), STAGES slices ahead;
+//   2. per slice and per 16x16 sub-tile issues ONE v_mfma_f32_16x16x128_f8f6f4 with a zero
+//      accumulator input, so the matrix core returns the fresh fp32 partial of exactly that
+//      128-wide block (the FP8 matrix-core sum is not exact fp32, so the partial is kept short);
+//   3. promotes the partial: acc += partial * (sa[m][kb] * sb[n/128][kb]) with VALU FMAs in
+//      fp32 -- the pages' two-level accumulation, re-derived for MFMA;
+//   4. rounds acc once to bf16 (round to nearest even) and stores D, or, when the K range is
+//      split across workgroups, writes its fp32 partial tile to a workspace; the last workgroup
+//      of the tile to arrive sums all partials in split order and stores D.
+//
+// MFMA orientation: the matrix core computes C[i][j] = sum_k X[i][k] Y[j][k] with lane l
+// holding X row (l % 16), Y row (l % 16) and output column (l % 16), rows 4*(l/16)..+3.  The
+// kernel feeds B rows as X and A rows as Y, so every lane owns 4 consecutive n of one m: the
+// promotion scale sa[m]*sb[n/128] is one value per lane per sub-tile and the bf16 results of a
+// lane are contiguous in D.  Both operands give lane l the K bytes [32*(l/16), +32) of the
+// slice, in the same order (the hardware pairs equal positions of X and Y).
+//
+// LDS layout of one slice: rows of 128 bytes, 16-byte chunk c of row r stored at chunk
+// position c ^ s(r) with s(r) = (r>>1 & 3) | ((r>>2 ^ r>>3) & 1) << 2.  A fragment read
+// (ds_read_b128, lane l: row l%16, chunk 2*(l/16)+h) is served 16 lanes per LDS cycle; measured
+// on gfx950, the lanes served together are those of one half-wave with equal parity of lane
+// bits 2..4.  The permutation gives those 16 lanes 16 distinct 16-byte bank groups of the
+// 256-byte-wide LDS (it is also conflict-free for runs of 8 or 16 consecutive lanes), so a
+// fragment read runs at the full ds_read_b128 rate; the DMA writes are contiguous 1 KB runs.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8gemm_args.h"
+#include "fp8gemm_device.h"
+
+namespace fp8gemm {
+
+// Chunk permutation of a 128-byte LDS row (see the layout note at the top of the file).
+__device__ __forceinline__ int swz(int row) {
+    return ((row >> 1) & 3) | ((((row >> 2) ^ (row >> 3)) & 1) << 2);
+}
+
+// ------------------------------------------------------------------------------------------
+// the kernel
+// ------------------------------------------------------------------------------------------
+
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT>
+struct Tile {
+    static constexpr int NW = WMW * WNW;            // waves per workgroup
+    static constexpr int NT = 64 * NW;
+    static constexpr int WM = BM / WMW;             // rows of M per wave
+    static constexpr int WN = BN / WNW;             // rows of N per wave
+    static constexpr int JM = WM / 16;              // 16-wide M sub-tiles per wave
+    static constexpr int IN = WN / 16;              // 16-wide N sub-tiles per wave
+    static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
+    static_assert(BN % 8 == 0 && BM % (8 * NW) == 0, "whole 8-row groups; every wave moves the same A rows count");
+    static_assert(BM % 64 == 0, "scale rows of A are moved 64 at a time");
+    static constexpr int B_OFF = 0;
+    static constexpr int A_OFF = BN * 128;
+    static constexpr int SA_OFF = (BN + BM) * 128;
+    static constexpr int SB_OFF = SA_OFF + BM * 4;
+    static constexpr int STAGE_BYTES = SB_OFF + 256;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    // x4 loads per wave per slice for B; when the BN/8 row groups do not split evenly over the
+    // waves, the spare slots repeat the last group (the same bytes to the same LDS rows), so every
+    // wave issues the same number of loads and waits with the same counts
+    static constexpr int B_GROUPS = BN / 8;
+    static constexpr int B_DMA = (B_GROUPS + NW - 1) / NW;
+    static constexpr int A_DMA = BM / (8 * NW);
+    static constexpr int AUX = (BM / 64 + 1 + NW - 1) / NW;  // x1 loads per wave: sa chunks + sb
+    static constexpr int NDMA = B_DMA + A_DMA + AUX;          // loads per wave per slice
+    static_assert(NDMA * (STAGES - 1) < 64, "vmcnt range");
+    // every wave's N range lies inside one 128-row block of B scales
+    static constexpr bool NB_UNIFORM = (BN % 128 == 0) && (128 % WN == 0);
+    // split-K partial reduction is compiled for tiles small enough to need it (decode shapes)
+    static constexpr bool SPLITK = BM * BN <= 128 * 256;
+};
+
+// NC, KC > 0 fix N and K at compile time (the run-time specialised variant); 0 reads them from
+// the arguments.
+template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int NC = 0, int KC = 0>
+__global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArgs args) {
+    using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
+    __shared__ int s_flag;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WMW;              // wave position along M
+    const int wn = wave / WMW;              // wave position along N
+    const int row16 = lane & 15;
+    const int grp = lane >> 4;
+    // every fragment row a lane reads is row16 plus a multiple of 16, so its two 16-byte chunks
+    // sit at the same swizzled positions in every row
+    const int frag_lo = ((2 * grp) ^ swz(row16)) << 4;
+    const int frag_hi = ((2 * grp + 1) ^ swz(row16)) << 4;
+
+    static_assert(KC % 128 == 0 && NC >= 0, "compile-time K is a multiple of 128");
+    const int K = KC > 0 ? KC : args.K;
+    const int N = NC > 0 ? NC : args.N;
+    const int nkb = KC > 0 ? KC / 128 : args.nkb;
+    const int nnb = NC > 0 ? (NC + 127) / 128 : args.nnb;
+    const uint32_t smem_base = lds_addr(smem);
+
+    // XCD-aware order: workgroups are dealt to the 8 XCDs round robin, so give the workgroups
+    // of one XCD a contiguous range of logical ids (consecutive units share operand panels).
+    const int P = gridDim.x;
+    int logical = blockIdx.x;
+    if ((P & 7) == 0) logical = (blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3);
+
+    for (int unit = logical; unit < args.units; unit += P) {
+        // ---- decode the unit: split s fastest, then M tile, N tile, group -------------------
+        // (uniform integer work on the scalar unit: multiply-shift divisions by launch constants)
+        uint32_t u = (uint32_t)unit;
+        const uint32_t tile_id = fast_div(u, args.div_splits);   // unit / splits
+        const int split = (int)(u - tile_id * (uint32_t)args.splits);
+        u = tile_id;
+        int tm, tn;
+        if (args.group_m > 1) {
+            // bands of group_m M tiles; inside a band the M tile varies fastest
+            const uint32_t grp_i = fast_div(u, args.div_group_tiles);
+            const uint32_t v = u - grp_i * args.div_group_tiles.d;
+            const uint32_t band = fast_div(v, args.div_band_units);
+            const uint32_t inb = v - band * args.div_band_units.d;
+            const int band_m0 = (int)band * args.group_m;
+            const bool full = band_m0 + args.group_m <= args.tiles_m;
+            const FastDiv& bh = full ? args.div_band_h : args.div_band_h_last;
+            const uint32_t q = fast_div(inb, bh);
+            tm = band_m0 + (int)(inb - q * bh.d);
+            tn = (int)q;
+            u = grp_i;
+        } else {
+            const uint32_t q = fast_div(u, args.div_tiles_m);
+            tm = (int)(u - q * (uint32_t)args.tiles_m);
+            u = q;
+            const uint32_t q2 = fast_div(u, args.div_tiles_n);
+            tn = (int)(u - q2 * (uint32_t)args.tiles_n);
+            u = q2;
+        }
+        const int gidx = (int)u;                       // group (masked layout), else 0
+        const int m0 = tm * BM;                        // first row of the tile (within group)
+        const int n0 = tn * BN;
+        const int kb0 = split * args.kb_per_split;
+        const int kb1 = min(nkb, kb0 + args.kb_per_split);
+        const int nks = kb1 - kb0;
+
+        // ---- rows of A, group of B ---------------------------------------------------------
+        int64_t arow0;        // first row of A / sa / D for this tile
+        int row_limit;        // rows [0, row_limit) of the tile are in range of the A array
+        int valid_rows;       // rows [0, valid_rows) may be valid (contiguous: further masked)
+        int g = 0;
+        int g_second = -1;    // contiguous 256-row tiles: the second 128-row block's group when it differs
+        if constexpr (LAYOUT == kMasked) {
+            g = gidx;
+            int cnt = args.masked_m[g];
+            if (cnt < 0 || cnt > args.rows) {
+                if (tm == 0 && tn == 0 && split == 0 && tid == 0)
+                    atomicOr(args.err, kDevErrBadCount);
+                cnt = cnt < 0 ? 0 : (int)args.rows;
+            }
+            if (m0 >= cnt) continue;                   // uniform: whole workgroup skips
+            arow0 = (int64_t)g * args.rows + m0;
+            row_limit = (int)min((int64_t)BM, args.rows - m0);
+            valid_rows = min(BM, cnt - m0);
+        } else if constexpr (LAYOUT == kContiguous) {
+            arow0 = m0;
+            row_limit = (int)min((int64_t)BM, args.rows - m0);
+            // the group of each 128-row block of the tile: the largest id among its rows; any row
+            // whose id is neither -1 nor its block's group breaks the precondition
+            constexpr int NBLK = BM > 128 ? BM / 128 : 1;
+            int gblk[NBLK];
+            int bad = 0;
+#pragma unroll
+            for (int h = 0; h < NBLK; ++h) {
+                const int r0 = h * 128, r1 = min(row_limit, r0 + min(BM, 128));
+                int gmax = -1;
+                for (int r = r0 + lane; r < r1; r += 64) {
+                    const int id = args.m_indices[arow0 + r];
+                    if (id < -1 || id >= args.G) bad = 1;
+                    else gmax = max(gmax, id);
+                }
+                gmax = __builtin_amdgcn_readfirstlane(wave_max(gmax));
+                for (int r = r0 + lane; r < r1; r += 64) {
+                    const int id = args.m_indices[arow0 + r];
+                    if (id >= 0 && id < args.G && id != gmax) bad = 1;
+                }
+                gblk[h] = gmax;
+            }
+            bad = __builtin_amdgcn_readfirstlane(wave_max(bad));
+            if (bad && wave == 0 && lane == 0 && split == 0 && tn == 0) atomicOr(args.err, kDevErrBadIndex);
+            // one pass when the blocks share a group (or one is padding only), else one per group;
+            // each pass stores only the rows of its own group
+            g = gblk[0];
+            if constexpr (NBLK == 2) {
+                if (g < 0) g = gblk[1];
+                else if (gblk[1] >= 0 && gblk[1] != g) g_second = gblk[1];
+            }
+            if (g < 0) continue;                       // padding only: nothing to compute
+            valid_rows = row_limit;
+        } else {
+            arow0 = m0;
+            row_limit = (int)min((int64_t)BM, args.rows - m0);
+            valid_rows = row_limit;
+        }
+        (void)valid_rows;
+        (void)g_second;
+        const uint8_t* Ag = args.A + arow0 * K;
+        // sa is stored K-block-major: [group][K/128][rows], so the scales of one K block for
+        // consecutive rows are contiguous (one DMA instruction covers 64 rows)
+        int64_t sa_first = arow0;                     // element (kb, r) of the group: kb*rows + r
+        if constexpr (LAYOUT == kMasked) sa_first = (int64_t)g * nkb * args.rows + m0;
+        const float* sag = args.sa + sa_first;
+        const int nb_first = n0 >> 7;
+        for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 1) {
+            if (g_second < 0) break;
+            g = g_second;
+        }
+        const uint8_t* Bg = args.B + (int64_t)g * N * K;
+        const float* sbg = args.sb + (int64_t)g * nnb * nkb;
+        const int nb_count = min(nnb, (n0 + BN + 127) >> 7) - nb_first;
+
+        // ---- per-lane DMA source offsets (32-bit, relative to uniform per-slice bases) -------
+        // B and A: x4 load q of wave w covers tile rows 8 (w count + q) .. + 7; lane -> (row, chunk)
+        auto b_row = [&](int q) -> int { return 8 * min(wave * T::B_DMA + q, T::B_GROUPS - 1); };
+        uint32_t b_off[T::B_DMA];
+#pragma unroll
+        for (int q = 0; q < T::B_DMA; ++q) {
+            const int r = b_row(q) + (lane >> 3);
+            const int c = (lane & 7) ^ swz(r);
+            const int n = min(r, N - 1 - n0);          // clamp the N tail to a real row
+            b_off[q] = (uint32_t)n * (uint32_t)K + (uint32_t)(c * 16);
+        }
+        uint32_t a_off[T::A_DMA];
+#pragma unroll
+        for (int q = 0; q < T::A_DMA; ++q) {
+            const int r = 8 * (wave * T::A_DMA + q) + (lane >> 3);
+            const int c = (lane & 7) ^ swz(r);
+            const int rr = min(r, row_limit - 1);
+            a_off[q] = (uint32_t)rr * (uint32_t)K + (uint32_t)(c * 16);
+        }
+        // aux x1 loads: chunk x < BM/64 moves sa rows 64x..64x+63, chunk BM/64 moves sb
+        uint32_t aux_off[T::AUX];
+#pragma unroll
+        for (int t = 0; t < T::AUX; ++t) {
+            const int x = wave + T::NW * t;
+            if (x < BM / 64) {
+                const int r = min(64 * x + lane, row_limit - 1);
+                aux_off[t] = (uint32_t)r * 4u;
+            } else {
+                const int nb = nb_first + min(lane, nb_count - 1);
+                aux_off[t] = (uint32_t)nb * (uint32_t)nkb * 4u;
+            }
+        }
+        const uint8_t* Bt = uniform_ptr(Bg + (int64_t)n0 * K + (int64_t)kb0 * 128);  // slice-0 bases
+        const uint8_t* At = uniform_ptr(Ag + (int64_t)kb0 * 128);
+        const float* sat = uniform_ptr(sag + (int64_t)kb0 * args.rows);
+        const float* sbt = uniform_ptr(sbg + kb0);
+
+        auto stage_addr = [&](int i) { return smem_base + (uint32_t)((i % STAGES) * T::STAGE_BYTES); };
+        // B loads q in [q0, q1) of slice i
+        auto issue_b = [&](int i, int q0, int q1) {
+            const uint32_t st = stage_addr(i);
+            const uint8_t* bs = uniform_ptr(Bt + (int64_t)i * 128);
+#pragma unroll
+            for (int q = 0; q < T::B_DMA; ++q)
+                if (q >= q0 && q < q1) dma_x4(st + T::B_OFF + b_row(q) * 128, bs, b_off[q]);
+        };
+        // A tile and scale loads of slice i
+        auto issue_a = [&](int i) {
+            const uint32_t st = stage_addr(i);
+            const uint8_t* as = uniform_ptr(At + (int64_t)i * 128);
+#pragma unroll
+            for (int q = 0; q < T::A_DMA; ++q)
+                dma_x4(st + T::A_OFF + 8 * (wave * T::A_DMA + q) * 128, as, a_off[q]);
+#pragma unroll
+            for (int t = 0; t < T::AUX; ++t) {
+                const int x = wave + T::NW * t;
+                if (x < BM / 64) dma_x1(st + T::SA_OFF + 256 * x, uniform_ptr(sat + (int64_t)i * args.rows), aux_off[t]);
+                else dma_x1(st + T::SB_OFF, uniform_ptr(sbt + i), aux_off[t]);
+            }
+        };
+
+        // ---- accumulators -------------------------------------------------------------------
+        v4f acc[T::IN][T::JM];
+#pragma unroll
+        for (int i = 0; i < T::IN; ++i)
+#pragma unroll
+            for (int j = 0; j < T::JM; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+        // ---- one 128-wide K slice on the matrix cores ---------------------------------------
+        auto compute_slice = [&](int i) {
+            const uint8_t* st = smem + (i % STAGES) * T::STAGE_BYTES;
+            const float* sa_l = reinterpret_cast<const float*>(st + T::SA_OFF);
+            const float* sb_l = reinterpret_cast<const float*>(st + T::SB_OFF);
+            auto load_bf = [&](int i2) {
+                const int r = wn * T::WN + 16 * i2 + row16;
+                const uint8_t* rp = st + T::B_OFF + r * 128;
+                const v4i lo = *reinterpret_cast<const v4i*>(rp + frag_lo);
+                const v4i hi = *reinterpret_cast<const v4i*>(rp + frag_hi);
+                return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            };
+            // A fragments (Y operand) and their scales for this wave's JM sub-tiles
+            v8i af[T::JM];
+            float sav[T::JM];
+#pragma unroll
+            for (int j = 0; j < T::JM; ++j) {
+                const int r = wm * T::WM + 16 * j + row16;
+                const uint8_t* rp = st + T::A_OFF + r * 128;
+                const v4i lo = *reinterpret_cast<const v4i*>(rp + frag_lo);
+                const v4i hi = *reinterpret_cast<const v4i*>(rp + frag_hi);
+                af[j] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                sav[j] = sa_l[r];
+            }
+            float sw[T::JM];
+            if constexpr (T::NB_UNIFORM) {
+                const float sbw = sb_l[((n0 + wn * T::WN) >> 7) - nb_first];
+#pragma unroll
+                for (int j = 0; j < T::JM; ++j) sw[j] = sav[j] * sbw;
+            }
+            v8i bf = load_bf(0);
+            auto promote = [&](int i2, const v4f (&p)[T::JM]) {
+                float sbi = 0.f;
+                if constexpr (!T::NB_UNIFORM) sbi = sb_l[((n0 + wn * T::WN + 16 * i2) >> 7) - nb_first];
+#pragma unroll
+                for (int j = 0; j < T::JM; ++j) {
+                    float s;
+                    if constexpr (T::NB_UNIFORM) s = sw[j];
+                    else s = sav[j] * sbi;
+                    acc[i2][j] += p[j] * s;
+                }
+            };
+            // Software pipeline over the N sub-tiles: the MFMAs of sub-tile i2 are issued before
+            // the promotion FMAs of sub-tile i2-1, so the matrix core and the VALU overlap and
+            // only one sub-tile row of partials is live.
+            v4f pprev[T::JM];
+#pragma unroll
+            for (int i2 = 0; i2 < T::IN; ++i2) {
+                v4f pcur[T::JM];
+#pragma unroll
+                for (int j = 0; j < T::JM; ++j) pcur[j] = mfma16x16x128(bf, af[j]);
+                if (i2 + 1 < T::IN) bf = load_bf(i2 + 1);
+                if (i2 > 0) promote(i2 - 1, pprev);
+#pragma unroll
+                for (int j = 0; j < T::JM; ++j) pprev[j] = pcur[j];
+                // issue order inside the step: one MFMA, the next fragment's LDS reads, then
+                // alternate MFMAs with the promotion FMAs of the previous step, so that one wave
+                // keeps the matrix core and the VALU busy at the same time
+                if (i2 > 0) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // DS read
+#pragma unroll
+                    for (int j = 1; j < T::JM; ++j) {
+                        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);      // VALU
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);         // VALU
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            promote(T::IN - 1, pprev);
+        };
+
+        // ---- ring of whole slices: slice i + STAGES - 1 goes into the stage slice i - 1 used
+#pragma unroll
+        for (int i = 0; i < STAGES - 1; ++i)
+            if (i < nks) { issue_b(i, 0, T::B_DMA); issue_a(i); }
+        for (int i = 0; i < nks; ++i) {
+            // slice i landed (this wave's loads), then every wave's loads
+            wait_slices<T::NDMA, STAGES - 2, 0>(min(STAGES - 2, nks - 1 - i));
+            __syncthreads();
+            if (i + STAGES - 1 < nks) { issue_b(i + STAGES - 1, 0, T::B_DMA); issue_a(i + STAGES - 1); }
+            compute_slice(i);
+        }
+
+        // ---- epilogue -----------------------------------------------------------------------
+        bool store_direct = true;
+        if (T::SPLITK && args.splits > 1) {
+            // Split-K exchange between the workgroups of one tile, which may sit on different
+            // XCDs (each with its own L2).  Partials are written and read with agent-coherent
+            // (sc1) 16-byte buffer accesses, so no L2-wide write-back or invalidate is needed:
+            //   write partial (sc1) -> wait until written -> barrier -> counter += 1 (agent)
+            //   last arrival: barrier -> read all partials (sc1) in split order -> store D
+            const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                uniform_ptr(args.ws + tile_id * args.splits * (int64_t)(BM * BN)), 0,
+                (int)(args.splits * BM * BN * 4), kBufferFlags);
+            const int lane_off = (wave * (T::WM * T::WN) + lane * 4) * 4;
+#pragma unroll
+            for (int i2 = 0; i2 < T::IN; ++i2)
+#pragma unroll
+                for (int j = 0; j < T::JM; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        acc[i2][j], ws_rsrc,
+                        lane_off + ((split * BM * BN) + (i2 * T::JM + j) * 256) * 4, 0, kSc1);
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (tid == 0) {
+                const int old = __hip_atomic_fetch_add(args.counters + tile_id, 1, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+                const int last = (old == args.splits - 1);
+                if (last)   // ready for the next launch
+                    __hip_atomic_store(args.counters + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_flag = last;
+            }
+            __syncthreads();
+            store_direct = s_flag != 0;
+            if (store_direct) {
+                // sum every split's partial (this one's included) in split order, so the result
+                // does not depend on which workgroup arrived last; the reads of CH splits are in
+                // flight together (loads first, unconditionally, then the ordered sums)
+                constexpr int CH = (T::IN * T::JM >= 16) ? 1 : 16 / (T::IN * T::JM);
+                for (int s0 = 0; s0 < args.splits; s0 += CH) {
+                    v4f x[CH][T::IN][T::JM];
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) {
+                        const int s2 = min(s0 + c, args.splits - 1);
+#pragma unroll
+                        for (int i2 = 0; i2 < T::IN; ++i2)
+#pragma unroll
+                            for (int j = 0; j < T::JM; ++j)
+                                x[c][i2][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                                    ws_rsrc, lane_off + ((s2 * BM * BN) + (i2 * T::JM + j) * 256) * 4, 0, kSc1);
+                    }
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) {
+                        if (s0 + c < args.splits) {
+#pragma unroll
+                            for (int i2 = 0; i2 < T::IN; ++i2)
+#pragma unroll
+                                for (int j = 0; j < T::JM; ++j)
+                                    acc[i2][j] = (s0 + c == 0) ? x[c][i2][j] : acc[i2][j] + x[c][i2][j];
+                        }
+                    }
+                }
+            }
+        }
+        if (store_direct) {
+            // lane owns D[m][n..n+3] per sub-tile
+#pragma unroll
+            for (int j = 0; j < T::JM; ++j) {
+                const int rm = wm * T::WM + 16 * j + row16;     // row within the tile
+                bool ok = rm < valid_rows;
+                if constexpr (LAYOUT == kContiguous) {
+                    if (ok) ok = args.m_indices[arow0 + rm] == g;
+                }
+                if (!ok) continue;
+                uint16_t* drow = args.D + (arow0 + rm) * (int64_t)N;
+#pragma unroll
+                for (int i2 = 0; i2 < T::IN; ++i2) {
+                    const int n = n0 + wn * T::WN + 16 * i2 + 4 * grp;
+                    const v4f v = acc[i2][j];
+                    if (n + 3 < N && (N & 3) == 0) {
+                        uint2 pk;
+                        pk.x = pack_bf16x2(v.x, v.y);
+                        pk.y = pack_bf16x2(v.z, v.w);
+                        *reinterpret_cast<uint2*>(drow + n) = pk;
+                    } else {
+                        const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            if (n + r < N) {
+                                __bf16 h = (__bf16)e[r];
+                                uint16_t hb;
+                                __builtin_memcpy(&hb, &h, 2);
+                                drow[n + r] = hb;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        // the next pass's or unit's prologue rewrites stages other waves may still be reading
+        __syncthreads();
+        }   // pass
+    }
+}
+
+}  // namespace fp8gemm

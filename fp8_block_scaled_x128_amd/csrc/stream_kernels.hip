@@ -39,10 +39,31 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fp8gemm_device.h"
 #include "fp8gemm_internal.h"
 
 namespace fp8gemm {
+
+// f(std::integral_constant<int, n>) for the runtime count n in [1, MAX]
+template <int C, int MAX, typename F>
+__device__ __forceinline__ void with_count_from(int n, F& f) {
+    if constexpr (C < MAX) {
+        if (n == C) {
+            f(std::integral_constant<int, C>{});
+            return;
+        }
+        with_count_from<C + 1, MAX>(n, f);
+    } else {
+        f(std::integral_constant<int, MAX>{});
+    }
+}
+
+template <int MAX, typename F>
+__device__ __forceinline__ void with_count(int n, F& f) {
+    with_count_from<1, MAX>(n, f);
+}
 
 template <int MT, int W, int JN, int KP, int PF>
 struct Stream {
@@ -171,19 +192,22 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
         // loop is unconditional (a K block or row past the end re-reads the last valid one, a cache
         // hit), so the compiler's memory-counter waits before each use stay exact and leave the
         // later loads in flight.
-        // rows of A loaded: the active sub-tiles, clamped to the array (rows past the count are
+        // rows of A loaded: the NS active sub-tiles (a compile-time count, so a workgroup issues
+        // only the loads its valid rows need), clamped to the array (rows past the count are
         // never read; a clamped row re-reads the last one, a cache hit)
         const int rows_needed = min(nsub * 16, row_limit);
         v4i a_reg[T::NA4];
         float sa_reg[T::NSA];
         float sb_reg = 0.f;
-        auto load_a = [&](int ph) {
+        auto load_a = [&](auto ns_c, int ph) {
+            constexpr int RN = decltype(ns_c)::value * 16;           // rows staged per K block
+            constexpr int NA = (KP * RN * 8 + T::NT - 1) / T::NT;    // 16-byte chunks per thread
             const int kbp = ph * KP;
 #pragma unroll
-            for (int i = 0; i < T::NA4; ++i) {
-                const int cid = tid + T::NT * i;          // chunk: 8 per row, MT rows per K block
-                const int kb = min(kbp + cid / (MT * 8), nks - 1);
-                const int r = min((cid >> 3) % MT, rows_needed - 1);
+            for (int i = 0; i < NA; ++i) {
+                const int cid = tid + T::NT * i;          // chunk: 8 per row, RN rows per K block
+                const int kb = min(kbp + cid / (RN * 8), nks - 1);
+                const int r = min((cid >> 3) % RN, rows_needed - 1);
                 a_reg[i] = *reinterpret_cast<const v4i*>(Ag + (int64_t)r * K + (int64_t)(kb0 + kb) * 128 + (cid & 7) * 16);
             }
 #pragma unroll
@@ -200,15 +224,17 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
                 sb_reg = sbg[(int64_t)(nb_first + nbi) * nkb + kb0 + kb];
             }
         };
-        auto store_a = [&](int ph) {
+        auto store_a = [&](auto ns_c, int ph) {
+            constexpr int RN = decltype(ns_c)::value * 16;
+            constexpr int NA = (KP * RN * 8 + T::NT - 1) / T::NT;
             const int kbp = ph * KP;
             const int tp = min(KP, nks - kbp);
             uint8_t* dst = smem + (ph & 1) * T::PHASE_BYTES;
 #pragma unroll
-            for (int i = 0; i < T::NA4; ++i) {
+            for (int i = 0; i < NA; ++i) {
                 const int cid = tid + T::NT * i;
-                const int t = cid / (MT * 8);
-                const int r = (cid >> 3) % MT;
+                const int t = cid / (RN * 8);
+                const int r = (cid >> 3) % RN;
                 if (t < tp && r < rows_needed)
                     *reinterpret_cast<v4i*>(dst + (t * MT + r) * 128 + (((cid & 7) ^ ((r >> 1) & 7)) << 4)) = a_reg[i];
             }
@@ -230,56 +256,99 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
 #pragma unroll
             for (int j = 0; j < T::MSUB; ++j) acc[f][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-        // one K block: MFMA partials of the active sub-tiles, promoted into acc
-        auto compute = [&](int kb, const v8i (&bf)[JN], const uint32_t (&sw)[JN]) {
+        // one K block over the NS active sub-tiles (a compile-time count, so the block is
+        // straight-line code: the A reads, then NS * JN independent MFMAs, then their promotions,
+        // which the scheduler can overlap; a branch per sub-tile would serialise every MFMA with
+        // the FMAs that read its result)
+        auto compute = [&](auto ns_c, int kb, const v8i (&bf)[JN], const uint32_t (&sw)[JN]) {
+            constexpr int NS = decltype(ns_c)::value;
             const int t = kb % KP;
             const uint8_t* ph = smem + ((kb / KP) & 1) * T::PHASE_BYTES;
             const uint8_t* ab = ph + t * MT * 128;
             const float* sal = reinterpret_cast<const float*>(ph + T::SA_OFF) + t * MT;
             // E4M3 B: the 128x128 block scale, applied with sa; E2M1 B: scales inside the MFMA
             const float sbv = FP4 ? 1.0f : reinterpret_cast<const float*>(ph + T::SB_OFF)[nbi_w * KP + t];
+            if constexpr (JN == 1 || JN >= 4) {
+                // one sub-tile at a time, so few registers stay live (JN MFMAs per step are
+                // independent when JN >= 4; with one fragment per wave there is one K loop for
+                // every count -- NS = all sub-tiles, the active ones chosen at run time -- and two
+                // workgroups fit on a CU, whose waves cover each other's latencies)
 #pragma unroll
-            for (int j = 0; j < T::MSUB; ++j) {
-                if (j < nsub) {
+                for (int j = 0; j < NS; ++j) {
+                    if (JN == 1 && j >= nsub) break;
                     const uint8_t* rp = ab + (16 * j + r16) * 128;
                     const v4i lo = *reinterpret_cast<const v4i*>(rp + frag_lo);
                     const v4i hi = *reinterpret_cast<const v4i*>(rp + frag_hi);
-                    const v8i af = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                    const float s = sal[16 * j + r16] * sbv;
+                    const v8i a1 = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                    const float s1 = sal[16 * j + r16] * sbv;
+                    v4f p1[JN];
 #pragma unroll
                     for (int f = 0; f < JN; ++f) {
-                        v4f p;
-                        if constexpr (FP4) p = mfma16x16x128_fp4_fp8(bf[f], af, (int)((sw[f] >> (8 * q)) & 0xFFu));
-                        else p = mfma16x16x128(bf[f], af);
-                        acc[f][j] += p * s;
+                        if constexpr (FP4) p1[f] = mfma16x16x128_fp4_fp8(bf[f], a1, (int)((sw[f] >> (8 * q)) & 0xFFu));
+                        else p1[f] = mfma16x16x128(bf[f], a1);
                     }
+#pragma unroll
+                    for (int f = 0; f < JN; ++f) acc[f][j] += p1[f] * s1;
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+                return;
             }
+            v8i af[NS];
+            float s[NS];
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                const uint8_t* rp = ab + (16 * j + r16) * 128;
+                const v4i lo = *reinterpret_cast<const v4i*>(rp + frag_lo);
+                const v4i hi = *reinterpret_cast<const v4i*>(rp + frag_hi);
+                af[j] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                s[j] = sal[16 * j + r16] * sbv;
+            }
+            v4f p[NS][JN];
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+#pragma unroll
+                for (int f = 0; f < JN; ++f) {
+                    if constexpr (FP4) p[j][f] = mfma16x16x128_fp4_fp8(bf[f], af[j], (int)((sw[f] >> (8 * q)) & 0xFFu));
+                    else p[j][f] = mfma16x16x128(bf[f], af[j]);
+                }
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+#pragma unroll
+                for (int f = 0; f < JN; ++f) acc[f][j] += p[j][f] * s[j];
         };
 
         // ---- K loop: B PF-1 blocks ahead in registers, A one phase ahead in LDS ----------------
         // the same issue order as in the loop (A of a phase, then B), so the memory-counter state
         // the compiler merges at the loop head does not force a full drain
-        load_a(0);
-        asm volatile("" ::: "memory");
+        auto kloop = [&](auto ns_c) {
+            load_a(ns_c, 0);
+            asm volatile("" ::: "memory");
 #pragma unroll
-        for (int u2 = 0; u2 < PF - 1; ++u2) issue_b(min(u2, nks - 1), ring[u2], sring[u2]);
-        for (int base = 0; base < nks; base += T::U) {
-            // U = lcm(KP, PF) K blocks: every trip starts a phase and a ring cycle
+            for (int u2 = 0; u2 < PF - 1; ++u2) issue_b(min(u2, nks - 1), ring[u2], sring[u2]);
+            for (int base = 0; base < nks; base += T::U) {
+                // U = lcm(KP, PF) K blocks: every trip starts a phase and a ring cycle
 #pragma unroll
-            for (int u2 = 0; u2 < T::U; ++u2) {
-                const int kb = base + u2;
-                if (u2 % KP == 0) {
-                    // phase start: this phase's A into LDS, visible to every wave, then the
-                    // next phase's loads (the buffer they go to was last read two phases ago)
-                    store_a(kb / KP);
-                    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-                    load_a(kb / KP + 1);
+                for (int u2 = 0; u2 < T::U; ++u2) {
+                    const int kb = base + u2;
+                    if (u2 % KP == 0) {
+                        // phase start: this phase's A into LDS, visible to every wave, then the
+                        // next phase's loads (the buffer they go to was last read two phases ago)
+                        store_a(ns_c, kb / KP);
+                        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                        load_a(ns_c, kb / KP + 1);
+                    }
+                    issue_b(min(kb + PF - 1, nks - 1), ring[(u2 + PF - 1) % PF], sring[(u2 + PF - 1) % PF]);
+                    if (kb < nks) compute(ns_c, kb, ring[u2 % PF], sring[u2 % PF]);
+                    // keep each K block's LDS reads and MFMAs in its own step: hoisting later blocks'
+                    // reads raises register use past what the ring and accumulators need
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                issue_b(min(kb + PF - 1, nks - 1), ring[(u2 + PF - 1) % PF], sring[(u2 + PF - 1) % PF]);
-                if (kb < nks) compute(kb, ring[u2 % PF], sring[u2 % PF]);
             }
-        }
+        };
+        // one instance of the K loop per active sub-tile count (one for all counts with one
+        // fragment per wave)
+        if constexpr (JN == 1) kloop(std::integral_constant<int, T::MSUB>{});
+        else with_count<T::MSUB>(nsub, kloop);
 
         // ---- epilogue: split-K exchange (agent-coherent partials), then bf16 stores ---------
         bool store_direct = true;
@@ -412,19 +481,28 @@ static KernelEntry stream_entry(const char* name) {
 
 // Masked groups of at most 128 valid rows (one tile per group and N tile, B streamed once per
 // group).  Measured on 16 groups x 256 rows (about 64 valid each), graphs of 3 launches:
-//   N = 4096, K = 7168: 4 waves x 2 fragments, 2-block phases 108 us (4.5 TB/s); 8 waves x 1
-//     fragment 113 us; 4 waves x 1 fragment 125 us; the tiled kernel's 128x128 tile 168 us;
-//   N = 7168, K = 2048: 4 waves x 1 fragment 64 us (3.9 TB/s); 8 x 1: 67 us; 4 x 2: 69 us.
+//   N = 4096, K = 7168: 4 waves x 2 fragments, 2-block phases 105 us (4.6 TB/s); 8 waves x 1
+//     fragment 109 us; 4 waves x 1 fragment 127 us; the tiled kernel's 128x128 tile 168 us;
+//     with E2M1 B: 4 waves x 4 fragments 92 us, x 2 fragments 95 us, 8 waves x 1 fragment 95 us;
+//   N = 7168, K = 2048: 4 waves x 1 fragment 66 us (3.8 TB/s); 8 x 1: 65 us; 4 x 2: 64 us.
 // Splitting K was slower everywhere (the groups times N tiles already fill the CUs).
+//
+// What bounds these kernels is the vector-memory issue rate of a CU, not HBM: a 16-byte-per-lane
+// load whose lanes walk 16 rows (the MFMA's lane layout: lane l holds row l % 16) occupies the
+// CU's address path about 58 cycles, against 18 for 8 rows x 128 bytes and 16 for a contiguous
+// kilobyte (measured on gfx950 with L2-resident data); B, and for E2M1 its per-row scales, are
+// loaded in the 16-row form.
 const KernelEntry* stream_table(int* count) {
     static const KernelEntry table[] = {
         STREAM_ENTRY(128, 4, 2, 2, 4),
         STREAM_ENTRY(128, 4, 1, 2, 4),
-        STREAM_ENTRY(128, 8, 1, 4, 4),
+        STREAM_ENTRY(128, 8, 1, 2, 4),
         // E4M3 x E2M1 (B with one E8M0 scale per 32 K): half the B bytes per K block
         STREAM_ENTRY_FP4(128, 4, 2, 2, 4),
         STREAM_ENTRY_FP4(128, 4, 4, 2, 4),
         STREAM_ENTRY_FP4(128, 4, 1, 2, 4),
+        STREAM_ENTRY_FP4(128, 4, 2, 2, 8),
+        STREAM_ENTRY_FP4(128, 8, 1, 2, 4),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -41,6 +41,7 @@
 #ifndef FP8GEMM_H
 #define FP8GEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -180,6 +181,39 @@ const char* fp8gemm_status_string(int status);
 /* Optional eager set-up on the current device: device query and the device error word.  The
  * GEMM calls do it lazily otherwise.  Returns FP8GEMM_ERR_HIP when no device is usable. */
 int fp8gemm_init(void);
+
+/* Run-time shape specialisation (the pages' JIT idea: every kernel compiled at run time with
+ * the block sizes and stages chosen for the shape, page "DeepSeek開源第三彈…", sections
+ * 深入了解DeepGEMM and 如何使用？).  The launch shape stays the table's choice; the tiled kernel
+ * is compiled with hipRTC for gfx950 with N and K as compile-time constants, loaded as a module
+ * on the current device and cached there for the life of the process (keyed by table entry, N
+ * and K).  Nothing is written to disk.
+ *
+ * fp8gemm_nt_specialized: the same operation, arguments, validation and results as fp8gemm_nt
+ *   (the same bits: the kernel body and its arithmetic order are identical).  The first call for
+ *   a new (launch shape, N, K) on a device compiles the kernel on the calling thread (a few
+ *   hundred milliseconds, serialised across threads) before enqueueing; later calls only launch.
+ *   A failed compile or module load returns FP8GEMM_ERR_HIP (the compiler log goes to stderr).
+ *   Not for HIP graph capture until the kernel is cached (call fp8gemm_specialize_nt first). */
+int fp8gemm_nt_specialized(const void* A, const float* sa, const void* B, const float* sb, void* D,
+                           int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Compile and load, ahead of use, the kernel fp8gemm_nt_specialized would run for (M, N, K)
+ * on the current device.  *compile_ms (if not NULL) receives the compile + load time in
+ * milliseconds, or 0 when the kernel was already cached.  M, N > 0; K as for fp8gemm_nt. */
+int fp8gemm_specialize_nt(int64_t M, int64_t N, int64_t K, double* compile_ms);
+
+/* The gfx950 code object of the tiled table entry (layout 0 dense, 1 contiguous, 2 masked;
+ * tile bm x bn, waves_m x waves_n waves, `stages` ring stages) specialised to (N, K), for
+ * inspection; no GPU is needed.  *size: in, the capacity of buf (bytes); out, the code object's
+ * size.  buf == NULL queries the size only.  log (log_len bytes, may be NULL) receives the
+ * kernel's symbol name, or the compiler log on failure.  An entry not in the table, N <= 0 or a
+ * bad K is FP8GEMM_ERR_BAD_SHAPE, as is a buffer too small; a compile failure FP8GEMM_ERR_HIP. */
+int fp8gemm_specialized_code_object(int layout, int bm, int bn, int waves_m, int waves_n, int stages,
+                                    int64_t N, int64_t K, void* buf, size_t* size, char* log, int log_len);
+
+/* Number of specialised kernels cached in this process (all devices). */
+int fp8gemm_specialized_count(void);
 
 /* Cap the number of compute units the launch shapes are sized for and the persistent grids
  * occupy (the "set max SM count" utility of page "DeepSeek開源第三彈…", section 如何使用？).
