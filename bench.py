@@ -71,9 +71,13 @@ COPY_BYTES = 1 << 30           # calibration copy: reads and writes this many by
 
 
 def kernel_source_hash():
+    """Hash of the sources that make the dense tiled kernel (its body, helpers, argument block and
+    instantiation table)."""
     import hashlib
-    src = os.path.join(ROOT, "fp8_block_scaled_x128_amd", "csrc", "fp8gemm_kernels.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in ("fp8gemm_tiled.h", "fp8gemm_device.h", "fp8gemm_args.h", "fp8gemm_kernels.hip"):
+        h.update(open(os.path.join(ROOT, "fp8_block_scaled_x128_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
@@ -344,7 +348,7 @@ def _counter_rows(folder, counter):
     return [per[k] for k in sorted(per)]
 
 
-DOMINANT_KERNEL = "fp8gemm_kernel<256, 256, 4, 2, 2, 0>"
+DOMINANT_KERNEL = "fp8gemm_kernel<256, 256, 4, 2, 2, 0, 0, 0>"
 
 
 def traffic_summary(fetch_dir, write_dir):
