@@ -10,6 +10,7 @@ namespace fp8gemm {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------------------------------
 // device helpers

@@ -157,34 +157,59 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
         const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(Bt), 0, 0x7FFFFFFF, kBufferFlags);
         uint32_t b_off[JN];
-        uint32_t s_off[JN];
+        uint32_t s_row[JN];          // E2M1: byte offset of the fragment row's E8M0 scales
 #pragma unroll
         for (int f = 0; f < JN; ++f) {
             const int r = min(wave * JN * 16 + 16 * f + r16, N - 1 - n0);
             b_off[f] = (uint32_t)r * (uint32_t)brow + (uint32_t)(16 * q) + (uint32_t)kb0 * KBB;
-            s_off[f] = (uint32_t)r * (uint32_t)(nkb * 4) + (uint32_t)kb0 * 4u;
+            s_row[f] = (uint32_t)r * (uint32_t)(nkb * 4);
         }
+        // E2M1 scales: the resource ends with the scale array, so a 16-byte load that runs past the
+        // array's end (K below 512, last row) reads zeros there instead of faulting
         __amdgpu_buffer_rsrc_t s_rsrc = b_rsrc;
-        if constexpr (FP4)
-            s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<uint8_t*>(uniform_ptr(args.sbe + ((int64_t)g * N + n0) * nkb * 4)), 0, 0x7FFFFFFF,
-                kBufferFlags);
+        if constexpr (FP4) {
+            const int64_t first = ((int64_t)g * N + n0) * nkb * 4;
+            const int64_t extent = (int64_t)args.G * N * nkb * 4 - first;
+            s_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(uniform_ptr(args.sbe + first)), 0,
+                                                       (int)min(extent, (int64_t)0x7FFFFFFF), kBufferFlags);
+        }
         v8i ring[PF][JN];
-        uint32_t sring[PF][JN];      // E2M1: the 4 E8M0 scale bytes of the row's K block
-        auto issue_b = [&](int kb, v8i (&dst)[JN], uint32_t (&sdst)[JN]) {
+        auto issue_b = [&](int kb, v8i (&dst)[JN]) {
 #pragma unroll
             for (int f = 0; f < JN; ++f) {
                 const uint32_t o = b_off[f] + (uint32_t)kb * KBB;
                 const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, (int)o, 0, 0));
                 if constexpr (FP4) {
                     dst[f] = (v8i){lo.x, lo.y, lo.z, lo.w, 0, 0, 0, 0};
-                    sdst[f] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, (int)(s_off[f] + (uint32_t)kb * 4u), 0, 0);
                 } else {
                     const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, (int)(o + 64), 0, 0));
                     dst[f] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                    sdst[f] = 0;
                 }
             }
+        };
+        // E2M1 scales of 4 consecutive K blocks per fragment row in one 16-byte load (a row's E8M0
+        // bytes are contiguous: 4 per K block), loaded one loop trip ahead: a load whose lanes walk
+        // 16 rows costs the CU's address path as much for 4 bytes as for 16.  The load starts at
+        // block min(a, nkb - 4) so it stays inside the row; sh = a - start moves the words up.
+        constexpr int SV = FP4 ? T::U / 4 : 1;
+        static_assert(!FP4 || T::U % 4 == 0, "E2M1 scale loads cover 4 K blocks of one loop trip");
+        v4u scur[SV][JN], snxt[SV][JN];
+        int shc[SV], shn[SV];
+        auto issue_s = [&](int first, v4u (&dst)[SV][JN], int (&sh)[SV]) {
+#pragma unroll
+            for (int i = 0; i < SV; ++i) {
+                const int a = kb0 + first + 4 * i;
+                const int start = max(0, min(a, nkb - 4));
+                sh[i] = a - start;
+#pragma unroll
+                for (int f = 0; f < JN; ++f)
+                    dst[i][f] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                        s_rsrc, (int)(s_row[f] + (uint32_t)start * 4u), 0, 0));
+            }
+        };
+        // the scale word of trip block u2 (uniform index: selects, no memory)
+        auto scale_word = [&](const v4u& v, int w) -> uint32_t {
+            return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
         };
 
         // ---- A and scales of phase ph (K blocks [ph*KP, ph*KP + tp)): global -> registers, one
@@ -323,10 +348,12 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
         auto kloop = [&](auto ns_c) {
             load_a(ns_c, 0);
             asm volatile("" ::: "memory");
+            if constexpr (FP4) issue_s(0, scur, shc);
 #pragma unroll
-            for (int u2 = 0; u2 < PF - 1; ++u2) issue_b(min(u2, nks - 1), ring[u2], sring[u2]);
+            for (int u2 = 0; u2 < PF - 1; ++u2) issue_b(min(u2, nks - 1), ring[u2]);
             for (int base = 0; base < nks; base += T::U) {
                 // U = lcm(KP, PF) K blocks: every trip starts a phase and a ring cycle
+                if constexpr (FP4) issue_s(base + T::U, snxt, shn);
 #pragma unroll
                 for (int u2 = 0; u2 < T::U; ++u2) {
                     const int kb = base + u2;
@@ -337,11 +364,25 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
                         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
                         load_a(ns_c, kb / KP + 1);
                     }
-                    issue_b(min(kb + PF - 1, nks - 1), ring[(u2 + PF - 1) % PF], sring[(u2 + PF - 1) % PF]);
-                    if (kb < nks) compute(ns_c, kb, ring[u2 % PF], sring[u2 % PF]);
+                    issue_b(min(kb + PF - 1, nks - 1), ring[(u2 + PF - 1) % PF]);
+                    if (kb < nks) {
+                        uint32_t sw[JN];
+#pragma unroll
+                        for (int f = 0; f < JN; ++f)
+                            sw[f] = FP4 ? scale_word(scur[(u2 / 4) % SV][f], u2 % 4 + shc[(u2 / 4) % SV]) : 0u;
+                        compute(ns_c, kb, ring[u2 % PF], sw);
+                    }
                     // keep each K block's LDS reads and MFMAs in its own step: hoisting later blocks'
                     // reads raises register use past what the ring and accumulators need
                     __builtin_amdgcn_sched_barrier(0);
+                }
+                if constexpr (FP4) {
+#pragma unroll
+                    for (int i = 0; i < SV; ++i) {
+                        shc[i] = shn[i];
+#pragma unroll
+                        for (int f = 0; f < JN; ++f) scur[i][f] = snxt[i][f];
+                    }
                 }
             }
         };
