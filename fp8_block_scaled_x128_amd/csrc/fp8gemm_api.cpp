@@ -186,11 +186,13 @@ int pick_split(int64_t tiles, int nkb, int cus) {
 // address K (then the tiled kernel serves the call).
 Choice choose_masked_decode(int64_t N, int nkb, int64_t groups, int cus, bool fp4) {
     const int64_t K = (int64_t)nkb * 128;
-    // short K (few blocks per unit): narrower N tiles, so more units overlap their start-up; an
-    // E2M1 B (half the bytes per K block) takes 256-row N tiles, so the A tile staged per
-    // workgroup serves twice the B bytes
-    Choice c{K <= 2048 ? find_stream(kMasked, 128, 4, 1, 2, 4, fp4)
-                       : find_stream(kMasked, 128, 4, fp4 ? 4 : 2, 2, 4, fp4), 1};
+    // 256-row N tiles (4 fragments per wave), so the A tile staged per workgroup serves as many B
+    // bytes as possible, while the groups times N tiles fill at least half the CUs; else 128-row
+    // tiles, and 64-row tiles for short K (few blocks per unit: more units overlap their start-up)
+    const int64_t tiles256 = groups * ((N + 255) / 256);
+    Choice c{tiles256 * 2 >= cus ? find_stream(kMasked, 128, 4, 4, 2, 4, fp4)
+             : (K <= 2048 ? find_stream(kMasked, 128, 4, 1, 2, 4, fp4) : find_stream(kMasked, 128, 4, 2, 2, 4, fp4)),
+             1};
     if (c.entry < 0) return c;
     const KernelEntry& e = kernels()[c.entry];
     if ((int64_t)std::max(e.bm, e.bn + 1) * K >= (int64_t(1) << 31)) return Choice{-1, 1};
@@ -219,7 +221,10 @@ Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_row
     }
     if (m <= 64) {
         const int64_t t64 = groups * ((N + 63) / 64);
-        if (t64 * 2 >= 3 * cus) c.entry = find_entry(layout, 64, 128, 1, 4, 3);
+        const int64_t K = (int64_t)nkb * 128;
+        // wide N, or long K (each unit re-reads A for its K range: wider tiles halve that;
+        // 64x7168x16384: 27.9 us against 32.3 us with 64x64 tiles)
+        if (t64 * 2 >= 3 * cus || K >= 8192) c.entry = find_entry(layout, 64, 128, 1, 4, 3);
         else c.entry = find_entry(layout, 64, 64, 1, 4, 4);
     } else if (m <= 128) {
         const int64_t K = (int64_t)nkb * 128;

@@ -522,11 +522,12 @@ static KernelEntry stream_entry(const char* name) {
 
 // Masked groups of at most 128 valid rows (one tile per group and N tile, B streamed once per
 // group).  Measured on 16 groups x 256 rows (about 64 valid each), graphs of 3 launches:
-//   N = 4096, K = 7168: 4 waves x 2 fragments, 2-block phases 105 us (4.6 TB/s); 8 waves x 1
-//     fragment 109 us; 4 waves x 1 fragment 127 us; the tiled kernel's 128x128 tile 168 us;
-//     with E2M1 B: 4 waves x 4 fragments 92 us, x 2 fragments 95 us, 8 waves x 1 fragment 95 us;
-//   N = 7168, K = 2048: 4 waves x 1 fragment 66 us (3.8 TB/s); 8 x 1: 65 us; 4 x 2: 64 us.
-// Splitting K was slower everywhere (the groups times N tiles already fill the CUs).
+//   N = 4096, K = 7168: 4 waves x 4 fragments 99 us (4.9 TB/s); x 2 fragments 104 us; 8 waves x 1
+//     fragment 106 us; 4 waves x 1 fragment 126 us; the tiled kernel's 128x128 tile 168 us;
+//     with E2M1 B: 4 waves x 4 fragments 81 us, x 2 fragments 82 us, 8 waves x 1 fragment 84 us;
+//   N = 7168, K = 2048: 4 waves x 4 fragments 60 us (4.2 TB/s); x 2: 64 us; x 1: 66 us.
+// Wider tiles win: the A tile staged per workgroup then serves more B bytes.  Splitting K was
+// slower everywhere (the groups times N tiles already fill the CUs).
 //
 // What bounds these kernels is the vector-memory issue rate of a CU, not HBM: a 16-byte-per-lane
 // load whose lanes walk 16 rows (the MFMA's lane layout: lane l holds row l % 16) occupies the
@@ -538,6 +539,7 @@ const KernelEntry* stream_table(int* count) {
         STREAM_ENTRY(128, 4, 2, 2, 4),
         STREAM_ENTRY(128, 4, 1, 2, 4),
         STREAM_ENTRY(128, 8, 1, 2, 4),
+        STREAM_ENTRY(128, 4, 4, 2, 4),
         // E4M3 x E2M1 (B with one E8M0 scale per 32 K): half the B bytes per K block
         STREAM_ENTRY_FP4(128, 4, 2, 2, 4),
         STREAM_ENTRY_FP4(128, 4, 4, 2, 4),
