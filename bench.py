@@ -450,44 +450,58 @@ def bench_specialized(fg, torch, stream, cases, per, replay, read_flush, reps):
                 per_shape=rows)
 
 
-GROUPED_CALLS = 3      # calls per timed graph of the grouped configurations
+GROUPED_CALLS = 3      # calls per timed graph of the grouped configurations (at least one per copy)
+
+
+ROTATE_BYTES = 600 * 1000 * 1000   # operand copies rotate over more than the 256 MB memory-side cache
+
+
+def copies_for(nbytes, cap=4):
+    """Operand copies so that the copies a graph rotates through exceed the memory-side cache."""
+    return int(min(cap, max(1, -(-ROTATE_BYTES // max(1, nbytes)))))
 
 
 def bench_grouped(fg, W, torch, dev, stream, reps=10):
+    """Grouped configurations 2-4 and configuration 4 with MXFP4 weights: HIP events on the launch
+    stream around a graph of calls after a read-only 1 GiB buffer read, divided by the calls; the
+    calls rotate over operand copies (together over 600 MB), so none reads an operand another
+    call left in the caches."""
     out = {}
     for name, make in (("contiguous_cfg2", W.config2), ("contiguous_cfg3", W.config3),
                        ("masked_cfg4", W.config4), ("masked_fp8xfp4_cfg4", W.config4_fp4)):
         t0 = time.time()
         w = make()
-        A, B, sb = (torch.from_numpy(x).to(dev) for x in (w.A, w.B, w.sb))
-        sa = torch.from_numpy(np.ascontiguousarray(np.swapaxes(w.sa, -1, -2))).to(dev)  # K-block-major
-        N, K = w.B.shape[1], w.B.shape[2]
+        base = dict(A=torch.from_numpy(w.A).to(dev), B=torch.from_numpy(w.B).to(dev),
+                    sb=torch.from_numpy(w.sb).to(dev),
+                    sa=torch.from_numpy(np.ascontiguousarray(np.swapaxes(w.sa, -1, -2))).to(dev))  # K-block-major
+        nbytes = sum(t.numel() * t.element_size() for t in base.values())
+        ncopy = copies_for(nbytes)
+        ops = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(ncopy - 1)]
+        N, K = w.B.shape[1], w.A.shape[-1]
         if name.startswith("contiguous"):
             idx = torch.from_numpy(w.m_indices).to(dev)
-            D = torch.empty((w.A.shape[0], N), dtype=torch.bfloat16, device=dev)
-            call = lambda: fg.grouped_contiguous(A, sa, B, sb, idx, out=D, stream=stream)
+            for o in ops:
+                o["D"] = torch.empty((w.A.shape[0], N), dtype=torch.bfloat16, device=dev)
+            call = lambda o: fg.grouped_contiguous(o["A"], o["sa"], o["B"], o["sb"], idx, out=o["D"], stream=stream)
             counts = [int(np.sum(w.m_indices == g)) for g in range(w.B.shape[0])]
             flop, byts = W.grouped_work(counts, N, K, index_bytes=4 * w.A.shape[0])
-        elif "fp4" in name:
-            K = w.A.shape[2]
-            mm = torch.from_numpy(w.masked_m).to(dev)
-            D = torch.empty((w.A.shape[0], w.A.shape[1], N), dtype=torch.bfloat16, device=dev)
-            call = lambda: fg.fp8fp4_grouped_masked(A, sa, B, sb, mm, w.expected_m, out=D, stream=stream)
-            counts = [int(x) for x in w.masked_m]
-            flop, byts = W.grouped_fp4_work(counts, N, K, index_bytes=4 * len(counts))
         else:
             mm = torch.from_numpy(w.masked_m).to(dev)
-            D = torch.empty((w.A.shape[0], w.A.shape[1], N), dtype=torch.bfloat16, device=dev)
-            call = lambda: fg.grouped_masked(A, sa, B, sb, mm, w.expected_m, out=D, stream=stream)
+            for o in ops:
+                o["D"] = torch.empty((w.A.shape[0], w.A.shape[1], N), dtype=torch.bfloat16, device=dev)
+            f = fg.fp8fp4_grouped_masked if "fp4" in name else fg.grouped_masked
+            call = lambda o, f=f: f(o["A"], o["sa"], o["B"], o["sb"], mm, w.expected_m, out=o["D"], stream=stream)
             counts = [int(x) for x in w.masked_m]
-            flop, byts = W.grouped_work(counts, N, K, index_bytes=4 * len(counts))
+            work = W.grouped_fp4_work if "fp4" in name else W.grouped_work
+            flop, byts = work(counts, N, K, index_bytes=4 * len(counts))
+        calls = max(GROUPED_CALLS, ncopy)
         with torch.cuda.stream(stream):
-            call()
+            call(ops[0])
         cfg = fg.last_config()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for _ in range(GROUPED_CALLS):
-                call()
+            for r in range(calls):
+                call(ops[r % ncopy])
         flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)
         sink = torch.zeros(1, device=dev)
         ts = []
@@ -500,49 +514,63 @@ def bench_grouped(fg, W, torch, dev, stream, reps=10):
                 g.replay()
                 e1.record(stream)
             stream.synchronize()
-            ts.append(e0.elapsed_time(e1) / GROUPED_CALLS)
+            ts.append(e0.elapsed_time(e1) / calls)
         ms = float(np.mean(ts))
         tf = flop / (ms * 1e-3) / 1e12
         gbs = byts / (ms * 1e-3) / 1e9
         out[name] = dict(us=round(ms * 1e3, 1), tflops=round(tf, 1), gbs=round(gbs, 1),
                          frac_mfma=round(tf / PEAK_FP8_TFLOPS, 4), frac_hbm=round(gbs / PEAK_HBM_GBS, 4),
-                         valid_rows=int(sum(counts)), config=cfg)
-        log("%s: %.1f us, %.1f TFLOP/s, %.1f GB/s (%s) [inputs %.1f s]" % (name, ms * 1e3, tf, gbs, cfg,
-                                                                            time.time() - t0))
-        del A, sa, B, sb, D, flush, g
+                         valid_rows=int(sum(counts)), operand_copies=ncopy, config=cfg)
+        log("%s: %.1f us, %.1f TFLOP/s, %.1f GB/s (%s) [%d copies, inputs %.1f s]" % (
+            name, ms * 1e3, tf, gbs, cfg, ncopy, time.time() - t0))
+        del ops, base, flush, g
         torch.cuda.empty_cache()
     return out
 
 
-MOE_CALLS = 4          # calls per timed graph of the MoE legs (the 705 MB of weights exceed the caches)
+MOE_CALLS = 4          # calls per timed graph of the MoE legs (at least one per copy)
 
 
 def bench_moe_chain(fg, W, torch, dev, stream, reps=5):
     """One DeepSeek-V3-sized MoE expert layer on the masked decode configuration's groups (16
     groups, M_max 256, about 64 valid rows each, H = 7168, I = 2048): the first grouped GEMM
     (N = 4096, K = 7168), SwiGLU + requantisation, the second grouped GEMM (N = 7168, K = 2048),
-    through the single chain entry point.  HIP events on the launch stream around a graph of
-    MOE_CALLS chain calls (and of each step alone), after a read-only 1 GiB buffer read, divided by
-    MOE_CALLS; HBM roofline on the algorithmic bytes (both layers' weights dominate)."""
+    through the single chain entry point, and each step alone.  HIP events on the launch stream
+    around a graph of calls after a read-only 1 GiB buffer read, divided by the calls; the calls of
+    a step rotate over copies of its weights and buffers (together over 600 MB, at most 4), so the
+    GEMM steps never read weights another call left in the caches (the SwiGLU step's 34 MB input
+    copies stay below that).  HBM roofline on the algorithmic bytes (both layers' weights dominate)."""
     t0 = time.time()
     e = W.moe_config4()
     G, M_max, H = e.A.shape
     I = e.W2.shape[2]
-    A, W1, s1, W2, s2 = (torch.from_numpy(x).to(dev) for x in (e.A, e.W1, e.s1, e.W2, e.s2))
+    A = torch.from_numpy(e.A).to(dev)
     sa = torch.from_numpy(np.ascontiguousarray(np.swapaxes(e.sa, -1, -2))).to(dev)
     mm = torch.from_numpy(e.masked_m).to(dev)
-    Y1 = torch.empty((G, M_max, 2 * I), dtype=torch.bfloat16, device=dev)
-    Hq = torch.empty((G, M_max, I), dtype=torch.float8_e4m3fn, device=dev)
-    sh = torch.empty((G, I // 128, M_max), dtype=torch.float32, device=dev)
-    out = torch.empty((G, M_max, H), dtype=torch.bfloat16, device=dev)
+    w0 = dict(W1=torch.from_numpy(e.W1).to(dev), s1=torch.from_numpy(e.s1).to(dev),
+              W2=torch.from_numpy(e.W2).to(dev), s2=torch.from_numpy(e.s2).to(dev))
+
+    def buffers():
+        return dict(Y1=torch.empty((G, M_max, 2 * I), dtype=torch.bfloat16, device=dev),
+                    Hq=torch.empty((G, M_max, I), dtype=torch.float8_e4m3fn, device=dev),
+                    sh=torch.empty((G, I // 128, M_max), dtype=torch.float32, device=dev),
+                    out=torch.empty((G, M_max, H), dtype=torch.bfloat16, device=dev))
+
+    nb = lambda *ts: sum(t.numel() * t.element_size() for t in ts)
     counts = [int(x) for x in e.masked_m]
     rows = sum(counts)
-    steps = {
-        "chain": lambda: fg.moe_expert_masked(A, sa, W1, s1, W2, s2, mm, e.expected_m, out=out,
-                                              workspace=(Y1, Hq, sh), stream=stream),
-        "first_layer": lambda: fg.grouped_masked(A, sa, W1, s1, mm, e.expected_m, out=Y1, stream=stream),
-        "swiglu_quantize": lambda: fg.swiglu_quantize_1x128_masked(Y1, mm, codes=Hq, scales=sh, stream=stream),
-        "second_layer": lambda: fg.grouped_masked(Hq, sh, W2, s2, mm, e.expected_m, out=out, stream=stream),
+    steps = {   # name: (bytes one call reads of weights and inputs, call on copy c)
+        "chain": (nb(*w0.values()),
+                  lambda c: fg.moe_expert_masked(A, sa, c["W1"], c["s1"], c["W2"], c["s2"], mm, e.expected_m,
+                                                 out=c["out"], workspace=(c["Y1"], c["Hq"], c["sh"]), stream=stream)),
+        "first_layer": (nb(w0["W1"], w0["s1"]),
+                        lambda c: fg.grouped_masked(A, sa, c["W1"], c["s1"], mm, e.expected_m, out=c["Y1"], stream=stream)),
+        "swiglu_quantize": (W.swiglu_quantize_work(rows, I),
+                            lambda c: fg.swiglu_quantize_1x128_masked(c["Y1"], mm, codes=c["Hq"], scales=c["sh"],
+                                                                      stream=stream)),
+        "second_layer": (nb(w0["W2"], w0["s2"]),
+                         lambda c: fg.grouped_masked(c["Hq"], c["sh"], c["W2"], c["s2"], mm, e.expected_m, out=c["out"],
+                                                     stream=stream)),
     }
     work = {"chain": W.moe_expert_work(counts, H, I, G),
             "first_layer": W.grouped_work(counts, 2 * I, H, index_bytes=4 * G),
@@ -551,15 +579,25 @@ def bench_moe_chain(fg, W, torch, dev, stream, reps=5):
     flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)
     sink = torch.zeros(1, device=dev)
     res = {}
-    for name, call in steps.items():
+    copies = [dict(w0, **buffers())]
+    for name, (nbytes, call) in steps.items():
+        ncopy = copies_for(nbytes)
+        while len(copies) < ncopy:
+            copies.append(dict({k: v.clone() for k, v in w0.items()}, **buffers()))
+        # every copy's buffers hold the previous step's results of that copy (chain order)
         with torch.cuda.stream(stream):
-            call()
+            for c in copies[:ncopy]:
+                steps["chain"][1](c)
+        stream.synchronize()
+        with torch.cuda.stream(stream):
+            call(copies[0])
         stream.synchronize()
         cfg = fg.last_config()
+        calls = max(MOE_CALLS, ncopy)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for _ in range(MOE_CALLS):
-                call()
+            for r in range(calls):
+                call(copies[r % ncopy])
         ts = []
         for _ in range(reps):
             with torch.cuda.stream(stream):
@@ -570,20 +608,20 @@ def bench_moe_chain(fg, W, torch, dev, stream, reps=5):
                 g.replay()
                 e1.record(stream)
             stream.synchronize()
-            ts.append(e0.elapsed_time(e1) / MOE_CALLS)
+            ts.append(e0.elapsed_time(e1) / calls)
         ms = float(np.mean(ts))
         flop, byts = work[name]
         gbs = byts / (ms * 1e-3) / 1e9
         res[name] = dict(us=round(ms * 1e3, 1), bytes=byts, gbs=round(gbs, 1),
-                         frac_hbm=round(gbs / PEAK_HBM_GBS, 4), config=cfg)
+                         frac_hbm=round(gbs / PEAK_HBM_GBS, 4), operand_copies=ncopy, config=cfg)
         if flop:
             res[name]["tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
-        log("moe %s: %.1f us, %.1f GB/s (%s)" % (name, ms * 1e3, gbs, cfg))
+        log("moe %s: %.1f us, %.1f GB/s (%s) [%d copies]" % (name, ms * 1e3, gbs, cfg, ncopy))
         del g
     res["chain"]["valid_rows"] = rows
     res["chain"]["shape"] = "G=%d M_max=%d H=%d I=%d" % (G, M_max, H, I)
     log("moe chain leg done in %.1f s" % (time.time() - t0))
-    del A, W1, s1, W2, s2, sa, mm, Y1, Hq, sh, out, flush
+    del A, sa, mm, w0, copies, flush
     torch.cuda.empty_cache()
     return res
 

@@ -221,10 +221,7 @@ Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_row
     }
     if (m <= 64) {
         const int64_t t64 = groups * ((N + 63) / 64);
-        const int64_t K = (int64_t)nkb * 128;
-        // wide N, or long K (each unit re-reads A for its K range: wider tiles halve that;
-        // 64x7168x16384: 27.9 us against 32.3 us with 64x64 tiles)
-        if (t64 * 2 >= 3 * cus || K >= 8192) c.entry = find_entry(layout, 64, 128, 1, 4, 3);
+        if (t64 * 2 >= 3 * cus) c.entry = find_entry(layout, 64, 128, 1, 4, 3);
         else c.entry = find_entry(layout, 64, 64, 1, 4, 4);
     } else if (m <= 128) {
         const int64_t K = (int64_t)nkb * 128;
