@@ -222,9 +222,13 @@ def main():
     per = []
     total_flop = 0
     kern_time, kern_flop, kern_launch = {}, {}, {}
+    # one untimed pass over every shape first: whichever shape is timed first after the step loop
+    # measures slow (20 against 14 us on 64x2112x7168, 89 against 77 us on 4096x7168x2048)
+    for i in range(len(cases)):
+        read_flush()
+        replay(shape_graphs[i])
+    stream.synchronize()
     for i, case in enumerate(cases):
-        replay(shape_graphs[i])          # untimed: the first replay of a graph pays one-time costs
-        stream.synchronize()
         ts = []
         for _ in range(reps):
             read_flush()
