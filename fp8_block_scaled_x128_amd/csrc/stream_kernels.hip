@@ -1,4 +1,4 @@
-// stream_kernels.hip -- gfx950 kernel of the M-grouped masked FP8 GEMM at decode sizes: each
+// stream_kernels.hip -- gfx950 kernel of the M-grouped masked FP8 (and FP8 x FP4) GEMM at decode sizes: each
 // group holds at most a few hundred rows of which about expected_m are valid, so the time is the
 // stream of every group's B from HBM.
 //
@@ -30,6 +30,15 @@
 // for the two fragment reads (chunks q and 4+q) the 16 lanes the LDS serves together (one
 // half-wave with equal parity of lane bits 2..4, measured on gfx950) hit 16 distinct 16-byte
 // bank groups.
+//
+// The K loop is compiled once per count of active 16-row sub-tiles, so each K block's work is
+// straight-line code over exactly the active sub-tiles, and A's loads cover only their rows.
+//
+// With FP4 = true, B holds E2M1 codes (two per byte) with one E8M0 scale per 32 values of K
+// (OCP MXFP4; page "Perpustakaan operator GPU sumber terbuka DeepSeek DeepGEMM memperbarui versi
+// besar, menambahkan Mega MoE…": FP8 x FP4 GEMM).  A K block of a B row is then 64 bytes, the
+// scales ride in the MFMA's per-lane scale operand, and A's fp32 scale is applied per block as
+// for E4M3.
 //
 // Work units are (M tile, group, N tile of BN = 16*JN*W rows, K split), the M tile outermost so
 // the units of tiles past every group's count (skipped at once) spread evenly over a persistent
