@@ -269,9 +269,9 @@ def main():
     grouped = {}
     if not args.no_grouped:
         del flush
-        grouped = bench_grouped(fg, W, torch, dev, stream)
+        grouped = bench_grouped(fg, W, torch, dev, stream, cpu=not args.no_cpu_baseline)
     quantize = bench_quantize(fg, W, torch, dev, stream)
-    moe = {} if args.no_grouped else bench_moe_chain(fg, W, torch, dev, stream)
+    moe = {} if args.no_grouped else bench_moe_chain(fg, W, torch, dev, stream, cpu=not args.no_cpu_baseline)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -465,7 +465,32 @@ def copies_for(nbytes, cap=4):
     return int(min(cap, max(1, -(-ROTATE_BYTES // max(1, nbytes)))))
 
 
-def bench_grouped(fg, W, torch, dev, stream, reps=10):
+def grouped_oracle_sample(name, w, target_rows=64):
+    """The CPU oracle (as it stands) beside a grouped leg, on a bounded sample of the same
+    workload: the first rows of the first two groups (contiguous: of the first group), all N and
+    K.  Returns the oracle's rate in TFLOP/s."""
+    import oracle
+
+    nth = oracle.num_threads(0)
+    t0 = time.perf_counter()
+    if name.startswith("contiguous"):
+        rows = np.nonzero(w.m_indices == 0)[0][:4 * target_rows]
+        oracle.grouped_contiguous(w.A[rows], w.sa[rows], w.B[:1], w.sb[:1], w.m_indices[rows])
+        flop = 2 * rows.size * w.B.shape[1] * w.A.shape[1]
+        what = "the first %d rows of group 0" % rows.size
+    else:
+        G = 2
+        mm = np.minimum(w.masked_m[:G], target_rows).astype(np.int32)
+        args = (w.A[:G, :target_rows], w.sa[:G, :target_rows], w.B[:G], w.sb[:G], mm)
+        (oracle.grouped_masked_fp4 if "fp4" in name else oracle.grouped_masked)(*args)
+        flop = 2 * int(mm.sum()) * w.B.shape[1] * w.A.shape[2]
+        what = "the first %d valid rows of groups 0 and 1" % int(mm.sum())
+    dt = time.perf_counter() - t0
+    return dict(value=round(flop / dt / 1e12, 6), unit="TFLOP/s", cores=nth, kind="oracle",
+                sample="%s, all N and K: %.2f GFLOP in %.2f s (operand decode included)" % (what, flop / 1e9, dt))
+
+
+def bench_grouped(fg, W, torch, dev, stream, reps=10, cpu=False):
     """Grouped configurations 2-4 and configuration 4 with MXFP4 weights: HIP events on the launch
     stream around a graph of calls after a read-only 1 GiB buffer read, divided by the calls; the
     calls rotate over operand copies (together over 600 MB), so none reads an operand another
@@ -529,6 +554,8 @@ def bench_grouped(fg, W, torch, dev, stream, reps=10):
         out[name] = dict(us=round(ms * 1e3, 1), tflops=round(tf, 1), gbs=round(gbs, 1),
                          frac_mfma=round(tf / PEAK_FP8_TFLOPS, 4), frac_hbm=round(gbs / PEAK_HBM_GBS, 4),
                          valid_rows=int(sum(counts)), operand_copies=ncopy, config=cfg)
+        if cpu:
+            out[name]["cpu_oracle"] = grouped_oracle_sample(name, w)
         log("%s: %.1f us, %.1f TFLOP/s, %.1f GB/s (%s) [%d copies, inputs %.1f s]" % (
             name, ms * 1e3, tf, gbs, cfg, ncopy, time.time() - t0))
         del ops, base, flush, g
@@ -539,7 +566,28 @@ def bench_grouped(fg, W, torch, dev, stream, reps=10):
 MOE_CALLS = 4          # calls per timed graph of the MoE legs (at least one per copy)
 
 
-def bench_moe_chain(fg, W, torch, dev, stream, reps=5):
+def moe_oracle_sample(e, rows_per_group=32, G=2):
+    """The CPU oracle (as it stands) beside the MoE leg: the whole expert layer (first GEMM,
+    SwiGLU + requantisation, second GEMM) for the first valid rows of the first two groups."""
+    import oracle
+
+    nth = oracle.num_threads(0)
+    I = e.W2.shape[2]
+    mm = np.minimum(e.masked_m[:G], rows_per_group).astype(np.int32)
+    r = rows_per_group
+    t0 = time.perf_counter()
+    y, _ = oracle.grouped_masked(e.A[:G, :r], e.sa[:G, :r], e.W1[:G], e.s1[:G], mm)
+    codes, sh, _ = oracle.swiglu_quantize_1x128(y.reshape(G * r, 2 * I))
+    oracle.grouped_masked(codes.reshape(G, r, I), sh.reshape(G, r, -1), e.W2[:G], e.s2[:G], mm)
+    dt = time.perf_counter() - t0
+    H = e.A.shape[2]
+    flop = 2 * int(mm.sum()) * (2 * I * H + H * I)
+    return dict(value=round(flop / dt / 1e12, 6), unit="TFLOP/s", cores=nth, kind="oracle",
+                sample="the expert layer for the first %d valid rows of groups 0 and 1: %.2f GFLOP in %.2f s "
+                       "(operand decode included)" % (int(mm.sum()), flop / 1e9, dt))
+
+
+def bench_moe_chain(fg, W, torch, dev, stream, reps=5, cpu=False):
     """One DeepSeek-V3-sized MoE expert layer on the masked decode configuration's groups (16
     groups, M_max 256, about 64 valid rows each, H = 7168, I = 2048): the first grouped GEMM
     (N = 4096, K = 7168), SwiGLU + requantisation, the second grouped GEMM (N = 7168, K = 2048),
@@ -632,6 +680,8 @@ def bench_moe_chain(fg, W, torch, dev, stream, reps=5):
         del g
     res["chain"]["valid_rows"] = rows
     res["chain"]["shape"] = "G=%d M_max=%d H=%d I=%d" % (G, M_max, H, I)
+    if cpu:
+        res["chain"]["cpu_oracle"] = moe_oracle_sample(e)
     log("moe chain leg done in %.1f s" % (time.time() - t0))
     del A, sa, mm, w0, copies, flush
     torch.cuda.empty_cache()
