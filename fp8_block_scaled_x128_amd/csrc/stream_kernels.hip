@@ -38,7 +38,8 @@
 // (OCP MXFP4; page "Perpustakaan operator GPU sumber terbuka DeepSeek DeepGEMM memperbarui versi
 // besar, menambahkan Mega MoE…": FP8 x FP4 GEMM).  A K block of a B row is then 64 bytes, the
 // scales ride in the MFMA's per-lane scale operand, and A's fp32 scale is applied per block as
-// for E4M3.
+// for E4M3.  B is then loaded two K blocks at a time, so each 128-byte line of a row is read from
+// L2 once.
 //
 // Work units are (M tile, group, N tile of BN = 16*JN*W rows, K split), the M tile outermost so
 // the units of tiles past every group's count (skipped at once) spread evenly over a persistent
@@ -93,6 +94,7 @@ struct Stream {
     static_assert(NBW * KP <= 64, "one x1 DMA moves the tile's B scales of a phase");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(PF >= 2, "at least one K block in flight");
+    static_assert(U % PF == 0, "every loop trip starts a ring cycle");
 };
 
 template <int MT, int W, int JN, int KP, int PF, bool FP4>
@@ -182,18 +184,20 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
             s_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(uniform_ptr(args.sbe + first)), 0,
                                                        (int)min(extent, (int64_t)0x7FFFFFFF), kBufferFlags);
         }
-        v8i ring[PF][JN];
+        // E4M3: one K block per ring slot, its lane chunks q and 4+q.  E2M1: a pair of K blocks
+        // (kb, kb + 1) per slot, lane chunk q of each: the two 64-byte halves of each row's 128-byte
+        // line are requested back to back, so the line crosses from L2 once (requested one K block
+        // apart, the line has left the CU's cache before its second half is read, and every line
+        // crosses twice).  Past the unit's last block the second load repeats the first.
+        v8i ring[FP4 ? PF / 2 : PF][JN];
         auto issue_b = [&](int kb, v8i (&dst)[JN]) {
 #pragma unroll
             for (int f = 0; f < JN; ++f) {
                 const uint32_t o = b_off[f] + (uint32_t)kb * KBB;
+                const uint32_t o2 = FP4 ? (kb + 1 < nks ? o + 64u : o) : o + 64u;
                 const v4i lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, (int)o, 0, 0));
-                if constexpr (FP4) {
-                    dst[f] = (v8i){lo.x, lo.y, lo.z, lo.w, 0, 0, 0, 0};
-                } else {
-                    const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, (int)(o + 64), 0, 0));
-                    dst[f] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                }
+                const v4i hi = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, (int)o2, 0, 0));
+                dst[f] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
             }
         };
         // E2M1 scales of 4 consecutive K blocks per fragment row in one 16-byte load (a row's E8M0
@@ -202,6 +206,7 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
         // block min(a, nkb - 4) so it stays inside the row; sh = a - start moves the words up.
         constexpr int SV = FP4 ? T::U / 4 : 1;
         static_assert(!FP4 || T::U % 4 == 0, "E2M1 scale loads cover 4 K blocks of one loop trip");
+        static_assert(!FP4 || (PF % 2 == 0 && PF >= 4), "E2M1: whole pairs of K blocks, one pair in flight");
         v4u scur[SV][JN], snxt[SV][JN];
         int shc[SV], shn[SV];
         auto issue_s = [&](int first, v4u (&dst)[SV][JN], int (&sh)[SV]) {
@@ -358,8 +363,17 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
             load_a(ns_c, 0);
             asm volatile("" ::: "memory");
             if constexpr (FP4) issue_s(0, scur, shc);
+            // E2M1: PP slots of block pairs, the pair starting at block kb + 2 (PP - 1) issued at
+            // every even block kb into the slot the previous pair used
+            constexpr int PP = PF / 2;
+            const int last_pair = (nks - 1) & ~1;
+            if constexpr (FP4) {
 #pragma unroll
-            for (int u2 = 0; u2 < PF - 1; ++u2) issue_b(min(u2, nks - 1), ring[u2]);
+                for (int p = 0; p < PP - 1; ++p) issue_b(min(2 * p, last_pair), ring[p]);
+            } else {
+#pragma unroll
+                for (int u2 = 0; u2 < PF - 1; ++u2) issue_b(min(u2, nks - 1), ring[u2]);
+            }
             for (int base = 0; base < nks; base += T::U) {
                 // U = lcm(KP, PF) K blocks: every trip starts a phase and a ring cycle
                 if constexpr (FP4) issue_s(base + T::U, snxt, shn);
@@ -373,13 +387,29 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
                         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
                         load_a(ns_c, kb / KP + 1);
                     }
-                    issue_b(min(kb + PF - 1, nks - 1), ring[(u2 + PF - 1) % PF]);
+                    if constexpr (FP4) {
+                        if (u2 % 2 == 0) issue_b(min(kb + 2 * (PP - 1), last_pair), ring[(u2 / 2 + PP - 1) % PP]);
+                    } else {
+                        issue_b(min(kb + PF - 1, nks - 1), ring[(u2 + PF - 1) % PF]);
+                    }
                     if (kb < nks) {
                         uint32_t sw[JN];
 #pragma unroll
                         for (int f = 0; f < JN; ++f)
                             sw[f] = FP4 ? scale_word(scur[(u2 / 4) % SV][f], u2 % 4 + shc[(u2 / 4) % SV]) : 0u;
-                        compute(ns_c, kb, ring[u2 % PF], sw);
+                        if constexpr (FP4) {
+                            // this block's half of the pair in the operand's low four registers
+                            // (the E2M1 operand reads only those)
+                            v8i bsel[JN];
+#pragma unroll
+                            for (int f = 0; f < JN; ++f) {
+                                const v8i x = ring[(u2 / 2) % PP][f];
+                                bsel[f] = (u2 % 2 == 0) ? x : __builtin_shufflevector(x, x, 4, 5, 6, 7, 4, 5, 6, 7);
+                            }
+                            compute(ns_c, kb, bsel, sw);
+                        } else {
+                            compute(ns_c, kb, ring[u2 % PF], sw);
+                        }
                     }
                     // keep each K block's LDS reads and MFMAs in its own step: hoisting later blocks'
                     // reads raises register use past what the ring and accumulators need
