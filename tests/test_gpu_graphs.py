@@ -1,0 +1,137 @@
+"""GPU: every entry point captured in a HIP graph and replayed.
+
+Each call is made once eagerly on a stream into zeroed outputs, then captured on the same stream
+(so its split-K workspace already exists), then the graph is replayed several times.  Between
+replays the outputs are zeroed again by ordinary eager work and the device is synchronised.
+Every replay must reproduce the eager result bit for bit.  The cases include split-K launches
+(whose arrival counters the kernels reset themselves, with no memset node in the graph), the
+masked decode kernel, E2M1 weights, the quantisers and the whole expert layer."""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU runs deselect these with -m "not gpu"
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import fp8_block_scaled_x128_amd as fg  # noqa: E402
+
+REPLAYS = 3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def dev_sa(sa):
+    return dev(np.swapaxes(sa, -1, -2))
+
+
+def bf16_dev(bits):
+    return dev(bits.view(np.int16)).view(torch.bfloat16)
+
+
+def raw(t):
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy().copy()
+
+
+def replay_matches_eager(name, call, outs):
+    """call(stream) writes the tensors in `outs`."""
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call(s)
+    s.synchronize()
+    ref = [raw(t) for t in outs]
+    cfg = fg.last_config()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(s)
+    for r in range(REPLAYS):
+        for t in outs:      # back to the contents before the eager call (rows a call leaves alone stay so)
+            t.view(torch.uint8).zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, t in enumerate(outs):
+            got = raw(t)
+            assert np.array_equal(got, ref[k]), "%s, replay %d, output %d: %d bytes differ (%s)" % (
+                name, r, k, int((got != ref[k]).sum()), cfg)
+    assert fg.read_device_error() == 0
+    del g
+    say("graph", name, cfg)
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (100, 700, 1024), (1024, 512, 512), (300, 1000, 384)])
+def test_dense(M, N, K):
+    d = W.dense(M, N, K, seed=M + N + K)
+    ops = (dev(d.A), dev_sa(d.sa), dev(d.B), dev(d.sb))
+    D = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    replay_matches_eager("dense %dx%dx%d" % (M, N, K), lambda s: fg.gemm_nt(*ops, out=D, stream=s), [D])
+
+
+def test_contiguous():
+    c = W.contiguous([100, 0, 3, 128, 60, 250, 7], 0, 520, 640, seed=31, packed=True)
+    ops = (dev(c.A), dev_sa(c.sa), dev(c.B), dev(c.sb), dev(c.m_indices))
+    D = torch.zeros((c.A.shape[0], 520), dtype=torch.bfloat16, device="cuda")
+    replay_matches_eager("contiguous", lambda s: fg.grouped_contiguous(*ops, out=D, stream=s), [D])
+
+
+@pytest.mark.parametrize("mm,M_max,N,K", [([37, 64], 64, 512, 2048), ([0, 1, 64, 200, 130], 200, 192, 384),
+                                          ([70, 90, 5, 128], 128, 1024, 1024)])
+def test_masked(mm, M_max, N, K):
+    w = W.masked(np.array(mm, np.int32), M_max, N, K, seed=sum(mm) + N)
+    ops = (dev(w.A), dev_sa(w.sa), dev(w.B), dev(w.sb), dev(w.masked_m))
+    D = torch.zeros((len(mm), M_max, N), dtype=torch.bfloat16, device="cuda")
+    replay_matches_eager("masked %s" % mm, lambda s: fg.grouped_masked(*ops, 64, out=D, stream=s), [D])
+
+
+@pytest.mark.parametrize("mm,M_max,N,K", [([32, 20], 32, 160, 512), ([0, 1, 64, 200, 130], 200, 192, 384)])
+def test_fp8fp4_masked(mm, M_max, N, K):
+    w = W.masked_fp4(np.array(mm, np.int32), M_max, N, K, seed=sum(mm) + N + 5)
+    ops = (dev(w.A), dev_sa(w.sa), dev(w.B), dev(w.sb), dev(w.masked_m))
+    D = torch.zeros((len(mm), M_max, N), dtype=torch.bfloat16, device="cuda")
+    replay_matches_eager("fp8xfp4 masked %s" % mm, lambda s: fg.fp8fp4_grouped_masked(*ops, 64, out=D, stream=s),
+                         [D])
+
+
+def test_quantisers():
+    X = bf16_dev(W.activations_bf16(300, 1024, seed=7))
+    codes = torch.zeros((300, 1024), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    scales = torch.zeros((8, 300), dtype=torch.float32, device="cuda")
+    replay_matches_eager("quantize", lambda s: fg.quantize_1x128(X, codes=codes, scales=scales, stream=s),
+                         [codes, scales])
+    G, M_max, K = 3, 40, 512
+    Xm = bf16_dev(W.activations_bf16(G * M_max, K, seed=8).reshape(G, M_max, K))
+    mm = dev(np.array([40, 0, 17], np.int32))
+    cm = torch.zeros((G, M_max, K), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    sm = torch.zeros((G, K // 128, M_max), dtype=torch.float32, device="cuda")
+    replay_matches_eager("quantize masked",
+                         lambda s: fg.quantize_1x128_masked(Xm, mm, codes=cm, scales=sm, stream=s), [cm, sm])
+    Y = bf16_dev(W.swiglu_input_bf16(257, 640, seed=9))
+    cy = torch.zeros((257, 640), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    sy = torch.zeros((5, 257), dtype=torch.float32, device="cuda")
+    replay_matches_eager("swiglu quantize", lambda s: fg.swiglu_quantize_1x128(Y, codes=cy, scales=sy, stream=s),
+                         [cy, sy])
+
+
+def test_moe_expert_chain():
+    mm = np.array([70, 0, 33], np.int32)
+    G, M_max, H, I = 3, 80, 256, 384
+    e = W.moe_expert(mm, M_max, H, I, seed=11, expected_m=64)
+    ops = (dev(e.A), dev_sa(e.sa), dev(e.W1), dev(e.s1), dev(e.W2), dev(e.s2), dev(e.masked_m))
+    out = torch.zeros((G, M_max, H), dtype=torch.bfloat16, device="cuda")
+    ws = (torch.zeros((G, M_max, 2 * I), dtype=torch.bfloat16, device="cuda"),
+          torch.zeros((G, M_max, I), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn),
+          torch.zeros((G, I // 128, M_max), dtype=torch.float32, device="cuda"))
+    replay_matches_eager("moe expert chain",
+                         lambda s: fg.moe_expert_masked(*ops, 64, out=out, workspace=ws, stream=s), [out])
