@@ -151,12 +151,12 @@ def main():
         return
 
     # ---- eager reference outputs and launch configurations ------------------------------------
-    configs = []
+    launch_cfgs = []
     with torch.cuda.stream(stream):
         for case in cases:
             for r in range(COPIES):
                 call(case, r)
-            configs.append(fg.last_config())
+            launch_cfgs.append(fg.last_config())
     stream.synchronize()
     eager = [[c["D"].clone() for c in case["copies"]] for case in cases]
 
@@ -244,14 +244,14 @@ def main():
         total_flop += flop
         tf = flop / (ms * 1e-3) / 1e12
         gbs = byts / (ms * 1e-3) / 1e9
-        kname = configs[i].split(" split=")[0]
+        kname = launch_cfgs[i].split(" split=")[0]
         kern_time[kname] = kern_time.get(kname, 0.0) + ms
         kern_flop[kname] = kern_flop.get(kname, 0) + flop
         kern_launch[kname] = kern_launch.get(kname, 0) + 1
         bound = "mfma" if flop / byts * PEAK_HBM_GBS * 1e9 > PEAK_FP8_TFLOPS * 1e12 else "hbm"
         per.append(dict(M=case["M"], N=case["N"], K=case["K"], us=round(ms * 1e3, 2), tflops=round(tf, 1),
                         gbs=round(gbs, 1), frac_mfma=round(tf / PEAK_FP8_TFLOPS, 4),
-                        frac_hbm=round(gbs / PEAK_HBM_GBS, 4), roof=bound, config=configs[i]))
+                        frac_hbm=round(gbs / PEAK_HBM_GBS, 4), roof=bound, config=launch_cfgs[i]))
     value = total_flop / (ms_per_step * 1e-3) / 1e12
 
     dom = max(kern_time, key=kern_time.get)
