@@ -189,8 +189,10 @@ Choice choose_masked_decode(int64_t N, int nkb, int64_t groups, int cus, bool fp
     // 256-row N tiles (4 fragments per wave), so the A tile staged per workgroup serves as many B
     // bytes as possible, while the groups times N tiles fill at least half the CUs; else 128-row
     // tiles, and 64-row tiles for short K (few blocks per unit: more units overlap their start-up)
+    // (E2M1 B at that width: 128-row tiles, 8 blocks deep -- four slots of block pairs in flight)
     const int64_t tiles256 = groups * ((N + 255) / 256);
-    Choice c{tiles256 * 2 >= cus ? find_stream(kMasked, 128, 4, 4, 2, 4, fp4)
+    const int wide = fp4 ? find_stream(kMasked, 128, 4, 2, 2, 8, true) : find_stream(kMasked, 128, 4, 4, 2, 4, false);
+    Choice c{tiles256 * 2 >= cus ? wide
              : (K <= 2048 ? find_stream(kMasked, 128, 4, 1, 2, 4, fp4) : find_stream(kMasked, 128, 4, 2, 2, 4, fp4)),
              1};
     if (c.entry < 0) return c;
