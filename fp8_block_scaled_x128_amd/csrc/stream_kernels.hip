@@ -564,7 +564,8 @@ static KernelEntry stream_entry(const char* name) {
 //   N = 4096, K = 7168: 4 waves x 4 fragments 99 us (4.9 TB/s); x 2 fragments 104 us; 8 waves x 1
 //     fragment 106 us; 4 waves x 1 fragment 126 us; the tiled kernel's 128x128 tile 168 us;
 //     with E2M1 B (loaded in block pairs; operand copies beyond the memory-side cache): 4 waves x
-//     2 fragments 8 blocks deep 85.0-85.8 us, x 4 fragments 4 deep 87.0-87.2 us;
+//     2 fragments 8 blocks deep 85.0-85.8 us, x 4 fragments 4 deep 87.0-87.2 us; the same 2 x 8 with
+//     E4M3 B: 111.5-111.8 us against 101.7-103.0 us for 4 x 4;
 //   N = 7168, K = 2048: 4 waves x 4 fragments 60 us (4.2 TB/s); x 2: 64 us; x 1: 66 us.
 // Wider tiles win: the A tile staged per workgroup then serves more B bytes.  Splitting K was
 // slower everywhere (the groups times N tiles already fill the CUs).
