@@ -6,8 +6,8 @@ One step = the dense decode/prefill sweep over DeepSeek-V3-like projection shape
 (128x128 fp32 scales).  Inputs are synthetic, seeded, quantised from N(0,1) and resident in HBM
 before timing.
 
-Launch path: each step's 18 library calls are captured once into a HIP graph (the library
-allocates nothing per call, so capture is safe once each stream's workspace exists) and the
+Launch path: each step's 18 library calls are captured once into a HIP graph (the launch
+stream's split-K workspace is created first, by fp8gemm_prepare_stream, and never moves) and the
 graph is replayed; R copies of every operand set rotate between steps and between the launches
 of the per-shape graphs, so no GEMM finds its operands in the 256 MB last-level cache.
 Graph outputs are checked bit for bit against eager calls before timing.
@@ -119,6 +119,7 @@ def main():
     torch.cuda.set_device(dev)
     fg.init()
     stream = torch.cuda.Stream(dev)
+    fg.prepare_stream(stream)           # the split-K workspace, before any capture
 
     # ---- inputs: all 18 sweep cases resident on the device, COPIES copies each -----------------
     t0 = time.time()

@@ -26,7 +26,7 @@ import os
 __all__ = ["gemm_nt", "gemm_nt_specialized", "specialize_nt", "specialized_code_object", "specialized_count",
            "grouped_contiguous", "grouped_masked", "quantize_1x128",
            "quantize_1x128_masked", "fp8fp4_grouped_masked", "swiglu_quantize_1x128", "swiglu_quantize_1x128_masked",
-           "moe_expert_masked", "init", "set_num_cus",
+           "moe_expert_masked", "init", "prepare_stream", "set_num_cus",
            "last_config", "read_device_error", "status_string", "lib", "library_path",
            "Fp8GemmError", "STATUS", "DEVERR_BAD_INDEX", "DEVERR_BAD_COUNT"]
 
@@ -61,6 +61,7 @@ SIGNATURES = {
                                                  _I32, _I64, _I64, _I64, _I64, _P]),
     "fp8gemm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fp8gemm_init": (ctypes.c_int, []),
+    "fp8gemm_prepare_stream": (ctypes.c_int, [_P]),
     "fp8gemm_set_num_cus": (ctypes.c_int, [ctypes.c_int]),
     "fp8gemm_last_config": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_int]),
     "fp8gemm_read_device_error": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32)]),
@@ -103,6 +104,13 @@ def _check(status: int, where: str) -> None:
 
 def init() -> None:
     _check(lib().fp8gemm_init(), "fp8gemm_init")
+
+
+def prepare_stream(stream=None) -> None:
+    """Create the split-K workspace of `stream` (default: torch's current stream) now, so that
+    later calls on it -- HIP graph capture included -- allocate nothing."""
+    torch = _torch()
+    _check(lib().fp8gemm_prepare_stream(_stream(stream, torch.cuda.current_device())), "fp8gemm_prepare_stream")
 
 
 def set_num_cus(n: int) -> None:

@@ -91,35 +91,46 @@ int device_state(DeviceState** out) {
     return FP8GEMM_OK;
 }
 
-// The split-K workspace of `stream`, grown to at least the given sizes.  Counters start at zero
-// and every launch leaves them at zero.
+// Capacity of a stream's split-K workspace.  An automatically chosen split launch has at most one
+// unit per CU (pick_split), and the largest tile compiled with the split-K exchange is 128 x 256
+// fp32, so cus * 128 KiB of partials and one counter per unit cover every such launch.  A forced
+// configuration (FP8GEMM_FORCE_CONFIG) beyond it is refused.
+constexpr size_t kMaxSplitTileBytes = 128 * 256 * sizeof(float);
+size_t workspace_partial_bytes(int cus) { return (size_t)std::max(cus, 1) * kMaxSplitTileBytes; }
+size_t workspace_counters(int cus) { return std::max<size_t>((size_t)cus, 4096); }
+
+// The split-K workspace of `stream`: allocated once, at full capacity, the first time the stream
+// needs one, and never freed or moved afterwards, so a HIP graph captured on the stream keeps
+// valid pointers for the life of the process.  Counters are zeroed at allocation and every
+// launch leaves them at zero.  No allocation is made while the stream is capturing (the stream
+// must be prepared before: fp8gemm_prepare_stream or an earlier split-K call).
 int workspace(DeviceState* d, hipStream_t stream, size_t partial_bytes, size_t counters,
               Workspace** out) {
     std::lock_guard<std::mutex> lock(d->mu);
-    Workspace& w = d->ws[stream];
-    if (w.partial_bytes < partial_bytes) {
-        if (w.partials) {
-            if (hipStreamSynchronize(stream) != hipSuccess) return FP8GEMM_ERR_HIP;
-            hipFree(w.partials);
-        }
-        w.partials = nullptr;
-        w.partial_bytes = 0;
-        size_t bytes = std::max(partial_bytes, (size_t)1 << 22);
+    auto it = d->ws.find(stream);
+    if (it == d->ws.end()) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return FP8GEMM_ERR_HIP;
+        if (cs != hipStreamCaptureStatusNone) return FP8GEMM_ERR_UNSUPPORTED;
+        Workspace w;
+        const size_t bytes = workspace_partial_bytes(d->cus);
+        const size_t n = workspace_counters(d->cus);
         if (hipMalloc(&w.partials, bytes) != hipSuccess) return FP8GEMM_ERR_HIP;
-        w.partial_bytes = bytes;
-    }
-    if (w.counter_count < counters) {
-        if (w.counters) {
-            if (hipStreamSynchronize(stream) != hipSuccess) return FP8GEMM_ERR_HIP;
-            hipFree(w.counters);
+        if (hipMalloc(&w.counters, n * sizeof(int32_t)) != hipSuccess) {
+            hipFree(w.partials);
+            return FP8GEMM_ERR_HIP;
         }
-        w.counters = nullptr;
-        w.counter_count = 0;
-        size_t n = std::max(counters, (size_t)4096);
-        if (hipMalloc(&w.counters, n * sizeof(int32_t)) != hipSuccess) return FP8GEMM_ERR_HIP;
-        if (hipMemset(w.counters, 0, n * sizeof(int32_t)) != hipSuccess) return FP8GEMM_ERR_HIP;
+        if (hipMemset(w.counters, 0, n * sizeof(int32_t)) != hipSuccess) {
+            hipFree(w.partials);
+            hipFree(w.counters);
+            return FP8GEMM_ERR_HIP;
+        }
+        w.partial_bytes = bytes;
         w.counter_count = n;
+        it = d->ws.emplace(stream, w).first;
     }
+    Workspace& w = it->second;
+    if (w.partial_bytes < partial_bytes || w.counter_count < counters) return FP8GEMM_ERR_UNSUPPORTED;
     *out = &w;
     return FP8GEMM_OK;
 }
@@ -327,9 +338,13 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream,
                       a.kb_per_split, (long long)a.units, (long long)grid);
     if (std::getenv("FP8GEMM_LOG")) std::fprintf(stderr, "[fp8gemm] %s\n", g_last_config);
     if (jk) {
-        void* params[] = {&a};
-        if (hipModuleLaunchKernel(jk->fn, (unsigned)grid, 1, 1, (unsigned)e.threads, 1, 1, 0, stream, params,
-                                  nullptr) != hipSuccess)
+        // the argument block travels by value with its size stated: HIP copies the bytes into the
+        // launch (or, under stream capture, into the graph's kernel node) before returning
+        size_t arg_bytes = sizeof(KernelArgs);
+        void* extra[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &a, HIP_LAUNCH_PARAM_BUFFER_SIZE, &arg_bytes,
+                         HIP_LAUNCH_PARAM_END};
+        if (hipModuleLaunchKernel(jk->fn, (unsigned)grid, 1, 1, (unsigned)e.threads, 1, 1, 0, stream, nullptr,
+                                  extra) != hipSuccess)
             return FP8GEMM_ERR_LAUNCH;
         return FP8GEMM_OK;
     }
@@ -658,6 +673,14 @@ const char* fp8gemm_status_string(int status) {
 int fp8gemm_init(void) {
     DeviceState* d = nullptr;
     return device_state(&d);
+}
+
+int fp8gemm_prepare_stream(void* stream) {
+    DeviceState* d = nullptr;
+    int st = device_state(&d);
+    if (st != FP8GEMM_OK) return st;
+    Workspace* w = nullptr;
+    return workspace(d, static_cast<hipStream_t>(stream), 0, 0, &w);
 }
 
 int fp8gemm_set_num_cus(int n) {

@@ -30,11 +30,20 @@
  *     return.  An argument error is reported before anything is enqueued.
  *   - Results are deterministic: the same inputs give the same bits, whatever the launch
  *     configuration's timing (split-K partials are summed in a fixed order).
+ *   - Split-K workspace: each stream has its own library-owned workspace (fp32 partial tiles
+ *     and arrival counters, CUs x 128 KiB + 16 KiB on the stream's device).  It is allocated
+ *     once, at full size, by fp8gemm_prepare_stream or by the first call on the stream whose
+ *     launch splits K (one hipMalloc pair and one blocking hipMemset), and it is never freed,
+ *     moved or regrown, so a HIP graph captured on the stream stays valid for the life of the
+ *     process.  Nothing is allocated while the stream is capturing: a split-K call on a stream
+ *     that has no workspace yet, made during capture, returns FP8GEMM_ERR_UNSUPPORTED; call
+ *     fp8gemm_prepare_stream before capturing (and before any capture starts in the process,
+ *     since the blocking hipMemset must not run while another thread captures).  A graph uses
+ *     the workspace of the stream it was captured on: its replays must not overlap each other
+ *     or calls on that stream.
  *   - Thread safety: calls may come from any host thread.  Calls on different streams may run
- *     concurrently; each stream has its own library-owned split-K workspace, created on first
- *     use of that stream (one hipMalloc; call fp8gemm_init() or make one call per stream before
- *     any HIP graph capture).  fp8gemm_set_num_cus is a global knob, not synchronised with
- *     calls in flight.
+ *     concurrently.  fp8gemm_set_num_cus is a global knob, not synchronised with calls in
+ *     flight.
  *
  * Return value of every int function: a fp8gemm_status code.
  */
@@ -55,7 +64,9 @@ typedef enum fp8gemm_status {
     FP8GEMM_ERR_MISALIGNED = 3,  /* A, B or D not 16-byte aligned, or a scale/index vector not 4-byte aligned */
     FP8GEMM_ERR_UNSUPPORTED = 4, /* a size beyond the supported range (an operand of 2^40 bytes or more, K > 2^24,
                                     2^30 or more output tiles x K splits in one launch, 2^31 or more
-                                    128-value blocks in one quantiser call) */
+                                    128-value blocks in one quantiser call, a forced launch shape whose
+                                    split-K partials exceed the stream's workspace), or a split-K call
+                                    on an unprepared stream during graph capture */
     FP8GEMM_ERR_LAUNCH = 5,      /* the HIP launch failed (hipGetLastError after the launch) */
     FP8GEMM_ERR_HIP = 6          /* a HIP runtime call failed (device query, workspace allocation, copy) */
 } fp8gemm_status;
@@ -181,6 +192,13 @@ const char* fp8gemm_status_string(int status);
 /* Optional eager set-up on the current device: device query and the device error word.  The
  * GEMM calls do it lazily otherwise.  Returns FP8GEMM_ERR_HIP when no device is usable. */
 int fp8gemm_init(void);
+
+/* Create `stream`'s split-K workspace now, on the current device (see "Split-K workspace" above),
+ * so that later calls on the stream, captured in HIP graphs or not, allocate nothing.  Calling it
+ * again for a prepared stream does nothing.  Not while any stream of the process is capturing.
+ * Returns FP8GEMM_ERR_HIP if the allocation fails, FP8GEMM_ERR_UNSUPPORTED if `stream` is
+ * capturing. */
+int fp8gemm_prepare_stream(void* stream);
 
 /* Run-time shape specialisation (the pages' JIT idea: every kernel compiled at run time with
  * the block sizes and stages chosen for the shape, page "DeepSeek開源第三彈…", sections

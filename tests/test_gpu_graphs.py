@@ -135,3 +135,73 @@ def test_moe_expert_chain():
           torch.zeros((G, I // 128, M_max), dtype=torch.float32, device="cuda"))
     replay_matches_eager("moe expert chain",
                          lambda s: fg.moe_expert_masked(*ops, 64, out=out, workspace=ws, stream=s), [out])
+
+
+def test_split_k_graph_survives_a_larger_call():
+    """A split-K call captured on a prepared stream keeps its workspace: a larger split-K call on
+    the same stream afterwards (more and wider partial tiles) neither frees nor moves it, so the
+    graph's replays still give the bits of the first replay, which match the oracle."""
+    import oracle
+    from parity import assert_close, gpu_bits
+
+    s = torch.cuda.Stream()
+    fg.prepare_stream(s)
+    small = W.dense(64, 2112, 7168, seed=501)
+    ops = (dev(small.A), dev_sa(small.sa), dev(small.B), dev(small.sb))
+    D = torch.zeros((64, 2112), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):        # no eager call first: the prepared stream suffices
+        fg.gemm_nt(*ops, out=D, stream=s)
+    cfg_small = fg.last_config()
+    assert "split=1 " not in cfg_small, cfg_small
+    g.replay()
+    torch.cuda.synchronize()
+    ref = raw(D)
+    assert_close(gpu_bits(D), oracle.gemm_nt(small.A, small.sa, small.B, small.sb), what=cfg_small)
+    big = W.dense(128, 7168, 16384, seed=502)
+    with torch.cuda.stream(s):
+        D2 = fg.gemm_nt(dev(big.A), dev_sa(big.sa), dev(big.B), dev(big.sb), stream=s)
+    s.synchronize()
+    cfg_big = fg.last_config()
+    assert "split=1 " not in cfg_big, cfg_big
+    assert_close(gpu_bits(D2), oracle.gemm_nt(big.A, big.sa, big.B, big.sb), what=cfg_big)
+    for r in range(REPLAYS):
+        D.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(raw(D), ref), "replay %d after a larger split-K call (%s, %s)" % (r, cfg_small, cfg_big)
+    del g
+    say("graph survives larger call", cfg_small, "|", cfg_big)
+
+
+def test_split_k_capture_on_unprepared_stream_is_refused():
+    """A split-K call captured on a stream that has no workspace yet returns UNSUPPORTED before
+    anything is enqueued (the library allocates nothing during capture); after
+    fp8gemm_prepare_stream the same capture succeeds."""
+    import ctypes
+
+    hip = ctypes.CDLL("libamdhip64.so")
+    lib = fg.lib()
+    d = W.dense(64, 2112, 1024, seed=503)
+    ops = (dev(d.A), dev_sa(d.sa), dev(d.B), dev(d.sb))
+    D = torch.zeros((64, 2112), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    s = ctypes.c_void_p()
+    assert hip.hipStreamCreate(ctypes.byref(s)) == 0
+    try:
+        def capture():
+            graph = ctypes.c_void_p()
+            assert hip.hipStreamBeginCapture(s, 2) == 0          # relaxed mode
+            rc = lib.fp8gemm_nt(*[t.data_ptr() for t in ops], D.data_ptr(), 64, 2112, 1024, s)
+            assert hip.hipStreamEndCapture(s, ctypes.byref(graph)) == 0
+            assert hip.hipGraphDestroy(graph) == 0
+            return rc
+        assert capture() == 4                                    # FP8GEMM_ERR_UNSUPPORTED
+        assert lib.fp8gemm_prepare_stream(s) == 0
+        assert capture() == 0
+    finally:
+        assert hip.hipStreamSynchronize(s) == 0
+        assert hip.hipStreamDestroy(s) == 0
+    say("unprepared capture refused, prepared capture accepted")
