@@ -276,7 +276,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cases, args.cpu_seconds)
+        cpu = cpu_baseline(cases, eager, args.cpu_seconds)
 
     line = {
         "metric": "FP8 TFLOPS and HBM GB/s per shape (dense, contiguous, masked) on 1 MI355X",
@@ -466,29 +466,35 @@ def copies_for(nbytes, cap=4):
     return int(min(cap, max(1, -(-ROTATE_BYTES // max(1, nbytes)))))
 
 
-def grouped_oracle_sample(name, w, target_rows=64):
+def grouped_oracle_sample(name, w, got, target_rows=64):
     """The CPU oracle (as it stands) beside a grouped leg, on a bounded sample of the same
     workload: the first rows of the first two groups (contiguous: of the first group), all N and
-    K.  Returns the oracle's rate in TFLOP/s."""
+    K.  Returns the oracle's rate in TFLOP/s; the sample's outputs are compared with the GPU's
+    (`got`, the leg's output as bf16 bits), and a mismatch fails the run."""
     import oracle
 
     nth = oracle.num_threads(0)
     t0 = time.perf_counter()
     if name.startswith("contiguous"):
         rows = np.nonzero(w.m_indices == 0)[0][:4 * target_rows]
-        oracle.grouped_contiguous(w.A[rows], w.sa[rows], w.B[:1], w.sb[:1], w.m_indices[rows])
+        ref, _ = oracle.grouped_contiguous(w.A[rows], w.sa[rows], w.B[:1], w.sb[:1], w.m_indices[rows])
         flop = 2 * rows.size * w.B.shape[1] * w.A.shape[1]
         what = "the first %d rows of group 0" % rows.size
+        dt = time.perf_counter() - t0
+        par = check_sample(got[rows], ref, name)
     else:
         G = 2
         mm = np.minimum(w.masked_m[:G], target_rows).astype(np.int32)
         args = (w.A[:G, :target_rows], w.sa[:G, :target_rows], w.B[:G], w.sb[:G], mm)
-        (oracle.grouped_masked_fp4 if "fp4" in name else oracle.grouped_masked)(*args)
+        ref, valid = (oracle.grouped_masked_fp4 if "fp4" in name else oracle.grouped_masked)(*args)
         flop = 2 * int(mm.sum()) * w.B.shape[1] * w.A.shape[2]
         what = "the first %d valid rows of groups 0 and 1" % int(mm.sum())
-    dt = time.perf_counter() - t0
+        dt = time.perf_counter() - t0
+        v = valid.astype(bool)
+        par = check_sample(got[:G, :target_rows][v], ref[v], name)
     return dict(value=round(flop / dt / 1e12, 6), unit="TFLOP/s", cores=nth, kind="oracle",
-                sample="%s, all N and K: %.2f GFLOP in %.2f s (operand decode included)" % (what, flop / 1e9, dt))
+                sample="%s, all N and K: %.2f GFLOP in %.2f s (operand decode included)" % (what, flop / 1e9, dt),
+                parity_vs_gpu=par)
 
 
 def bench_grouped(fg, W, torch, dev, stream, reps=10, cpu=False):
@@ -556,7 +562,8 @@ def bench_grouped(fg, W, torch, dev, stream, reps=10, cpu=False):
                          frac_mfma=round(tf / PEAK_FP8_TFLOPS, 4), frac_hbm=round(gbs / PEAK_HBM_GBS, 4),
                          valid_rows=int(sum(counts)), operand_copies=ncopy, config=cfg)
         if cpu:
-            out[name]["cpu_oracle"] = grouped_oracle_sample(name, w)
+            got = ops[0]["D"].view(torch.int16).cpu().numpy().view(np.uint16)
+            out[name]["cpu_oracle"] = grouped_oracle_sample(name, w, got)
         log("%s: %.1f us, %.1f TFLOP/s, %.1f GB/s (%s) [%d copies, inputs %.1f s]" % (
             name, ms * 1e3, tf, gbs, cfg, ncopy, time.time() - t0))
         del ops, base, flush, g
@@ -784,9 +791,26 @@ def bench_quantize(fg, W, torch, dev, stream, reps=5):
     return out
 
 
-def cpu_baseline(cases, target_s):
+def check_sample(got_bits, ref_bits, what):
+    """GPU outputs against the oracle's on the same outputs: |gpu - ref| <= 2^-7 |ref| +
+    1e-3 rms(ref) per element (rms over the sample).  Raises on a mismatch, so a bench run whose
+    outputs are wrong fails; returns the count, bit-equal share and worst error / tolerance."""
+    f = lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    g, r = f(got_bits).ravel(), f(ref_bits).ravel()
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    lim = 2.0 ** -7 * np.abs(r) + 1e-3 * rms
+    err = np.abs(g - r)
+    bad = int(np.sum(~(err <= lim)))
+    if bad:
+        raise RuntimeError("%s: %d of %d GPU outputs differ from the oracle beyond the tolerance" % (what, bad, r.size))
+    return dict(outputs=int(r.size), bit_equal=round(float(np.mean(g == r)), 6),
+                max_err_over_tolerance=round(float(np.max(err / np.maximum(lim, 1e-300))), 4) if r.size else 0.0)
+
+
+def cpu_baseline(cases, eager, target_s):
     """The CPU oracle (as it stands) on rows 0..r-1 of every sweep case, r sized so the whole
-    sample takes about target_s seconds on this host."""
+    sample takes about target_s seconds on this host; the oracle's rows of the reported sample
+    are compared with the GPU's outputs of the same rows (the run fails on a mismatch)."""
     import oracle
 
     nth = oracle.num_threads(0)
@@ -800,24 +824,33 @@ def cpu_baseline(cases, target_s):
     rows = int(max(1, min(4096, target_s / max(per_row_all, 1e-9))))
 
     def run(rows):
-        flop = 0
+        flop, refs = 0, []
         t0 = time.perf_counter()
         for c in cases:
             r = min(rows, c["M"])
-            oracle.gemm_nt(c["hostA"][:r], c["hostsa"][:r], c["hostB"], c["hostsb"])
+            refs.append(oracle.gemm_nt(c["hostA"][:r], c["hostsa"][:r], c["hostB"], c["hostsb"]))
             flop += 2 * r * c["N"] * c["K"]
-        return flop, time.perf_counter() - t0
+        return flop, time.perf_counter() - t0, refs
 
-    flop, dt = run(rows)
+    flop, dt, refs = run(rows)
     # the probe also pays the per-call decode of B, so the first sample can fall short of the
     # target: resize once from the measured time (the reported sample is the second)
     if dt < 0.6 * target_s and rows < 4096:
         rows = int(max(1, min(4096, rows * target_s / dt)))
-        flop, dt = run(rows)
+        flop, dt, refs = run(rows)
     log("cpu oracle: %d rows of each case, %.1f GFLOP in %.1f s on %d threads" % (rows, flop / 1e9, dt, nth))
+    import torch
+    checked = []
+    for c, ref, outs in zip(cases, refs, eager):
+        got = outs[0][:ref.shape[0]].view(torch.int16).cpu().numpy().view(np.uint16)
+        checked.append(check_sample(got, ref, "%dx%dx%d" % (c["M"], c["N"], c["K"])))
+    n = sum(x["outputs"] for x in checked)
+    parity = dict(outputs=n, bit_equal=round(sum(x["bit_equal"] * x["outputs"] for x in checked) / n, 6),
+                  max_err_over_tolerance=max(x["max_err_over_tolerance"] for x in checked), within_tolerance=True)
+    log("cpu oracle sample vs GPU outputs: %d outputs within tolerance, %.4f bit-equal" % (n, parity["bit_equal"]))
     return dict(value=round(flop / dt / 1e12, 6), unit="TFLOP/s", cores=nth, kind="oracle",
                 sample="first %d rows (at most M) of each of the 18 sweep GEMMs, all N and K: %.1f GFLOP in %.1f s"
-                       % (rows, flop / 1e9, dt))
+                       % (rows, flop / 1e9, dt), parity_vs_gpu=parity)
 
 
 if __name__ == "__main__":

@@ -49,3 +49,53 @@ def assert_bit_exact(got_bits, ref_bits, mask=None, what=""):
     r = ref_bits if mask is None else ref_bits[mask]
     neq = int(np.sum(g != r))
     assert neq == 0, "%s: %d of %d outputs differ in bits" % (what, neq, r.size)
+
+
+# ---- full-output reports ---------------------------------------------------------------------
+
+ULP_BUCKETS = ((0, 0, "0"), (1, 1, "1"), (2, 2, "2"), (3, 3, "3"), (4, 7, "4-7"), (8, 15, "8-15"),
+               (16, 1 << 30, "16+"))
+
+
+def ulp_distance(got_bits: np.ndarray, ref_bits: np.ndarray) -> np.ndarray:
+    """Distance in bf16 units in the last place between finite bf16 bit patterns: the patterns
+    mapped to a monotonic integer line (sign-magnitude to two's complement, +0 and -0 both 0)."""
+    def line(b):
+        b = np.asarray(b, dtype=np.uint16).astype(np.int32)
+        mag = b & 0x7FFF
+        return np.where(b & 0x8000, -mag, mag)
+    return np.abs(line(got_bits) - line(ref_bits))
+
+
+def full_report(got_bits, ref_bits, mask=None) -> dict:
+    """Over every valid output (mask; all if None): count, share of bit-equal outputs, the bf16
+    ulp-distance histogram, the worst error as a fraction of the tolerance and rms(ref)."""
+    g = got_bits if mask is None else got_bits[mask]
+    r = ref_bits if mask is None else ref_bits[mask]
+    ok, rep = within_tolerance(g, r)
+    d = ulp_distance(g, r)
+    rep["ulp_histogram"] = {name: int(np.sum((d >= lo) & (d <= hi))) for lo, hi, name in ULP_BUCKETS}
+    rep["within_tolerance"] = ok
+    return rep
+
+
+def record(name: str, rep: dict) -> None:
+    """Print a full-output report; with FP8GEMM_PARITY_REPORT=<path> also append it there as a
+    JSON line (for the design notes)."""
+    import json
+    import os
+    line = dict(case=name, **rep)
+    print("parity", json.dumps(line), flush=True)
+    path = os.environ.get("FP8GEMM_PARITY_REPORT")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(line) + "\n")
+
+
+def assert_close_full(got_bits, ref_bits, mask=None, what=""):
+    """assert_close over every valid output of a call (rms over all of them), and record the
+    full-output report."""
+    rep = full_report(got_bits, ref_bits, mask)
+    record(what, rep)
+    assert rep["within_tolerance"], "%s: %s" % (what, rep)
+    return rep

@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import workloads as W
-from parity import assert_close, gpu_bits
+from parity import assert_close, assert_close_full, gpu_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -191,26 +191,20 @@ def test_fp4_argument_errors():
 
 
 @pytest.mark.slow
-def test_fp4_config4_full_size_sampled():
+def test_fp4_config4_full_size():
     """The masked decode workload (16 groups x 256 rows, Poisson(64) counts, N=4096, K=7168) with
-    MXFP4 weights, at full size in the launch shape the benchmark times.  Each output depends only
-    on its row of A and its row of B, so the oracle runs on 3 groups' sampled rows and columns."""
+    MXFP4 weights, at full size in the launch shape the benchmark times: every valid output
+    against the oracle (rms over all of them)."""
     say("fp4 config 4")
     w = W.config4_fp4()
     G, M_max, K = w.A.shape
     N = w.B.shape[1]
     D = run(w, w.expected_m, out=sentinel_tensor((G, M_max, N)))
+    lc = fg.last_config()
     got = gpu_bits(D)
     v = valid_mask(w, N)
     assert np.all(got[~v] == SENTINEL)
     assert fg.read_device_error() == 0
-    rng = np.random.default_rng(4)
-    for g in rng.choice(G, 3, replace=False):
-        c = int(w.masked_m[g])
-        rows = np.unique(np.concatenate([[0, c - 1], rng.integers(0, c, 30)]))
-        cols = np.unique(np.concatenate([np.arange(64), np.arange(N - 64, N), rng.integers(0, N, 128)]))
-        sub = W.MaskedFp4(w.A[g:g + 1, rows], w.sa[g:g + 1, rows], w.B[g:g + 1, cols], w.sb[g:g + 1, cols],
-                          np.array([rows.size], np.int32), 0)
-        ref, _ = oracle.grouped_masked_fp4(sub.A, sub.sa, sub.B, sub.sb, sub.masked_m)
-        rep = assert_close(got[g][np.ix_(rows, cols)], ref[0], what="config 4 fp4 group %d" % g)
-        say("fp4 config 4 group", g, fg.last_config(), rep["bit_equal"])
+    ref, _ = oracle.grouped_masked_fp4(w.A, w.sa, w.B, w.sb, w.masked_m)
+    rep = assert_close_full(got, ref, mask=v, what="masked fp8xfp4 config 4 [%s]" % lc)
+    say("fp4 config 4", lc, rep["bit_equal"], rep["ulp_histogram"])

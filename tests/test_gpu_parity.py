@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import workloads as W
-from parity import assert_bit_exact, assert_close, gpu_bits
+from parity import assert_bit_exact, assert_close, assert_close_full, gpu_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -425,90 +425,63 @@ def test_masked_count_out_of_range_clamps_and_flags():
 
 
 # ------------------------------------------------------------------------------------------
-# full-size workloads: sampled outputs
+# full-size workloads: every valid output against the oracle
 # ------------------------------------------------------------------------------------------
-
-def sample_positions(rng, rows, N, n_random=3000):
-    r = [0, rows - 1] + list(rng.integers(0, rows, 6))
-    rr, cc = [], []
-    for x in r:
-        cols = np.unique(np.concatenate([np.arange(min(64, N)), np.arange(max(0, N - 64), N),
-                                         rng.integers(0, N, 64)]))
-        rr.append(np.full(cols.size, x))
-        cc.append(cols)
-    rr.append(rng.integers(0, rows, n_random))
-    cc.append(rng.integers(0, N, n_random))
-    return np.concatenate(rr).astype(np.int64), np.concatenate(cc).astype(np.int64)
-
-
-def check_sampled_dense(d, D, seed):
-    M, N, K = d.shape
-    rng = np.random.default_rng(seed)
-    r, c = sample_positions(rng, M, N)
-    ref = oracle.elements(d.A, d.sa, d.B, d.sb, r, c, c // 128)
-    got = gpu_bits(D)
-    gs = got[r, c]
-    full = oracle.bf16_bits_to_float(got)
-    assert np.all(np.isfinite(full)), "non-finite outputs"
-    return assert_close(gs, ref, what="sampled %dx%dx%d" % (M, N, K))
+# Each call runs in the launch configuration the benchmark times (the library's own choice).
+# rms(ref) in the tolerance is taken over all valid outputs of the call; each test records the
+# share of bit-equal outputs and the bf16 ulp-distance histogram (printed; appended as a JSON
+# line to $FP8GEMM_PARITY_REPORT when set).
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("mi", range(len(W.SWEEP_M)))
 @pytest.mark.parametrize("nki", range(len(W.SWEEP_NK)))
-def test_sweep_full_size_sampled(mi, nki):
+def test_sweep_full_size(mi, nki):
     M, (N, K) = W.SWEEP_M[mi], W.SWEEP_NK[nki]
     say("sweep case", M, N, K)
     d = W.sweep_case(mi, nki)
     D = run_dense(d)
-    rep = check_sampled_dense(d, D, seed=mi * 10 + nki)
-    say("sweep", M, N, K, fg.last_config(), rep["bit_equal"])
-
-
-def check_sampled_grouped(A, sa, B, sb, D_bits, rows_valid, rows_group, N, seed, what):
-    """rows_valid: flattened row ids (into A/sa/D) with their group rows_group."""
-    rng = np.random.default_rng(seed)
-    K = A.shape[-1]
-    nkb, nnb = K // 128, (N + 127) // 128
-    pick = rng.integers(0, rows_valid.size, 4000)
-    r = rows_valid[pick]
-    g = rows_group[pick]
-    c = rng.integers(0, N, pick.size)
-    ref = oracle.elements(A.reshape(-1, K), sa.reshape(-1, nkb), B.reshape(-1, K), sb.reshape(-1, nkb),
-                          r, g * N + c, g * nnb + c // 128)
-    return assert_close(D_bits.reshape(-1, N)[r, c], ref, what=what)
+    cfg = fg.last_config()
+    got = gpu_bits(D)
+    ref = oracle.gemm_nt(d.A, d.sa, d.B, d.sb)
+    rep = assert_close_full(got, ref, what="sweep %dx%dx%d [%s]" % (M, N, K, cfg))
+    say("sweep", M, N, K, cfg, rep["bit_equal"], rep["ulp_histogram"])
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("cfg", [2, 3])
-def test_contiguous_configs_full_size_sampled(cfg):
+def test_contiguous_configs_full_size(cfg):
     say("contiguous config", cfg)
     c = W.config2() if cfg == 2 else W.config3()
     N = c.B.shape[1]
     out = sentinel_tensor((c.A.shape[0], N))
     D = run_contig(c, out=out)
+    lc = fg.last_config()
     got = gpu_bits(D)
     valid = c.m_indices >= 0
     assert np.all(got[~valid] == SENTINEL)
-    rows = np.nonzero(valid)[0]
-    rep = check_sampled_grouped(c.A, c.sa, c.B, c.sb, got, rows, c.m_indices[rows], N, cfg,
-                                "config %d" % cfg)
     assert fg.read_device_error() == 0
-    say("contiguous config", cfg, fg.last_config(), rep["bit_equal"])
+    ref, v = oracle.grouped_contiguous(c.A, c.sa, c.B, c.sb, c.m_indices)
+    assert np.array_equal(v.astype(bool), valid)
+    rep = assert_close_full(got, ref, mask=np.broadcast_to(valid[:, None], got.shape),
+                            what="contiguous config %d [%s]" % (cfg, lc))
+    say("contiguous config", cfg, lc, rep["bit_equal"], rep["ulp_histogram"])
 
 
 @pytest.mark.slow
-def test_masked_config4_full_size_sampled():
+def test_masked_config4_full_size():
     say("masked config 4")
     w = W.config4()
     G, M_max, K = w.A.shape
     N = w.B.shape[1]
     out = sentinel_tensor((G, M_max, N))
     D = run_masked(w, w.expected_m, out=out)
+    lc = fg.last_config()
     got = gpu_bits(D)
     valid = np.arange(M_max)[None, :] < w.masked_m[:, None]
-    assert np.all(got[~valid] == SENTINEL)
-    gi, ri = np.nonzero(valid)
-    rep = check_sampled_grouped(w.A, w.sa, w.B, w.sb, got, gi * M_max + ri, gi, N, 4, "config 4")
+    v = np.broadcast_to(valid[:, :, None], got.shape)
+    assert np.all(got[~v] == SENTINEL)
     assert fg.read_device_error() == 0
-    say("masked config 4", fg.last_config(), rep["bit_equal"])
+    ref, _ = oracle.grouped_masked(w.A, w.sa, w.B, w.sb, w.masked_m)
+    rep = assert_close_full(got, ref, mask=v, what="masked config 4 [%s]" % lc)
+    say("masked config 4", lc, rep["bit_equal"], rep["ulp_histogram"])
