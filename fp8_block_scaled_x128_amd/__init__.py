@@ -23,7 +23,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gemm_nt", "gemm_nt_specialized", "specialize_nt", "specialized_code_object", "specialized_count",
+__all__ = ["gemm_nt", "gemm_nt_noalloc", "gemm_nt_specialized", "specialize_nt", "specialized_code_object", "specialized_count",
            "grouped_contiguous", "grouped_masked", "quantize_1x128",
            "quantize_1x128_masked", "fp8fp4_grouped_masked", "swiglu_quantize_1x128", "swiglu_quantize_1x128_masked",
            "moe_expert_masked", "init", "prepare_stream", "set_num_cus",
@@ -44,6 +44,7 @@ DEVERR_BAD_COUNT = 2
 _P, _I64, _I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
 SIGNATURES = {
     "fp8gemm_nt": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "fp8gemm_nt_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "fp8gemm_nt_specialized": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "fp8gemm_specialize_nt": (ctypes.c_int, [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_double)]),
     "fp8gemm_specialized_code_object": (ctypes.c_int, [ctypes.c_int] * 6 + [_I64, _I64, _P,
@@ -193,6 +194,13 @@ def _shape_check(cond, msg):
 def gemm_nt(A, sa, B, sb, out=None, stream=None):
     """D[M,N] (bf16) = A[M,K] . B[N,K]^T with sa [K/128, M] and sb [ceil(N/128), K/128]."""
     return _dense("fp8gemm_nt", A, sa, B, sb, out, stream)
+
+
+def gemm_nt_noalloc(A, sa, B, sb, out=None, stream=None):
+    """gemm_nt with its split-K partials in the library's static device scratch: the library
+    allocates nothing (pass `out`, so that this wrapper does not allocate either).  Calls that
+    overlap in time on one GPU race on the scratch."""
+    return _dense("fp8gemm_nt_noalloc", A, sa, B, sb, out, stream)
 
 
 def gemm_nt_specialized(A, sa, B, sb, out=None, stream=None):

@@ -39,7 +39,8 @@ struct DeviceState {
     bool ready = false;
     int id = 0;
     int cus = 0;
-    int32_t* err = nullptr;                              // device error word
+    int32_t* err = nullptr;                              // device error word (static device memory)
+    ScratchPointers scratch;                             // static split-K scratch of fp8gemm_nt_noalloc
     std::vector<int> occupancy;                          // per kernel-table entry
     std::unordered_map<hipStream_t, Workspace> ws;       // split-K workspace per stream
 };
@@ -62,7 +63,8 @@ const std::vector<KernelEntry>& kernels() {
 std::atomic<int> g_cu_cap{0};
 thread_local char g_last_config[256] = "";
 
-// Query the device once: CU count, occupancy of every kernel, device error word.
+// Query the device once: CU count, occupancy of every kernel, the device addresses of the
+// static error word and scratch.  Allocates nothing.
 int device_state(DeviceState** out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8GEMM_ERR_HIP;
@@ -81,10 +83,10 @@ int device_state(DeviceState** out) {
                     hipSuccess && blocks > 0)
                 d.occupancy[i] = blocks;
         }
-        void* e = nullptr;
-        if (hipMalloc(&e, 256) != hipSuccess) return FP8GEMM_ERR_HIP;
-        if (hipMemset(e, 0, 256) != hipSuccess) return FP8GEMM_ERR_HIP;
-        d.err = static_cast<int32_t*>(e);
+        // the error word and the no-allocation scratch are static device arrays: their device
+        // addresses on this device (nothing is allocated; both are zero from the code object's load)
+        if (scratch_pointers(&d.scratch) != 0) return FP8GEMM_ERR_HIP;
+        d.err = d.scratch.err;
         d.ready = true;
     }
     *out = &d;
@@ -271,8 +273,10 @@ Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_row
 
 // specialize: run the tiled kernel compiled at run time with this call's N and K (the launch
 // shape is the table's choice either way).
+// noalloc: split-K partials and counters in the device's static scratch (fp8gemm_nt_noalloc)
+// instead of the stream's workspace; launches that need more than it holds are refused.
 int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream, bool fp4 = false,
-           bool specialize = false) {
+           bool specialize = false, bool noalloc = false) {
     DeviceState* d = nullptr;
     int st = device_state(&d);
     if (st != FP8GEMM_OK) return st;
@@ -315,11 +319,19 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream,
     a.counters = nullptr;
     if (a.splits > 1) {
         const int64_t tiles = (int64_t)a.units / a.splits;
-        Workspace* w = nullptr;
-        st = workspace(d, stream, (size_t)a.units * e.bm * e.bn * sizeof(float), (size_t)tiles, &w);
-        if (st != FP8GEMM_OK) return st;
-        a.ws = w->partials;
-        a.counters = w->counters;
+        const size_t partial_bytes = (size_t)a.units * e.bm * e.bn * sizeof(float);
+        if (noalloc) {
+            if (partial_bytes > kScratchPartialBytes || (size_t)tiles > kScratchCounters)
+                return FP8GEMM_ERR_UNSUPPORTED;
+            a.ws = d->scratch.partials;
+            a.counters = d->scratch.counters;
+        } else {
+            Workspace* w = nullptr;
+            st = workspace(d, stream, partial_bytes, (size_t)tiles, &w);
+            if (st != FP8GEMM_OK) return st;
+            a.ws = w->partials;
+            a.counters = w->counters;
+        }
     }
     int64_t slots = (int64_t)cus * (jk ? jk->occupancy : d->occupancy[c.entry]);
     int64_t grid = std::min<int64_t>(a.units, slots);
@@ -409,7 +421,7 @@ int quantize(const void* X, void* A, float* sa, const int32_t* masked_m, int32_t
 
 // Dense NT GEMM, from the table's kernel or its run-time specialisation.
 int dense(const void* A, const float* sa, const void* B, const float* sb, void* D, int64_t M, int64_t N,
-          int64_t K, void* stream, bool specialize) {
+          int64_t K, void* stream, bool specialize, bool noalloc = false) {
     if (M < 0 || N < 0) return FP8GEMM_ERR_BAD_SHAPE;
     int st = check_k(K);
     if (st != FP8GEMM_OK) return st;
@@ -430,7 +442,7 @@ int dense(const void* A, const float* sa, const void* B, const float* sb, void* 
     a.G = 1;
     a.nkb = (int32_t)(K / 128);
     a.nnb = (int32_t)((N + 127) / 128);
-    return launch(kDense, a, M, static_cast<hipStream_t>(stream), false, specialize);
+    return launch(kDense, a, M, static_cast<hipStream_t>(stream), false, specialize, noalloc);
 }
 
 }  // namespace
@@ -516,6 +528,11 @@ int fp8gemm_moe_expert_masked(const void* A, const float* sa, const void* W1, co
 int fp8gemm_nt(const void* A, const float* sa, const void* B, const float* sb, void* D, int64_t M,
                int64_t N, int64_t K, void* stream) {
     return dense(A, sa, B, sb, D, M, N, K, stream, false);
+}
+
+int fp8gemm_nt_noalloc(const void* A, const float* sa, const void* B, const float* sb, void* D, int64_t M,
+                       int64_t N, int64_t K, void* stream) {
+    return dense(A, sa, B, sb, D, M, N, K, stream, false, true);
 }
 
 int fp8gemm_nt_specialized(const void* A, const float* sa, const void* B, const float* sb, void* D, int64_t M,

@@ -36,6 +36,22 @@ struct KernelEntry {
 const KernelEntry* kernel_table(int* count);
 const KernelEntry* stream_table(int* count);
 
+// Static device scratch of the allocation-free dense entry point (scratch.hip): fp32 split-K
+// partial tiles and int32 arrival counters.  16 MiB of partials hold every automatically chosen
+// dense split launch on up to 256 CUs (at most one unit per CU, tiles of at most 128 x 128 fp32);
+// larger needs are refused.
+constexpr size_t kScratchPartialBytes = size_t(16) << 20;
+constexpr size_t kScratchCounters = 4096;
+
+struct ScratchPointers {
+    float* partials = nullptr;
+    int32_t* counters = nullptr;
+    int32_t* err = nullptr;     // the device error word (static as well)
+};
+
+// Device addresses of the static arrays on the current device (hipGetSymbolAddress); 0 on success.
+int scratch_pointers(ScratchPointers* out);
+
 // Tiled kernel of a table entry with N and K fixed at compile time, built at run time
 // (fp8gemm_jit.cpp).
 struct JitKernel {

@@ -77,6 +77,21 @@ typedef enum fp8gemm_status {
 int fp8gemm_nt(const void* A, const float* sa, const void* B, const float* sb, void* D,
                int64_t M, int64_t N, int64_t K, void* stream);
 
+/* fp8gemm_nt for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The same operation, arguments,
+ * validation, launch shape and results (bit for bit) as fp8gemm_nt, but the split-K partial tiles
+ * and arrival counters live in a static device array of the library (16 MiB of fp32 partials and
+ * 4096 counters per GPU, held until the process ends) instead of a per-stream workspace, and the
+ * call allocates nothing, ever, and never synchronises.  A launch whose partials or tiles exceed
+ * that array returns FP8GEMM_ERR_UNSUPPORTED before enqueueing anything; every automatically
+ * chosen dense launch on up to 256 CUs fits.  All calls of this entry point on one GPU share the
+ * array: calls whose kernels overlap in time on the same GPU (on different streams, or graphs
+ * replayed concurrently) race on it and give unspecified results; serialise them.  The arrival
+ * counters start at zero when the library's code object is loaded and every launch leaves them
+ * at zero; the partials are written before they are read. */
+int fp8gemm_nt_noalloc(const void* A, const float* sa, const void* B, const float* sb, void* D,
+                       int64_t M, int64_t N, int64_t K, void* stream);
+
 /* M-grouped GEMM, contiguous layout, m_grouped_gemm_fp8_fp8_bf16_nt_contiguous (same page and
  * section; page "DeepGEMM：AI計算の経済性を…", section DeepGEMMが重要な理由: token sequences are
  * grouped per expert).  The rows of all groups are concatenated along M:
