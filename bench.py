@@ -59,10 +59,12 @@ def parse():
     p.add_argument("--no-grouped", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU-oracle sample time")
     p.add_argument("--counters", action="store_true",
-                   help="launch each M=4096 sweep GEMM and a 1 GiB copy a few times, eagerly (run under "
-                        "rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)")
-    p.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                   help="turn the two rocprofv3 --pmc output folders of a --counters run into " + TRAFFIC_FILE)
+                   help="launch every kernel the benchmark times (the 18 sweep GEMMs, the grouped "
+                        "configurations, the quantiser) COUNTER_REPS times each, eagerly, then a 1 GiB copy "
+                        "(run under rocprofv3 --pmc, one pass per counter group)")
+    p.add_argument("--counter-summary", nargs="+", metavar="PASS_DIR",
+                   help="turn the rocprofv3 --pmc output folders of --counters runs (one per pass) into "
+                        "the per-family summaries profiles/counters_*.txt and " + TRAFFIC_FILE)
     return p.parse_args()
 
 
@@ -101,8 +103,8 @@ def read_traffic():
 
 def main():
     args = parse()
-    if args.traffic_summary:
-        traffic_summary(*args.traffic_summary)
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)"
@@ -265,6 +267,7 @@ def main():
                     flop_per_launch=kern_flop[dom] // kern_launch[dom],
                     share_of_step=round(kern_time[dom] / sum(kern_time.values()), 3))
 
+    read_floor = bench_read_floor(torch, dev, stream, per, read_flush, reps)
     specialized = bench_specialized(fg, torch, stream, cases, per, replay, read_flush, reps)
 
     grouped = {}
@@ -304,41 +307,98 @@ def main():
         "quantize_1x128": quantize,
         "moe_expert_chain": moe,
         "specialized": specialized,
+        "read_floor": read_floor,
     }
     print(json.dumps(line), flush=True)
 
 
 COUNTER_REPS = 3
+# kernels of the library, as rocprofv3 names their dispatches
+LIB_KERNELS = ("fp8gemm_kernel", "fp8gemm_masked_decode_kernel", "quantize_1x128_kernel")
+
+
+def counter_legs():
+    """(label, family, flop, bytes) of every leg of a --counters run, in launch order: the 18 sweep
+    GEMMs, the grouped configurations 2, 3, 4 and 4 with MXFP4 weights, the activation quantiser
+    (32768 x 7168).  Each leg is launched COUNTER_REPS times."""
+    import workloads as W
+    legs = []
+    for M in W.SWEEP_M:
+        for N, K in W.SWEEP_NK:
+            flop, byts = W.dense_work(M, N, K)
+            legs.append(("dense %dx%dx%d" % (M, N, K), "dense_decode" if M <= 128 else "dense_prefill", flop, byts))
+    c2 = [7782] * 4
+    legs.append(("contiguous cfg2 4x8192 N=4096 K=7168", "grouped") + W.grouped_work(c2, 4096, 7168, 4 * 32768))
+    c3 = W.config3_counts()
+    legs.append(("contiguous cfg3 8x4096 N=7168 K=2048", "grouped") + W.grouped_work(c3, 7168, 2048, 4 * 32768))
+    c4 = [int(x) for x in W.config4_masked_m()]
+    legs.append(("masked cfg4 16x256 N=4096 K=7168", "grouped") + W.grouped_work(c4, 4096, 7168, 4 * 16))
+    legs.append(("masked fp8xfp4 cfg4 16x256 N=4096 K=7168", "grouped") +
+                W.grouped_fp4_work(c4, 4096, 7168, 4 * 16))
+    legs.append(("quantize_1x128 32768x7168", "quantize", 0, W.quantize_work(W.QUANT_M, W.QUANT_K)))
+    return legs
 
 
 def counters_run(fg, W, torch, dev, stream, cases, call):
-    """Eager launches for hardware-counter passes: every M=4096 sweep GEMM (the 256x256 kernel)
-    COUNTER_REPS times after a read-only cache flush, then an elementwise copy (dst = src + 0) of
-    COPY_BYTES COUNTER_REPS times.  Prints the launch order."""
+    """Eager launches for hardware-counter passes: every leg of counter_legs() COUNTER_REPS times,
+    each after a read-only cache flush (a reduction), then an elementwise copy (dst = src + 0) of
+    COPY_BYTES COUNTER_REPS times, the calibration of the traffic counters.  Prints the launch
+    order with each launch's configuration."""
     flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)
     sink = torch.zeros((), device=dev)
-    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    torch.cuda.synchronize()
     order = []
+
+    def run(label, f):
+        for r in range(COUNTER_REPS):
+            torch.sum(flush, dim=0, out=sink)   # read-only flush: a reduction, no elementwise kernel
+            f(r)
+            order.append((label, fg.last_config()))
+
     with torch.cuda.stream(stream):
         for case in cases:
-            if case["M"] != 4096:
-                continue
-            for r in range(COUNTER_REPS):
-                torch.sum(flush, dim=0, out=sink)   # read-only flush: a reduction, no elementwise kernel
-                call(case, r % COPIES)
-                order.append("gemm %d %d %d" % (case["M"], case["N"], case["K"]))
+            run("dense %dx%dx%d" % (case["M"], case["N"], case["K"]), lambda r, case=case: call(case, r % COPIES))
+    stream.synchronize()
+    for label, make in (("contiguous cfg2 4x8192 N=4096 K=7168", W.config2),
+                        ("contiguous cfg3 8x4096 N=7168 K=2048", W.config3),
+                        ("masked cfg4 16x256 N=4096 K=7168", W.config4),
+                        ("masked fp8xfp4 cfg4 16x256 N=4096 K=7168", W.config4_fp4)):
+        w = make()
+        A, B, sb = (torch.from_numpy(x).to(dev) for x in (w.A, w.B, w.sb))
+        sa = torch.from_numpy(np.ascontiguousarray(np.swapaxes(w.sa, -1, -2))).to(dev)
+        N = w.B.shape[1]
+        with torch.cuda.stream(stream):
+            if label.startswith("contiguous"):
+                idx = torch.from_numpy(w.m_indices).to(dev)
+                D = torch.empty((w.A.shape[0], N), dtype=torch.bfloat16, device=dev)
+                run(label, lambda r: fg.grouped_contiguous(A, sa, B, sb, idx, out=D, stream=stream))
+            else:
+                mm = torch.from_numpy(w.masked_m).to(dev)
+                D = torch.empty((w.A.shape[0], w.A.shape[1], N), dtype=torch.bfloat16, device=dev)
+                f = fg.fp8fp4_grouped_masked if "fp8xfp4" in label else fg.grouped_masked
+                run(label, lambda r: f(A, sa, B, sb, mm, w.expected_m, out=D, stream=stream))
+        stream.synchronize()
+        del A, B, sb, sa, D, w
+        torch.cuda.empty_cache()
+    bits = W.activations_bf16(W.QUANT_M, W.QUANT_K, seed=31)
+    X = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    codes = torch.empty((W.QUANT_M, W.QUANT_K), dtype=torch.float8_e4m3fn, device=dev)
+    scales = torch.empty((W.QUANT_K // 128, W.QUANT_M), dtype=torch.float32, device=dev)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        run("quantize_1x128 32768x7168", lambda r: fg.quantize_1x128(X, codes=codes, scales=scales, stream=stream))
         # the calibration copy: the last elementwise kernels of the run (read and write COPY_BYTES)
         for r in range(COUNTER_REPS):
             torch.add(src, 0.0, out=dst)
-            order.append("copy %d" % COPY_BYTES)
+            order.append(("copy %d" % COPY_BYTES, ""))
     stream.synchronize()
-    print(json.dumps({"counter_launches": order, "config": fg.last_config()}), flush=True)
+    print(json.dumps({"counter_launches": order}), flush=True)
 
 
-def _counter_rows(folder, counter):
-    """(kernel name, value in KiB) per dispatch, in dispatch order, from a rocprofv3 csv folder."""
+def _pass_rows(folder):
+    """{dispatch id: (kernel name, {counter: value})} from one rocprofv3 --pmc csv output folder
+    (values summed over the dimensions rocprofv3 reports them in; GRBM counters, which count
+    cycles per XCD, take the maximum instead)."""
     import csv
     import glob
     files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
@@ -347,64 +407,205 @@ def _counter_rows(folder, counter):
     per = {}
     for f in files:
         for r in csv.DictReader(open(f)):
-            if r["Counter_Name"] != counter:
-                continue
             key = int(r["Dispatch_Id"])
-            name, val = per.get(key, (r["Kernel_Name"], 0.0))
-            per[key] = (name, val + float(r["Counter_Value"]))
-    return [per[k] for k in sorted(per)]
+            name, vals = per.setdefault(key, (r["Kernel_Name"], {}))
+            c, v = r["Counter_Name"], float(r["Counter_Value"])
+            vals[c] = max(vals.get(c, v), v) if c.startswith("GRBM_") else vals.get(c, 0.0) + v
+    return per
+
+
+def _short_kernel(name):
+    for k in LIB_KERNELS:
+        if k in name:
+            i = name.index(k)
+            j = name.find(">", i)
+            return name[i:j + 1] if j > 0 else k
+    return name
+
+
+def counter_summary(folders):
+    """Per leg of counter_legs(): the median over its COUNTER_REPS dispatches of every counter the
+    passes collected, with derived figures where the counters allow:
+      HBM traffic  = FETCH_SIZE and WRITE_SIZE (KiB) scaled by what they count for the calibration
+                     copy of COPY_BYTES, against the leg's algorithmic bytes;
+      MFMA busy    = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x CUs x 4 SIMDs);
+      FP8 MFMA work = SQ_INSTS_VALU_MFMA_MOPS_F8 x 512 flop, against the leg's algorithmic flop;
+      wait share   = SQ_WAIT_ANY / SQ_WAVE_CYCLES; TA busy = TA_BUSY_avr / GRBM_GUI_ACTIVE.
+    Writes profiles/counters_<family>.txt per family and the dominant kernel's traffic file."""
+    legs = counter_legs()
+    lib, copies = [], []
+    merged = {}
+    for folder in folders:
+        for key, (name, vals) in _pass_rows(folder).items():
+            m = merged.setdefault(key, [name, {}])
+            m[1].update(vals)
+    for key in sorted(merged):
+        name, vals = merged[key]
+        if any(k in name for k in LIB_KERNELS):
+            lib.append((name, vals))
+        elif "elementwise" in name.lower():
+            copies.append(vals)
+    if len(lib) != COUNTER_REPS * len(legs):
+        raise SystemExit("%d library dispatches found, %d expected" % (len(lib), COUNTER_REPS * len(legs)))
+    cal = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        v = [x[c] for x in copies[-COUNTER_REPS:] if c in x]
+        if v:
+            cal[c] = COPY_BYTES / (float(np.median(v)) * 1024.0)
+    cus = 256
+    rows = []
+    for i, (label, family, flop, byts) in enumerate(legs):
+        part = lib[i * COUNTER_REPS:(i + 1) * COUNTER_REPS]
+        names = {n for n, _ in part}
+        med = {c: float(np.median([v[c] for _, v in part if c in v])) for c in part[0][1]}
+        d = {}
+        if "FETCH_SIZE" in med and "WRITE_SIZE" in med and len(cal) == 2:
+            t = med["FETCH_SIZE"] * 1024 * cal["FETCH_SIZE"] + med["WRITE_SIZE"] * 1024 * cal["WRITE_SIZE"]
+            d["hbm_MB"] = t / 1e6
+            d["alg_MB"] = byts / 1e6
+            d["hbm/alg"] = t / byts
+        gui = med.get("GRBM_GUI_ACTIVE")
+        if "MfmaUtil" in med:
+            d["mfma_busy"] = med["MfmaUtil"] / 100.0
+        elif "SQ_VALU_MFMA_BUSY_CYCLES" in med and gui:
+            d["mfma_busy"] = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * cus * 4)
+        if "SQ_INSTS_VALU_MFMA_MOPS_F8" in med and flop:
+            d["mfma_flop/alg"] = med["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512 / flop
+        if med.get("SQ_WAVE_CYCLES") and "SQ_WAIT_ANY" in med:
+            d["wait_share"] = med["SQ_WAIT_ANY"] / med["SQ_WAVE_CYCLES"]
+        if gui and "TA_BUSY_avr" in med:
+            d["ta_busy"] = med["TA_BUSY_avr"] / gui
+        if gui and "TD_BUSY_avr" in med:
+            d["td_busy"] = med["TD_BUSY_avr"] / gui
+        if gui and "SQ_LDS_IDX_ACTIVE" in med:
+            d["lds_active"] = med["SQ_LDS_IDX_ACTIVE"] / (gui * cus)
+        if gui and "SQ_LDS_BANK_CONFLICT" in med:
+            d["lds_bank_conflict"] = med["SQ_LDS_BANK_CONFLICT"] / (gui * cus)
+        if "VALUBusy" in med:
+            d["valu_busy"] = med["VALUBusy"] / 100.0
+        rows.append((label, family, sorted(_short_kernel(n) for n in names), med, d, byts))
+    src = kernel_source_hash()
+    for family in sorted({r[1] for r in rows}):
+        path = os.path.join(ROOT, "profiles", "counters_%s.txt" % family)
+        with open(path, "w") as f:
+            f.write("Hardware counters of the %s legs (rocprofv3 --pmc; median of %d eager launches per leg, each "
+                    "after a read-only 1 GiB buffer read)\n" % (family.replace("_", " "), COUNTER_REPS))
+            f.write("command (one per counter group): rocprofv3 --pmc <counters> --output-format csv -d <dir> "
+                    "-- python3 bench.py --counters\n")
+            f.write("summary: python3 bench.py --counter-summary <dir> [<dir> ...]\n")
+            f.write("kernel_source_sha256_16: %s\n" % src)
+            for c, fct in sorted(cal.items()):
+                f.write("%s calibration: factor %.4f (bytes of a %d-byte copy / bytes counted)\n" % (c, fct, COPY_BYTES))
+            f.write("derived (GRBM_GUI_ACTIVE: cycles of the busiest XCD): hbm = calibrated FETCH_SIZE + WRITE_SIZE; "
+                    "mfma_busy = MfmaUtil / 100 (MFMA busy cycles over all SIMDs / (GRBM_GUI_ACTIVE x SIMDs)); "
+                    "mfma_flop/alg = SQ_INSTS_VALU_MFMA_MOPS_F8 x 512 / algorithmic flop; wait_share = SQ_WAIT_ANY / "
+                    "SQ_WAVE_CYCLES; ta_busy, td_busy = TA_BUSY_avr, TD_BUSY_avr / GRBM_GUI_ACTIVE; lds_active, "
+                    "lds_bank_conflict = SQ_LDS_IDX_ACTIVE, SQ_LDS_BANK_CONFLICT / (GRBM_GUI_ACTIVE x %d CUs); "
+                    "valu_busy = VALUBusy / 100\n" % cus)
+            for label, fam, kern, med, d, byts in rows:
+                if fam != family:
+                    continue
+                f.write("%s  [%s]\n" % (label, ", ".join(kern)))
+                f.write("    derived: %s\n" % "  ".join("%s %.3f" % (k, v) for k, v in d.items()))
+                f.write("    raw: %s\n" % "  ".join("%s %.6g" % (k, v) for k, v in sorted(med.items())))
+        print(open(path).read())
+    # the dominant kernel's traffic per launch (read by the benchmark's roofline.traffic)
+    dom = [r for r in rows if r[2] == [DOMINANT_KERNEL] and "hbm_MB" in r[4]]
+    if dom:
+        per_launch = int(round(np.mean([r[4]["hbm_MB"] for r in dom]) * 1e6))
+        with open(os.path.join(ROOT, TRAFFIC_FILE), "w") as f:
+            f.write("HBM traffic of the dense 256x256 kernel on the M=4096 sweep shapes (rocprofv3 --pmc)\n")
+            f.write("command (per counter): rocprofv3 --pmc <FETCH_SIZE | WRITE_SIZE> --output-format csv -d <dir> "
+                    "-- python3 bench.py --counters\n")
+            f.write("summary: python3 bench.py --counter-summary <dir> [<dir> ...]\n")
+            f.write("kernel_source_sha256_16: %s\n" % src)
+            for c, fct in sorted(cal.items()):
+                f.write("%s_copy_calibration: factor %.4f\n" % (c, fct))
+            for r in dom:
+                f.write("  %-28s traffic %7.1f MB  algorithmic %6.1f MB  ratio %.2f\n"
+                        % (r[0], r[4]["hbm_MB"], r[4]["alg_MB"], r[4]["hbm/alg"]))
+            f.write("traffic_bytes_per_launch: %d   (mean over the %d shapes run by %s)\n"
+                    % (per_launch, len(dom), DOMINANT_KERNEL))
+        print(open(os.path.join(ROOT, TRAFFIC_FILE)).read())
 
 
 DOMINANT_KERNEL = "fp8gemm_kernel<256, 256, 4, 2, 2, 0, 0, 0>"
 
 
-def traffic_summary(fetch_dir, write_dir):
-    """HBM traffic per launch of the dense 256x256 kernel on the M=4096 sweep shapes that use it,
-    from FETCH_SIZE and WRITE_SIZE (KiB per dispatch) each scaled by what the counter reads for a
-    plain copy of COPY_BYTES (true bytes / counted bytes).  Shapes that run another kernel are
-    listed for reference and left out of the per-launch figure."""
+READ_WGS = (256, 512, 1024, 2048)
+READ_DEPTHS = (8, 16)
+
+
+def bench_read_floor(torch, dev, stream, per, read_flush, reps):
+    """The read floor of every decode-sized sweep GEMM (M <= 128): a plain streaming read
+    (libreadprobe.so: contiguous 16-byte loads, 8 or 16 in flight per thread, 256-2048
+    workgroups, the best of these) of the GEMM's algorithmic byte count, timed like the GEMMs:
+    HIP events on the launch stream around a graph of COPIES launches that each read another
+    buffer copy, after a read-only 1 GiB buffer read.  Adds read_floor_us and frac_read_floor
+    (read time / GEMM time) to the per-shape rows."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp8_block_scaled_x128_amd", "libreadprobe.so"))
+    lib.read_probe.restype = ctypes.c_int
+    lib.read_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                               ctypes.c_void_p]
+    rows = [p for p in per if p["M"] <= 128]
+    if not rows:
+        return {}
+    nbytes = [(-(-W_bytes(p) // 16)) * 16 for p in rows]
+    bufs = [torch.empty(max(nbytes), dtype=torch.uint8, device=dev) for _ in range(COPIES)]
+    for b in bufs:
+        b.fill_(1)
+    sink = torch.zeros(max(READ_WGS), dtype=torch.int32, device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    t0 = time.time()
+    out = []
+    for p, nb in zip(rows, nbytes):
+        best = None
+        for wgs in READ_WGS:
+            for depth in READ_DEPTHS:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for b in bufs:
+                        if lib.read_probe(b.data_ptr(), nb, wgs, depth, sink.data_ptr(), sp) != 0:
+                            raise RuntimeError("read_probe launch failed")
+                replay_on(stream, g)
+                stream.synchronize()
+                ts = []
+                for _ in range(reps):
+                    read_flush()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    replay_on(stream, g)
+                    e1.record(stream)
+                    stream.synchronize()
+                    ts.append(e0.elapsed_time(e1) / COPIES)
+                us = float(np.mean(ts)) * 1e3
+                if best is None or us < best[0]:
+                    best = (us, wgs, depth)
+                del g
+        p["read_floor_us"] = round(best[0], 2)
+        p["frac_read_floor"] = round(best[0] / p["us"], 4)
+        out.append(dict(M=p["M"], N=p["N"], K=p["K"], bytes=nb, read_us=round(best[0], 2),
+                        read_frac_hbm=round(nb / (best[0] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                        gemm_us=p["us"], frac_read_floor=p["frac_read_floor"], wgs=best[1], depth=best[2]))
+    log("read floor of %d decode shapes in %.1f s: GEMM time / read time %s" % (
+        len(rows), time.time() - t0, " ".join("%.2f" % (1.0 / r["frac_read_floor"]) for r in out)))
+    del bufs
+    return dict(method="plain streaming read of each shape's algorithmic bytes (best of %s workgroups x %s "
+                       "loads in flight), timed as the GEMMs" % (list(READ_WGS), list(READ_DEPTHS)),
+                per_shape=out)
+
+
+def W_bytes(p):
     import workloads as W
-    out = {}
-    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        rows = _counter_rows(folder, counter)
-        gem = [(n, v) for n, v in rows if "fp8gemm_kernel" in n]
-        cop = [v for n, v in rows if "elementwise" in n.lower()]
-        if len(cop) < 1 or len(gem) != COUNTER_REPS * len(W.SWEEP_NK):
-            raise SystemExit("%s: %d gemm and %d copy dispatches found" % (counter, len(gem), len(cop)))
-        copy_kib = float(np.median(cop[-COUNTER_REPS:]))
-        factor = COPY_BYTES / (copy_kib * 1024.0)
-        shapes = []
-        for i, (N, K) in enumerate(W.SWEEP_NK):
-            part = gem[i * COUNTER_REPS:(i + 1) * COUNTER_REPS]
-            kib = float(np.median([v for _, v in part]))
-            name = part[0][0]
-            kern = name[name.index("fp8gemm_kernel"):name.index(">") + 1] if ">" in name else name
-            shapes.append((N, K, kern, kib, kib * 1024.0 * factor))
-        out[counter] = (copy_kib, factor, shapes)
-    path = os.path.join(ROOT, TRAFFIC_FILE)
-    fetch, write = out["FETCH_SIZE"], out["WRITE_SIZE"]
-    dom = [f[4] + w[4] for f, w in zip(fetch[2], write[2]) if f[2] == DOMINANT_KERNEL]
-    per_launch = int(round(sum(dom) / len(dom)))
-    with open(path, "w") as f:
-        f.write("HBM traffic of the dense 256x256 kernel on the M=4096 sweep shapes (rocprofv3 --pmc)\n")
-        f.write("command (per counter): rocprofv3 --pmc <FETCH_SIZE | WRITE_SIZE> --output-format csv -d <dir> "
-                "-- python3 bench.py --counters\n")
-        f.write("summary: python3 bench.py --traffic-summary <fetch dir> <write dir>\n")
-        f.write("kernel_source_sha256_16: %s\n" % kernel_source_hash())
-        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-            copy_kib, factor, shapes = out[counter]
-            f.write("%s_copy_calibration: %.0f KiB counted for a %d-byte copy, factor %.4f\n"
-                    % (counter, copy_kib, COPY_BYTES, factor))
-        f.write("per shape (median of %d launches; bytes = KiB * 1024 * factor; algorithmic = A + B + scales + D):\n"
-                % COUNTER_REPS)
-        for (N, K, kern, fk, fb), (_, _, _, wk, wb) in zip(fetch[2], write[2]):
-            alg = W.dense_work(4096, N, K)[1]
-            f.write("  M=4096 N=%-5d K=%-5d %-38s fetch %10.0f KiB  write %9.0f KiB  traffic %6.1f MB  "
-                    "algorithmic %6.1f MB  ratio %.2f\n"
-                    % (N, K, kern, fk, wk, (fb + wb) / 1e6, alg / 1e6, (fb + wb) / alg))
-        f.write("traffic_bytes_per_launch: %d   (mean over the %d shapes run by %s)\n"
-                % (per_launch, len(dom), DOMINANT_KERNEL))
-    print(open(path).read())
+    return W.dense_work(p["M"], p["N"], p["K"])[1]
+
+
+def replay_on(stream, g):
+    import torch
+    with torch.cuda.stream(stream):
+        g.replay()
 
 
 def bench_specialized(fg, torch, stream, cases, per, replay, read_flush, reps):
