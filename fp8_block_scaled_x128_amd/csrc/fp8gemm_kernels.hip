@@ -38,7 +38,7 @@ static KernelEntry entry(const char* name) {
     e.kp = 0;
     e.threads = T::NT;
     e.splitk = T::SPLITK;
-    e.lds_bytes = T::LDS_BYTES;
+    e.lds_bytes = T::SMEM_BYTES;
     e.func = reinterpret_cast<const void*>(&fp8gemm_kernel<BM, BN, WMW, WNW, STAGES, LAYOUT>);
     e.launch = &launch_impl<BM, BN, WMW, WNW, STAGES, LAYOUT>;
     return e;

@@ -84,6 +84,19 @@ struct Tile {
     static constexpr bool NB_UNIFORM = (BN % 128 == 0) && (128 % WN == 0);
     // split-K partial reduction is compiled for tiles small enough to need it (decode shapes)
     static constexpr bool SPLITK = BM * BN <= 128 * 256;
+    // Epilogue staging: each wave writes its WM x WN bf16 results row-major into a private LDS
+    // region (after the K loop, over the ring), then stores whole 16-byte chunks of rows.  The
+    // row pitch holds an odd number of 16-byte units, so the 8-byte writes of 32 lanes in the
+    // MFMA layout (16 rows x 2 column groups) fall into 64 distinct banks.
+    static_assert(WM <= 64, "row mask: one bit per row of a wave's slab");
+    static_assert(WN % 8 == 0, "16-byte chunks of a wave's rows");
+    static constexpr int ROW_BYTES = 2 * WN;
+    static constexpr int CPR = ROW_BYTES / 16;                  // 16-byte chunks per row
+    static constexpr int PITCH = ROW_BYTES + ((CPR % 2 == 0) ? 16 : 0);
+    static constexpr int STG_WAVE_BYTES = WM * PITCH;
+    static constexpr int STORES = (WM * CPR + 63) / 64;         // store instructions per wave
+    static constexpr int SMEM_BYTES = LDS_BYTES > NW * STG_WAVE_BYTES ? LDS_BYTES : NW * STG_WAVE_BYTES;
+    static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget (staging)");
 };
 
 // NC, KC > 0 fix N and K at compile time (the run-time specialised variant); 0 reads them from
@@ -91,7 +104,7 @@ struct Tile {
 template <int BM, int BN, int WMW, int WNW, int STAGES, int LAYOUT, int NC = 0, int KC = 0>
 __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArgs args) {
     using T = Tile<BM, BN, WMW, WNW, STAGES, LAYOUT>;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::SMEM_BYTES];
     __shared__ int s_flag;
 
     const int tid = threadIdx.x;
@@ -446,37 +459,57 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
             }
         }
         if (store_direct) {
-            // lane owns D[m][n..n+3] per sub-tile
-#pragma unroll
-            for (int j = 0; j < T::JM; ++j) {
-                const int rm = wm * T::WM + 16 * j + row16;     // row within the tile
-                bool ok = rm < valid_rows;
+            // The lane index is made opaque here, so the epilogue's per-lane addresses are formed
+            // after the K loop rather than kept live across it (registers are at the limit there).
+            int el = lane;
+            asm volatile("" : "+v"(el));
+            const int erow16 = el & 15;
+            const int egrp = el >> 4;
+            // Rows of this wave's slab that are stored (bit r: tile row wm * WM + r): valid rows
+            // only, and in the contiguous layout only the rows of this pass's group.
+            bool row_ok = false;
+            if (el < T::WM) {
+                const int rm = wm * T::WM + el;
+                row_ok = rm < valid_rows;
                 if constexpr (LAYOUT == kContiguous) {
-                    if (ok) ok = args.m_indices[arow0 + rm] == g;
+                    if (row_ok) row_ok = args.m_indices[arow0 + rm] == g;
                 }
-                if (!ok) continue;
-                uint16_t* drow = args.D + (arow0 + rm) * (int64_t)N;
+            }
+            const uint64_t rowmask = __builtin_amdgcn_ballot_w64(row_ok);
+            // every wave is past its last slice before any wave overwrites the ring with its stage
+            if (!T::SPLITK || args.splits == 1) __syncthreads();
+            // bf16 results into this wave's LDS region, row-major: lane owns row 16 j + row16,
+            // columns 16 i2 + 4 grp .. + 3 of the wave's slab
+            uint8_t* stg = smem + wave * T::STG_WAVE_BYTES;
+#pragma unroll
+            for (int j = 0; j < T::JM; ++j)
 #pragma unroll
                 for (int i2 = 0; i2 < T::IN; ++i2) {
-                    const int n = n0 + wn * T::WN + 16 * i2 + 4 * grp;
                     const v4f v = acc[i2][j];
-                    if (n + 3 < N && (N & 3) == 0) {
-                        uint2 pk;
-                        pk.x = pack_bf16x2(v.x, v.y);
-                        pk.y = pack_bf16x2(v.z, v.w);
-                        *reinterpret_cast<uint2*>(drow + n) = pk;
-                    } else {
-                        const float e[4] = {v.x, v.y, v.z, v.w};
+                    uint2 pk;
+                    pk.x = pack_bf16x2(v.x, v.y);
+                    pk.y = pack_bf16x2(v.z, v.w);
+                    *reinterpret_cast<uint2*>(stg + (16 * j + erow16) * T::PITCH + (16 * i2 + 4 * egrp) * 2) = pk;
+                }
+            // then whole 16-byte chunks (8 columns) of rows, consecutive lanes along a row (the
+            // wave's own LDS writes precede its reads in order; no barrier is needed)
+            const int ncol0 = n0 + wn * T::WN;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            if (n + r < N) {
-                                __bf16 h = (__bf16)e[r];
-                                uint16_t hb;
-                                __builtin_memcpy(&hb, &h, 2);
-                                drow[n + r] = hb;
-                            }
-                        }
-                    }
+            for (int st = 0; st < T::STORES; ++st) {
+                const int idx = 64 * st + el;
+                const int r = idx / T::CPR;
+                const int c = idx - r * T::CPR;
+                if (r >= T::WM || !((rowmask >> r) & 1)) continue;
+                const uint4 v = *reinterpret_cast<const uint4*>(stg + r * T::PITCH + c * 16);
+                const int n = ncol0 + 8 * c;
+                uint16_t* drow = args.D + (arow0 + wm * T::WM + r) * (int64_t)N;
+                if ((N & 7) == 0 && n + 8 <= N) {
+                    *reinterpret_cast<uint4*>(drow + n) = v;
+                } else {
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < N) drow[n + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
                 }
             }
         }
