@@ -143,6 +143,7 @@ def main():
             for c in copies:
                 c["D"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             cases.append(dict(M=M, N=N, K=K, copies=copies, hostA=Aq, hostsa=saq, hostB=Bq, hostsb=sbq))
+    torch.cuda.synchronize()            # operands (and their copies) are made on the default stream
     log("inputs ready in %.1f s" % (time.time() - t0))
 
     def call(case, r):
@@ -732,6 +733,7 @@ def bench_grouped(fg, W, torch, dev, stream, reps=10, cpu=False):
             work = W.grouped_fp4_work if "fp4" in name else W.grouped_work
             flop, byts = work(counts, N, K, index_bytes=4 * len(counts))
         calls = max(GROUPED_CALLS, ncopy)
+        torch.cuda.synchronize()        # operand copies are made on the default stream
         with torch.cuda.stream(stream):
             call(ops[0])
         cfg = fg.last_config()
@@ -850,6 +852,7 @@ def bench_moe_chain(fg, W, torch, dev, stream, reps=5, cpu=False):
         while len(copies) < ncopy:
             copies.append(dict({k: v.clone() for k, v in w0.items()}, **buffers()))
         # every copy's buffers hold the previous step's results of that copy (chain order)
+        torch.cuda.synchronize()        # weight copies are made on the default stream
         with torch.cuda.stream(stream):
             for c in copies[:ncopy]:
                 steps["chain"][1](c)

@@ -219,7 +219,8 @@ Choice choose_masked_decode(int64_t N, int nkb, int64_t groups, int cus, bool fp
 //  - <= 128 rows (decode): HBM-bound stream of B.  Masked groups: the masked decode kernel above.
 //    Otherwise tiles span all rows of A (64, or 128 when A re-reads would cost as much as B:
 //    K >= 8192 or very wide N), N tiles of 64 or 128 so that about one unit per CU is in flight,
-//    and split-K to reach that count on narrow N.
+//    and split-K to reach that count on narrow N.  64-row tiles over K >= 8192 take the 6-slice
+//    ring consumed two slices per barrier.
 //  - >= 1024 rows (prefill): MFMA-bound; 256x256 tiles, 8 waves.
 //  - in between: 128x128 tiles.
 Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_rows, int G, int cus, bool fp4) {
@@ -237,6 +238,7 @@ Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_row
     if (m <= 64) {
         const int64_t t64 = groups * ((N + 63) / 64);
         if (t64 * 2 >= 3 * cus) c.entry = find_entry(layout, 64, 128, 1, 4, 3);
+        else if (layout == kDense && nkb >= 64) c.entry = find_entry(layout, 64, 64, 1, 4, 6);  // long K
         else c.entry = find_entry(layout, 64, 64, 1, 4, 4);
     } else if (m <= 128) {
         const int64_t K = (int64_t)nkb * 128;

@@ -60,6 +60,9 @@ const KernelEntry* kernel_table(int* count) {
         FP8GEMM_ENTRY(64, 64, 1, 4, 4, kDense),
         FP8GEMM_ENTRY(64, 128, 1, 4, 3, kDense),
         FP8GEMM_ENTRY(128, 128, 2, 4, 3, kDense),
+        // dense, decode, long K: a 6-slice ring consumed two slices per barrier (64x7168x16384:
+        // 34.0 against 36.0 us for the 4-slice ring, same split; 8 slices 35.6 us)
+        FP8GEMM_ENTRY(64, 64, 1, 4, 6, kDense),
         // contiguous grouped: 256-row tiles run one pass per group among their two 128-row blocks
         // (configuration 2: 891 us against 1179 us for 128x256 tiles; configuration 3: 546 / 651 us)
         FP8GEMM_ENTRY(256, 256, 4, 2, 2, kContiguous),

@@ -82,6 +82,11 @@ struct Tile {
     static_assert(NDMA * (STAGES - 1) < 64, "vmcnt range");
     // every wave's N range lies inside one 128-row block of B scales
     static constexpr bool NB_UNIFORM = (BN % 128 == 0) && (128 % WN == 0);
+    // K slices consumed per workgroup barrier.  Deep rings (5 or more stages, the decode tiles)
+    // take two: one barrier per pair, both slices' fragment reads issued together, then all their
+    // MFMAs, then the promotions in slice order (the same arithmetic order as one at a time).
+    static constexpr int SPB = STAGES >= 5 ? 2 : 1;
+    static_assert(SPB == 1 || IN <= 2, "paired slices: decode tiles (at most two N sub-tiles per wave)");
     // split-K partial reduction is compiled for tiles small enough to need it (decode shapes)
     static constexpr bool SPLITK = BM * BN <= 128 * 256;
     // Epilogue staging: each wave writes its WM x WN bf16 results row-major into a private LDS
@@ -385,16 +390,81 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
             promote(T::IN - 1, pprev);
         };
 
-        // ---- ring of whole slices: slice i + STAGES - 1 goes into the stage slice i - 1 used
+        // ---- two slices at a time (decode tiles): the fragments of slices i and i+1, then all
+        // their MFMAs, then the promotions, slice i first
+        auto compute_pair = [&](int i) {
+            v8i af[2][T::JM];
+            v8i bfr[2][T::IN];
+            float sw[2][T::IN][T::JM];
 #pragma unroll
-        for (int i = 0; i < STAGES - 1; ++i)
-            if (i < nks) { issue_b(i, 0, T::B_DMA); issue_a(i); }
-        for (int i = 0; i < nks; ++i) {
-            // slice i landed (this wave's loads), then every wave's loads
-            wait_slices<T::NDMA, STAGES - 2, 0>(min(STAGES - 2, nks - 1 - i));
-            __syncthreads();
-            if (i + STAGES - 1 < nks) { issue_b(i + STAGES - 1, 0, T::B_DMA); issue_a(i + STAGES - 1); }
-            compute_slice(i);
+            for (int sl = 0; sl < 2; ++sl) {
+                const uint8_t* st = smem + ((i + sl) % STAGES) * T::STAGE_BYTES;
+                const float* sa_l = reinterpret_cast<const float*>(st + T::SA_OFF);
+                const float* sb_l = reinterpret_cast<const float*>(st + T::SB_OFF);
+                float sav[T::JM];
+#pragma unroll
+                for (int j = 0; j < T::JM; ++j) {
+                    const int r = wm * T::WM + 16 * j + row16;
+                    const uint8_t* rp = st + T::A_OFF + r * 128;
+                    const v4i lo = *reinterpret_cast<const v4i*>(rp + frag_lo);
+                    const v4i hi = *reinterpret_cast<const v4i*>(rp + frag_hi);
+                    af[sl][j] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                    sav[j] = sa_l[r];
+                }
+#pragma unroll
+                for (int i2 = 0; i2 < T::IN; ++i2) {
+                    const int r = wn * T::WN + 16 * i2 + row16;
+                    const uint8_t* rp = st + T::B_OFF + r * 128;
+                    const v4i lo = *reinterpret_cast<const v4i*>(rp + frag_lo);
+                    const v4i hi = *reinterpret_cast<const v4i*>(rp + frag_hi);
+                    bfr[sl][i2] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                    const float sbi = sb_l[((n0 + wn * T::WN + 16 * i2) >> 7) - nb_first];
+#pragma unroll
+                    for (int j = 0; j < T::JM; ++j) sw[sl][i2][j] = sav[j] * sbi;
+                }
+            }
+            v4f p[2][T::IN][T::JM];
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int i2 = 0; i2 < T::IN; ++i2)
+#pragma unroll
+                    for (int j = 0; j < T::JM; ++j) p[sl][i2][j] = mfma16x16x128(bfr[sl][i2], af[sl][j]);
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int i2 = 0; i2 < T::IN; ++i2)
+#pragma unroll
+                    for (int j = 0; j < T::JM; ++j) acc[i2][j] += p[sl][i2][j] * sw[sl][i2][j];
+        };
+
+        if constexpr (T::SPB == 1) {
+            // ---- ring of whole slices: slice i + STAGES - 1 goes into the stage slice i - 1 used
+#pragma unroll
+            for (int i = 0; i < STAGES - 1; ++i)
+                if (i < nks) { issue_b(i, 0, T::B_DMA); issue_a(i); }
+            for (int i = 0; i < nks; ++i) {
+                // slice i landed (this wave's loads), then every wave's loads
+                wait_slices<T::NDMA, STAGES - 2, 0>(min(STAGES - 2, nks - 1 - i));
+                __syncthreads();
+                if (i + STAGES - 1 < nks) { issue_b(i + STAGES - 1, 0, T::B_DMA); issue_a(i + STAGES - 1); }
+                compute_slice(i);
+            }
+        } else {
+            // ---- ring consumed two slices per barrier: slices i + STAGES - 2 and i + STAGES - 1 go
+            // into the stages slices i - 2 and i - 1 used (read before this barrier)
+#pragma unroll
+            for (int i = 0; i < STAGES - 2; ++i)
+                if (i < nks) { issue_b(i, 0, T::B_DMA); issue_a(i); }
+            for (int i = 0; i < nks; i += 2) {
+                // slices i and i + 1 landed: at most slices i + 2 .. i + STAGES - 3 still in flight
+                wait_slices<T::NDMA, STAGES - 4, 0>(min(STAGES - 4, nks - 2 - i));
+                __syncthreads();
+                if (i + STAGES - 2 < nks) { issue_b(i + STAGES - 2, 0, T::B_DMA); issue_a(i + STAGES - 2); }
+                if (i + STAGES - 1 < nks) { issue_b(i + STAGES - 1, 0, T::B_DMA); issue_a(i + STAGES - 1); }
+                if (i + 1 < nks) compute_pair(i);
+                else compute_slice(i);
+            }
         }
 
         // ---- epilogue -----------------------------------------------------------------------

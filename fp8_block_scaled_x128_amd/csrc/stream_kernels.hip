@@ -43,8 +43,9 @@
 //
 // Work units are (M tile, group, N tile of BN = 16*JN*W rows, K split), the M tile outermost so
 // the units of tiles past every group's count (skipped at once) spread evenly over a persistent
-// grid.  When K is split, partial tiles are exchanged and summed in split order by the last
-// workgroup of the tile to arrive, as in the tiled kernel.
+// grid; each XCD takes a contiguous range of units, so the N tiles of a group share one L2.
+// When K is split, partial tiles are exchanged and summed in split order by the last workgroup
+// of the tile to arrive, as in the tiled kernel.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -119,7 +120,13 @@ __global__ __launch_bounds__(W * 64) void fp8gemm_masked_decode_kernel(const Ker
     const int nkb = args.nkb;
     const int nnb = args.nnb;
 
-    for (int unit = blockIdx.x; unit < args.units; unit += gridDim.x) {
+    // XCD-aware order: workgroups are dealt to the 8 XCDs round robin, so give the workgroups of
+    // one XCD a contiguous range of units -- the N tiles of a group then share its A tile in one
+    // L2 instead of every XCD fetching every group's A.
+    const int P = gridDim.x;
+    int logical = blockIdx.x;
+    if ((P & 7) == 0) logical = (blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3);
+    for (int unit = logical; unit < args.units; unit += P) {
         // ---- unit -> (split fastest, N tile, group, M tile) --------------------------------
         uint32_t u = (uint32_t)unit;
         const uint32_t tile_id = fast_div(u, args.div_splits);

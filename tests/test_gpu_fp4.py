@@ -190,6 +190,36 @@ def test_fp4_argument_errors():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("entry", fp4_table(), ids=lambda e: "mt%d_w%d_jn%d_kp%d_pf%d" % e)
+@pytest.mark.parametrize("split", [1, 2, 3])
+def test_every_fp4_config_odd_block_count(entry, split):
+    """K = 7 blocks: the last block pair of the ring holds one block, and with 2 or 3 K splits the
+    ranges hold 4 + 3 or 3 + 3 + 1 blocks, the second starting at an odd block; random MXFP4
+    weights within tolerance, integer inputs with power-of-two scales bit-exact."""
+    mt, wv, jn, kp, pf = entry
+    bn = 16 * jn * wv
+    M_max, N, K = 2 * mt, bn + 40, 896
+    w = W.masked_fp4(np.array([mt + 9, 5, M_max], np.int32), M_max, N, K, seed=mt + bn + 7 * split)
+    ref, _ = oracle.grouped_masked_fp4(w.A, w.sa, w.B, w.sb, w.masked_m)
+    with forced_stream(mt, wv, jn, kp, pf, split):
+        D = run(w, 64, out=sentinel_tensor((3, M_max, N)))
+        cfg = fg.last_config()
+    assert "stream tile=%dx%d" % (mt, bn) in cfg and "split=%d " % split in cfg, cfg
+    got = gpu_bits(D)
+    v = valid_mask(w, N)
+    assert_close(got, ref, mask=v, what=cfg)
+    assert np.all(got[~v] == SENTINEL)
+    wi = integer_case(np.random.default_rng(bn + 11 * split), [mt + 1, 3, M_max], M_max, N, K)
+    ref2, _ = oracle.grouped_masked_fp4(wi.A, wi.sa, wi.B, wi.sb, wi.masked_m)
+    v2 = valid_mask(wi, N)
+    with forced_stream(mt, wv, jn, kp, pf, split):
+        D2 = run(wi, 64, out=sentinel_tensor((3, M_max, N)))
+    got2 = gpu_bits(D2)
+    assert np.array_equal(got2[v2], ref2[v2]), "%s: %d outputs differ" % (cfg, int((got2[v2] != ref2[v2]).sum()))
+    assert np.all(got2[~v2] == SENTINEL)
+    say("fp4 odd block count", cfg)
+
+
 @pytest.mark.slow
 def test_fp4_config4_full_size():
     """The masked decode workload (16 groups x 256 rows, Poisson(64) counts, N=4096, K=7168) with

@@ -54,10 +54,11 @@ def check_code(code: bytes, entry, what):
     ins = [l for l in lines if re.match(r"^[sv]_|^global_|^buffer_|^ds_|^scratch_", l)]
     assert not [l for l in ins if re.match(r"v_pk_(fma|mul|add)_f32", l)], what + ": packed fp32 VALU op"
     assert not [l for l in ins if l.startswith("scratch_")], what + ": scratch access"
-    # M0: set only right before a direct-to-LDS load (s_mov_b32 m0, sN; s_nop 0; global_load_lds_*)
+    # M0: set only right before a direct-to-LDS load (s_mov_b32 m0, <scalar register>; s_nop 0;
+    # global_load_lds_*) -- the register holds the LDS address; vcc_lo/hi serve as scalar registers too
     for i, l in enumerate(ins):
         if re.search(r"\bm0\b", l):
-            assert re.match(r"s_mov_b32 m0, s\d+$", l), (what, l)
+            assert re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", l), (what, l)
             assert ins[i + 1].startswith("s_nop") and ins[i + 2].startswith("global_load_lds_dword"), (what, l)
     n_mfma = sum(1 for l in ins if re.match(r"v_mfma_(scale_)?f32_16x16x128_f8f6f4", l))
     per_slice = (bm // wm // 16) * (bn // wn // 16)
