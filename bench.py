@@ -62,6 +62,9 @@ def parse():
                    help="launch every kernel the benchmark times (the 18 sweep GEMMs, the grouped "
                         "configurations, the quantiser) COUNTER_REPS times each, eagerly, then a 1 GiB copy "
                         "(run under rocprofv3 --pmc, one pass per counter group)")
+    p.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
+                   help="turn the rocprofv3 --kernel-trace output folder of a benchmark run and that run's "
+                        "JSON line into profiles/kernel_stats_*_bench.txt (dispatches per leg by the leg markers)")
     p.add_argument("--counter-summary", nargs="+", metavar="PASS_DIR",
                    help="turn the rocprofv3 --pmc output folders of --counters runs (one per pass) into "
                         "the per-family summaries profiles/counters_*.txt and " + TRAFFIC_FILE)
@@ -105,6 +108,9 @@ def main():
     args = parse()
     if args.counter_summary:
         counter_summary(args.counter_summary)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)"
@@ -155,6 +161,7 @@ def main():
         return
 
     # ---- eager reference outputs and launch configurations ------------------------------------
+    mark_leg(torch, stream, "sweep")
     launch_cfgs = []
     with torch.cuda.stream(stream):
         for case in cases:
@@ -228,6 +235,7 @@ def main():
     kern_time, kern_flop, kern_launch = {}, {}, {}
     # one untimed pass over every shape first: whichever shape is timed first after the step loop
     # measures slow (20 against 14 us on 64x2112x7168, 89 against 77 us on 4096x7168x2048)
+    mark_leg(torch, stream, "sweep_per_shape")
     for i in range(len(cases)):
         read_flush()
         replay(shape_graphs[i])
@@ -545,10 +553,7 @@ def bench_read_floor(torch, dev, stream, per, read_flush, reps):
     buffer copy, after a read-only 1 GiB buffer read.  Adds read_floor_us and frac_read_floor
     (read time / GEMM time) to the per-shape rows."""
     import ctypes
-    lib = ctypes.CDLL(os.path.join(ROOT, "fp8_block_scaled_x128_amd", "libreadprobe.so"))
-    lib.read_probe.restype = ctypes.c_int
-    lib.read_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                               ctypes.c_void_p]
+    lib = probe_lib()
     rows = [p for p in per if p["M"] <= 128]
     if not rows:
         return {}
@@ -560,6 +565,7 @@ def bench_read_floor(torch, dev, stream, per, read_flush, reps):
     sp = ctypes.c_void_p(stream.cuda_stream)
     t0 = time.time()
     out = []
+    mark_leg(torch, stream, "read_floor")
     for p, nb in zip(rows, nbytes):
         best = None
         for wgs in READ_WGS:
@@ -598,6 +604,188 @@ def bench_read_floor(torch, dev, stream, per, read_flush, reps):
                 per_shape=out)
 
 
+def _kernel_label(name):
+    """A dispatch's kernel name without its return type and trailing parameter list."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    if name.endswith(")"):
+        depth = 0
+        for i in range(len(name) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(name[i], 0)
+            if depth == 0:
+                return name[:i].rstrip()
+    return name
+
+
+def trace_dispatches(folder):
+    """[(start ns, end ns, kernel label, workgroups)] of every dispatch in one rocprofv3
+    --kernel-trace csv output folder, in start order."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no kernel_trace.csv under %s" % folder)
+    out = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
+            wg = max(1, int(r.get("Workgroup_Size_X") or r.get("Workgroup_Size") or 1))
+            # grid in work-items (a multiple of the workgroup size), else already in workgroups
+            wgs = grid // wg if grid >= wg and grid % wg == 0 else grid
+            out.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _kernel_label(r["Kernel_Name"]), wgs))
+    out.sort()
+    return out
+
+
+def legs_of(dispatches):
+    """{leg: [(label, duration us)]} of the library dispatches (kernels in namespace fp8gemm),
+    attributed to the leg of the last marker before them (mark_leg)."""
+    legs = {}
+    cur = None
+    for t0, t1, label, wgs in dispatches:
+        if label.endswith("read_probe_kernel<4>") and 1 <= wgs <= len(LEGS):
+            cur = LEGS[wgs - 1]
+            legs.setdefault(cur, [])
+        elif cur is not None and label.startswith("fp8gemm::"):
+            legs[cur].append((label, (t1 - t0) * 1e-3))
+    return legs
+
+
+def _stats(ds):
+    a = np.array(ds, dtype=np.float64)
+    return len(a), float(a.mean()), float(a.min()), float(a.max()), float(a.sum())
+
+
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+             "python3 bench.py --steps 5 --warmup 2 > <bench json>")
+TRACE_SUMMARY_CMD = "python3 bench.py --trace-summary <dir> <bench json>"
+
+
+def trace_summary(folder, bench_json):
+    """Kernel durations per leg of a benchmark run under rocprofv3 --kernel-trace, beside the
+    run's own HIP-event figures (its JSON line): writes profiles/kernel_stats_dense_sweep_bench.txt
+    (the sweep's kernels, and the dominant kernel's rocprofv3 average against the benchmark's
+    avg_launch_us), profiles/kernel_stats_grouped_moe_bench.txt and
+    profiles/kernel_stats_quantize_1x128_bench.txt."""
+    line = None
+    for ln in open(bench_json):
+        ln = ln.strip()
+        if ln.startswith("{"):
+            line = json.loads(ln)
+    if line is None:
+        raise SystemExit("no JSON line in %s" % bench_json)
+    legs = legs_of(trace_dispatches(folder))
+    missing = [l for l in LEGS if l not in legs]
+    if missing:
+        raise SystemExit("the trace has no marker for legs %s" % missing)
+    head = ("command: %s\nsummary: %s\nsource hash of the tiled kernel: %s\n"
+            % (TRACE_CMD, TRACE_SUMMARY_CMD, kernel_source_hash()))
+
+    def table(rows):
+        by = {}
+        for label, us in rows:
+            by.setdefault(label, []).append(us)
+        out = ["%-78s %6s %10s %10s %10s %12s" % ("kernel", "calls", "avg us", "min us", "max us", "total us")]
+        for label, ds in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+            n, avg, mn, mx, tot = _stats(ds)
+            out.append("%-78s %6d %10.2f %10.2f %10.2f %12.1f" % (label, n, avg, mn, mx, tot))
+        return "\n".join(out) + "\n"
+
+    # ---- dense sweep ---------------------------------------------------------------------------
+    rf = line["roofline"]
+    dom = "fp8gemm::" + DOMINANT_KERNEL
+    if not rf["kernel"].startswith("nt tile=256x256 waves=4x2 stages=2"):
+        raise SystemExit("the run's dominant kernel (%s) is not %s" % (rf["kernel"], DOMINANT_KERNEL))
+    timed = [us for label, us in legs["sweep_per_shape"] if label == dom]
+    everywhere = [us for leg in ("sweep", "sweep_per_shape") for label, us in legs[leg] if label == dom]
+    with open(os.path.join(ROOT, "profiles", "kernel_stats_dense_sweep_bench.txt"), "w") as f:
+        f.write("Kernel durations of the dense sweep legs of one benchmark run (rocprofv3 --kernel-trace --stats)\n")
+        f.write(head)
+        f.write("workload: the 18-GEMM dense sweep (M in {64,128,4096} x (N,K) in {(2112,7168),(24576,1536),"
+                "(32768,512),(7168,16384),(4096,7168),(7168,2048)}); template arguments BM, BN, waves M, waves N,\n"
+                "stages, layout (0 dense), N, K (N and K nonzero: the kernels specialised at run time).\n\n")
+        for leg, what in (("sweep", "eager reference calls, graph checks, warm-up and the timed steps (graph replays)"),
+                          ("sweep_per_shape", "per-shape graphs of 4 launches: one untimed pass, then 5 timed"),
+                          ("specialized", "the same shapes with the kernels specialised to N and K")):
+            f.write("leg %s: %s\n" % (leg, what))
+            f.write(table(legs[leg]) + "\n")
+        n, avg, mn, mx, _ = _stats(timed)
+        f.write("dominant kernel %s (%s):\n" % (DOMINANT_KERNEL, rf["kernel"]))
+        f.write("  rocprofv3, per-shape leg: %d dispatches, average %.2f us (min %.2f, max %.2f)\n" % (n, avg, mn, mx))
+        n2, avg2, _, _, _ = _stats(everywhere)
+        f.write("  rocprofv3, every sweep dispatch of it: %d, average %.2f us\n" % (n2, avg2))
+        f.write("  bench.py, same run (HIP events around the per-shape graphs): avg_launch_us %.2f over %d launches "
+                "per step, achieved %.1f TFLOP/s (frac %.4f of %.0f)\n"
+                % (rf["avg_launch_us"], rf["launches_per_step"], rf["achieved"], rf["frac"], rf["peak"]))
+        f.write("  ratio bench / rocprofv3 (per-shape leg): %.4f\n" % (rf["avg_launch_us"] / avg))
+        f.write("\nper-shape figures of the same run (bench.py):\n")
+        for p in line["per_shape"]:
+            f.write("  %5d x %5d x %5d  %8.2f us  %7.1f TFLOP/s  %7.1f GB/s  %s\n"
+                    % (p["M"], p["N"], p["K"], p["us"], p["tflops"], p["gbs"], p["config"]))
+    # ---- grouped, MoE and quantiser legs ------------------------------------------------------------
+    bench_us = {}
+    for k, v in (line.get("grouped") or {}).items():
+        bench_us[k] = (v["us"], v["config"])
+    for k, v in (line.get("moe_expert_chain") or {}).items():
+        bench_us["moe_" + k] = (v["us"], v["config"])
+    for k, v in (line.get("quantize_1x128") or {}).items():
+        bench_us["quantize_" + k] = (v["us"], v["config"])
+    for fname, title, names in (
+            ("kernel_stats_grouped_moe_bench.txt", "the grouped, FP8 x FP4 and MoE-chain legs",
+             ("contiguous_cfg2", "contiguous_cfg3", "masked_cfg4", "masked_fp8xfp4_cfg4", "moe_chain",
+              "moe_first_layer", "moe_swiglu_quantize", "moe_second_layer")),
+            ("kernel_stats_quantize_1x128_bench.txt", "the 1x128 activation quantiser legs",
+             ("quantize_dense_32768x7168", "quantize_masked_16x256x7168"))):
+        with open(os.path.join(ROOT, "profiles", fname), "w") as f:
+            f.write("Kernel durations of %s of one benchmark run (rocprofv3 --kernel-trace --stats)\n" % title)
+            f.write(head)
+            f.write("per leg: every library dispatch after the leg's marker (the leg's first eager call, then its "
+                    "graph: one untimed replay and the timed ones); bench us = the same run's HIP-event time per "
+                    "call.\n\n")
+            for leg in names:
+                us, cfg = bench_us.get(leg, (float("nan"), ""))
+                f.write("leg %s: bench %.2f us per call (%s)\n" % (leg, us, cfg))
+                f.write(table(legs[leg]) + "\n")
+    print("wrote profiles/kernel_stats_{dense_sweep,grouped_moe,quantize_1x128}_bench.txt; dominant kernel: "
+          "rocprofv3 %.2f us, bench %.2f us" % (avg, rf["avg_launch_us"]))
+
+
+_PROBE = {}
+
+
+def probe_lib():
+    """libreadprobe.so (the streaming-read kernel of the read floor and of the leg markers)."""
+    import ctypes
+    if "lib" not in _PROBE:
+        lib = ctypes.CDLL(os.path.join(ROOT, "fp8_block_scaled_x128_amd", "libreadprobe.so"))
+        lib.read_probe.restype = ctypes.c_int
+        lib.read_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+        _PROBE["lib"] = lib
+    return _PROBE["lib"]
+
+
+# the benchmark's legs in run order; mark_leg puts the start of each into a kernel trace
+LEGS = ("sweep", "sweep_per_shape", "read_floor", "specialized", "contiguous_cfg2", "contiguous_cfg3",
+        "masked_cfg4", "masked_fp8xfp4_cfg4", "quantize_dense_32768x7168", "quantize_masked_16x256x7168",
+        "moe_chain", "moe_first_layer", "moe_swiglu_quantize", "moe_second_layer", "moe_setup")
+
+
+def mark_leg(torch, stream, name):
+    """Mark the start of leg `name` in a kernel trace: one read_probe launch on the launch stream,
+    4 loads deep (the read floor uses 8 and 16), with (leg number + 1) workgroups, that reads 16
+    bytes.  Every library dispatch after it (in start order) belongs to its leg."""
+    import ctypes
+    if "buf" not in _PROBE:
+        _PROBE["buf"] = torch.zeros(64, dtype=torch.int32, device=torch.device("cuda", torch.cuda.current_device()))
+    buf = _PROBE["buf"]
+    rc = probe_lib().read_probe(buf.data_ptr(), 16, LEGS.index(name) + 1, 4, buf[16:].data_ptr(),
+                                ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise RuntimeError("leg marker launch failed")
+
+
 def W_bytes(p):
     import workloads as W
     return W.dense_work(p["M"], p["N"], p["K"])[1]
@@ -616,6 +804,7 @@ def bench_specialized(fg, torch, stream, cases, per, replay, read_flush, reps):
     against the table kernel's."""
     t0 = time.time()
     rows = []
+    mark_leg(torch, stream, "specialized")
     for i, case in enumerate(cases):
         compile_ms = fg.specialize_nt(case["M"], case["N"], case["K"])
         ref = case["copies"][0]["D"].clone()
@@ -734,6 +923,7 @@ def bench_grouped(fg, W, torch, dev, stream, reps=10, cpu=False):
             flop, byts = work(counts, N, K, index_bytes=4 * len(counts))
         calls = max(GROUPED_CALLS, ncopy)
         torch.cuda.synchronize()        # operand copies are made on the default stream
+        mark_leg(torch, stream, name)
         with torch.cuda.stream(stream):
             call(ops[0])
         cfg = fg.last_config()
@@ -853,10 +1043,12 @@ def bench_moe_chain(fg, W, torch, dev, stream, reps=5, cpu=False):
             copies.append(dict({k: v.clone() for k, v in w0.items()}, **buffers()))
         # every copy's buffers hold the previous step's results of that copy (chain order)
         torch.cuda.synchronize()        # weight copies are made on the default stream
+        mark_leg(torch, stream, "moe_setup")
         with torch.cuda.stream(stream):
             for c in copies[:ncopy]:
                 steps["chain"][1](c)
         stream.synchronize()
+        mark_leg(torch, stream, "moe_" + name)      # the step's own launches follow
         with torch.cuda.stream(stream):
             call(copies[0])
         stream.synchronize()
@@ -939,6 +1131,7 @@ def bench_quantize(fg, W, torch, dev, stream, reps=5):
     legs = (("dense_32768x7168", dense, W.quantize_work(M, K)),
             ("masked_16x256x7168", masked, W.quantize_work(int(mm.sum()), K)))
     for name, call, byts in legs:
+        mark_leg(torch, stream, "quantize_" + name)
         with torch.cuda.stream(stream):
             call(0)
             call(1)
