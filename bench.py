@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-grouped", action="store_true")
+    p.add_argument("--no-library-reference", action="store_true",
+                   help="skip the context leg timing the vendor library's plain FP8 GEMM")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU-oracle sample time")
     p.add_argument("--counters", action="store_true",
                    help="launch every kernel the benchmark times (the 18 sweep GEMMs, the grouped "
@@ -277,6 +279,7 @@ def main():
                     share_of_step=round(kern_time[dom] / sum(kern_time.values()), 3))
 
     read_floor = bench_read_floor(torch, dev, stream, per, read_flush, reps)
+    library = {} if args.no_library_reference else bench_library_reference(torch, dev, stream, per, read_flush, reps)
     specialized = bench_specialized(fg, torch, stream, cases, per, replay, read_flush, reps)
 
     grouped = {}
@@ -317,6 +320,7 @@ def main():
         "moe_expert_chain": moe,
         "specialized": specialized,
         "read_floor": read_floor,
+        "library_reference": library,
     }
     print(json.dumps(line), flush=True)
 
@@ -769,7 +773,8 @@ def probe_lib():
 # the benchmark's legs in run order; mark_leg puts the start of each into a kernel trace
 LEGS = ("sweep", "sweep_per_shape", "read_floor", "specialized", "contiguous_cfg2", "contiguous_cfg3",
         "masked_cfg4", "masked_fp8xfp4_cfg4", "quantize_dense_32768x7168", "quantize_masked_16x256x7168",
-        "moe_chain", "moe_first_layer", "moe_swiglu_quantize", "moe_second_layer", "moe_setup")
+        "moe_chain", "moe_first_layer", "moe_swiglu_quantize", "moe_second_layer", "moe_setup",
+        "library_reference")
 
 
 def mark_leg(torch, stream, name):
@@ -784,6 +789,72 @@ def mark_leg(torch, stream, name):
                                 ctypes.c_void_p(stream.cuda_stream))
     if rc != 0:
         raise RuntimeError("leg marker launch failed")
+
+
+def bench_library_reference(torch, dev, stream, per, read_flush, reps):
+    """Context, not part of value: the vendor library's plain FP8 GEMM (torch._scaled_mm, served by
+    hipBLASLt) on the prefill shapes (M >= 1024), with one fp32 scale per tensor and with one per
+    row of A and column of B, timed as the sweep GEMMs (HIP events on the launch stream around a
+    graph of COPIES launches on rotated operand copies, after a read-only 1 GiB buffer read).  It
+    computes a coarser-scaled product -- no 128-wide K blocks, no per-block promotion -- so it is
+    a ceiling for what this machine's matrix cores reach on an FP8 GEMM of the same shape, not
+    the same operation.  Operands are random E4M3 values; outputs are not compared."""
+    rows = [p for p in per if p["M"] >= 1024]
+    out = []
+    t0 = time.time()
+    mark_leg(torch, stream, "library_reference")
+    for p in rows:
+        M, N, K = p["M"], p["N"], p["K"]
+        g = torch.Generator(device=dev).manual_seed(M + N + K)
+        ops = [((torch.randn(M, K, device=dev, generator=g) * 0.5).to(torch.float8_e4m3fn),
+                (torch.randn(N, K, device=dev, generator=g) * 0.5).to(torch.float8_e4m3fn)) for _ in range(COPIES)]
+        one = torch.ones((), device=dev)
+        sa_row, sb_col = torch.ones(M, 1, device=dev), torch.ones(1, N, device=dev)
+        torch.cuda.synchronize()
+        row = dict(M=M, N=N, K=K, us_this=p["us"])
+        for kind, sa, sb in (("per_tensor", one, one), ("per_row_col", sa_row, sb_col)):
+            def call(r, sa=sa, sb=sb):
+                a, b = ops[r]
+                torch._scaled_mm(a, b.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+            try:
+                with torch.cuda.stream(stream):
+                    for r in range(COPIES):
+                        call(r)
+                stream.synchronize()
+            except RuntimeError as e:
+                row[kind] = "unavailable: %s" % str(e).splitlines()[0][:100]
+                continue
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                for r in range(COPIES):
+                    call(r)
+            read_flush()
+            replay_on(stream, gr)
+            stream.synchronize()
+            ts = []
+            for _ in range(reps):
+                read_flush()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                replay_on(stream, gr)
+                e1.record(stream)
+                stream.synchronize()
+                ts.append(e0.elapsed_time(e1) / COPIES)
+            us = float(np.mean(ts)) * 1e3
+            row[kind + "_us"] = round(us, 2)
+            row[kind + "_frac_mfma"] = round(2 * M * N * K / (us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4)
+            del gr
+        out.append(row)
+        del ops
+    torch.cuda.synchronize()
+    if out:
+        log("library FP8 GEMM (per-tensor scales) on %d prefill shapes in %.1f s: this kernel / library %s" % (
+            len(out), time.time() - t0,
+            " ".join("%.2f" % (r["us_this"] / r["per_tensor_us"]) for r in out if "per_tensor_us" in r)))
+    return dict(what="torch._scaled_mm (hipBLASLt), E4M3 x E4M3 -> bf16, one scale per tensor / per row and "
+                     "column: a coarser-scaled GEMM without 128-wide block promotion (context only)",
+                per_shape=out)
 
 
 def W_bytes(p):
