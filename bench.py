@@ -77,12 +77,17 @@ TRAFFIC_FILE = os.path.join("profiles", "traffic_dense_256x256_m4096_sweep.txt")
 COPY_BYTES = 1 << 30           # calibration copy: reads and writes this many bytes
 
 
+KERNEL_SOURCES = ("fp8gemm_tiled.h", "fp8gemm_device.h", "fp8gemm_args.h", "fp8gemm_kernels.hip",
+                  "stream_kernels.hip", "quantize_kernels.hip", "fp8gemm_internal.h")
+
+
 def kernel_source_hash():
-    """Hash of the sources that make the dense tiled kernel (its body, helpers, argument block and
-    instantiation table)."""
+    """Hash of every source that makes a GPU kernel the counters and traces cover (the tiled
+    kernel's body, helpers, argument block and instantiation table, the masked decode kernel and
+    the quantisers), stamped into each profile summary."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("fp8gemm_tiled.h", "fp8gemm_device.h", "fp8gemm_args.h", "fp8gemm_kernels.hip"):
+    for name in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, "fp8_block_scaled_x128_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
@@ -683,7 +688,7 @@ def trace_summary(folder, bench_json):
     missing = [l for l in LEGS if l not in legs]
     if missing:
         raise SystemExit("the trace has no marker for legs %s" % missing)
-    head = ("command: %s\nsummary: %s\nsource hash of the tiled kernel: %s\n"
+    head = ("command: %s\nsummary: %s\nsource hash of the kernels: %s\n"
             % (TRACE_CMD, TRACE_SUMMARY_CMD, kernel_source_hash()))
 
     def table(rows):
