@@ -118,13 +118,14 @@ int workspace(DeviceState* d, hipStream_t stream, size_t partial_bytes, size_t c
         const size_t bytes = workspace_partial_bytes(d->cus);
         const size_t n = workspace_counters(d->cus);
         if (hipMalloc(&w.partials, bytes) != hipSuccess) return FP8GEMM_ERR_HIP;
+        // on a failure, release what was allocated (the first error is the one reported)
         if (hipMalloc(&w.counters, n * sizeof(int32_t)) != hipSuccess) {
-            hipFree(w.partials);
+            (void)hipFree(w.partials);
             return FP8GEMM_ERR_HIP;
         }
         if (hipMemset(w.counters, 0, n * sizeof(int32_t)) != hipSuccess) {
-            hipFree(w.partials);
-            hipFree(w.counters);
+            (void)hipFree(w.partials);
+            (void)hipFree(w.counters);
             return FP8GEMM_ERR_HIP;
         }
         w.partial_bytes = bytes;

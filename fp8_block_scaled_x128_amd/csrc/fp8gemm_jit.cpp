@@ -187,7 +187,7 @@ int jit_kernel(int device, const KernelEntry& e, int entry, int N, int K, const 
     auto c = std::make_unique<Cached>();
     if (hipModuleLoadData(&c->module, code.data()) != hipSuccess) return FP8GEMM_ERR_HIP;
     if (hipModuleGetFunction(&c->k.fn, c->module, lowered.c_str()) != hipSuccess) {
-        hipModuleUnload(c->module);
+        (void)hipModuleUnload(c->module);
         return FP8GEMM_ERR_HIP;
     }
     int blocks = 0;
