@@ -234,6 +234,7 @@ def main():
     t_total = time.perf_counter() - t_start
     ms_per_step = 1e3 * t_total / args.steps
     gpu_ms_per_step = e_start.elapsed_time(e_end) / args.steps
+    gpu_state = sample_gpu_state()          # right after the timed steps, the part still warm
 
     # ---- per-shape launch times: HIP events around per-shape graphs on the launch stream -------
     reps = 5
@@ -326,6 +327,7 @@ def main():
         "specialized": specialized,
         "read_floor": read_floor,
         "library_reference": library,
+        "gpu_state": gpu_state,
     }
     print(json.dumps(line), flush=True)
 
@@ -758,6 +760,28 @@ def trace_summary(folder, bench_json):
                 f.write(table(legs[leg]) + "\n")
     print("wrote profiles/kernel_stats_{dense_sweep,grouped_moe,quantize_1x128}_bench.txt; dominant kernel: "
           "rocprofv3 %.2f us, bench %.2f us" % (avg, rf["avg_launch_us"]))
+
+
+def sample_gpu_state():
+    """Shader and memory clocks, power and temperature as rocm-smi reports them (one sample, taken
+    by the caller right after a timed region), or the reason there is none.  Context only: under a
+    matrix-core load the shader clock sits below the 2.4 GHz behind the published peaks."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showtemp", "--json"],
+                           capture_output=True, text=True, timeout=30)
+        data = json.loads(r.stdout)
+    except Exception as e:      # no tool, no JSON, or a time-out: the benchmark goes on without it
+        return {"unavailable": str(e)[:200]}
+    out = {}
+    for card, vals in data.items():
+        if not isinstance(vals, dict):
+            continue
+        keep = {k.strip(" :"): v for k, v in vals.items()
+                if any(w in k.lower() for w in ("sclk", "mclk", "fclk", "power", "temperature"))}
+        if keep:
+            out[card] = keep
+    return out or {"unavailable": "rocm-smi printed no clock, power or temperature fields"}
 
 
 _PROBE = {}

@@ -126,3 +126,20 @@ def test_trace_summary_refuses_a_trace_without_markers(tmp_path):
     js.write_text(json.dumps({"roofline": {"kernel": "nt tile=256x256"}}) + "\n")
     with pytest.raises(SystemExit):
         bench.trace_summary(str(tmp_path / "t"), str(js))
+
+
+def test_gpu_state_sample_never_fails(monkeypatch):
+    import subprocess
+
+    class R:
+        stdout = '{"card0": {"sclk clock speed:": "(2100Mhz)", "Current Socket Graphics Package Power (W)": "900", "unrelated": 1}}'
+
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: R())
+    st = bench.sample_gpu_state()
+    assert st == {"card0": {"sclk clock speed": "(2100Mhz)", "Current Socket Graphics Package Power (W)": "900"}}
+
+    def boom(*a, **k):
+        raise FileNotFoundError("rocm-smi")
+
+    monkeypatch.setattr(subprocess, "run", boom)
+    assert "unavailable" in bench.sample_gpu_state()
