@@ -18,6 +18,13 @@
 // process may already hold another ROCm's hipRTC and code-object compiler under the same names
 // (PyTorch wheels bundle their own); in its own namespace the library gets the ROCm compiler it
 // was built with, and its code-generation options are the ahead-of-time build's.
+//
+// That namespace has its own C library, whose environment pointer is the process's array as it
+// was at load time.  The compiler reads the environment on every compile, and setenv (Python's
+// os.environ, among others) frees that array when it grows the environment, so before each
+// compile the namespace's pointer is set to the process's current array, under a lock that
+// serialises the compiles.  As for getenv anywhere, a setenv on another thread while a compile
+// runs is the caller's race.
 
 #include <dlfcn.h>
 #include <hip/hip_runtime.h>
@@ -34,6 +41,8 @@
 #include <tuple>
 #include <type_traits>
 #include <vector>
+
+#include <unistd.h>
 
 #include "fp8gemm.h"
 #include "fp8gemm_internal.h"
@@ -74,6 +83,7 @@ struct Rtc {
     decltype(&hiprtcGetLoweredName) lowered = nullptr;
     decltype(&hiprtcGetCodeSize) code_size = nullptr;
     decltype(&hiprtcGetCode) code = nullptr;
+    char*** environ_slot = nullptr;     // `environ` of the namespace's C library
     std::string error;
 };
 
@@ -107,6 +117,14 @@ const Rtc& rtc() {
         if (!ok) {
             t = Rtc{};
             t.error = path + " lacks a hipRTC entry point";
+            return t;
+        }
+        Lmid_t ns = 0;
+        void* c = dlinfo(h, RTLD_DI_LMID, &ns) == 0 ? dlmopen(ns, "libc.so.6", RTLD_NOW | RTLD_NOLOAD) : nullptr;
+        t.environ_slot = c ? reinterpret_cast<char***>(dlsym(c, "environ")) : nullptr;
+        if (!t.environ_slot) {
+            t = Rtc{};
+            t.error = "cannot find the C library of the namespace of " + path;
         }
         return t;
     }();
@@ -126,6 +144,7 @@ struct Cached {
 };
 
 std::mutex g_mu;
+std::mutex g_compile_mu;    // one compile at a time: the namespace's environment pointer is shared
 std::map<std::tuple<int, int, int, int>, std::unique_ptr<Cached>> g_cache;   // (device, entry, N, K)
 
 }  // namespace
@@ -145,6 +164,8 @@ int jit_compile(const KernelEntry& e, int N, int K, std::vector<char>* code, std
         names.push_back(kJitSourceNames[i]);
     }
     const char* src = "#include \"fp8gemm_tiled.h\"\n";
+    std::lock_guard<std::mutex> lock(g_compile_mu);
+    *r.environ_slot = environ;          // the process's environment as it is now
     Program prog;
     if (r.create(&prog.p, src, "fp8gemm_specialized.hip", (int)headers.size(), headers.data(),
                             names.data()) != HIPRTC_SUCCESS)

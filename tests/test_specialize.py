@@ -6,6 +6,7 @@ loads, no scratch memory), and the entry points reject bad arguments before any 
 import os
 import re
 import subprocess
+import sys
 import tempfile
 
 import pytest
@@ -120,3 +121,50 @@ def test_specialized_entry_validation_errors(lib):
     assert lib.fp8gemm_specialize_nt(0, 8, 128, ctypes.byref(ms)) == 2
     assert lib.fp8gemm_specialize_nt(8, 8, 100, ctypes.byref(ms)) == 2
     assert lib.fp8gemm_specialized_count() == 0
+
+
+ENV_CHURN = r"""
+import ctypes, os, sys
+sys.path.insert(0, sys.argv[1])
+import fp8_block_scaled_x128_amd as fg
+libc = ctypes.CDLL(None)
+libc.dlmopen.restype = ctypes.c_void_p
+libc.dlmopen.argtypes = [ctypes.c_long, ctypes.c_char_p, ctypes.c_int]
+libc.dlsym.restype = ctypes.c_void_p
+libc.dlsym.argtypes = [ctypes.c_void_p, ctypes.c_char_p]
+RTLD_NOW, RTLD_NOLOAD = 2, 4
+main_environ = lambda: ctypes.c_void_p.in_dll(libc, "environ").value
+
+fg.specialized_code_object(0, 64, 64, 1, 4, 4, 256, 512)     # loads the compiler
+ns = [lm for lm in range(1, 16) if libc.dlmopen(lm, b"libhiprtc.so.7", RTLD_NOW | RTLD_NOLOAD)]
+assert len(ns) == 1, ns
+slot = libc.dlsym(libc.dlmopen(ns[0], b"libc.so.6", RTLD_NOW | RTLD_NOLOAD), b"environ")
+ns_environ = ctypes.c_void_p.from_address(slot)
+
+for i in range(40):                                          # grow the environment: its array moves
+    os.environ["FP8GEMM_TEST_CHURN_%d" % i] = "x" * (i + 1)
+for i in range(40):
+    os.environ.pop("FP8GEMM_TEST_CHURN_%d" % i)
+os.environ["FP8GEMM_TEST_LATE"] = "1"
+code, sym = fg.specialized_code_object(0, 64, 64, 1, 4, 4, 384, 512)
+assert code[:4] == b"\x7fELF", sym
+assert ns_environ.value == main_environ(), "the namespace reads a stale environment"
+
+# an environment pointer the compiler cannot read (as a freed array may be) is replaced before
+# the compile reads it
+bad = (ctypes.c_void_p * 3)(0x10, 0x10, None)
+ns_environ.value = ctypes.addressof(bad)
+code, sym = fg.specialized_code_object(0, 64, 64, 1, 4, 4, 512, 512)
+assert code[:4] == b"\x7fELF" and ns_environ.value == main_environ()
+print("ok")
+"""
+
+
+def test_compile_after_the_environment_moved(lib):
+    """The compiler lives in a linker namespace of its own, with its own C library, whose environment
+    pointer is the process's array as it was at load time; setenv frees that array when it grows
+    the environment, and every compile reads the environment.  Before each compile the namespace's
+    pointer must be the process's current one (checked after a real move of the array, and after
+    the pointer was set to memory that cannot be read).  Runs in a child process."""
+    r = subprocess.run([sys.executable, "-c", ENV_CHURN, ROOT], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), (r.returncode, r.stdout[-2000:], r.stderr[-2000:])
