@@ -95,10 +95,12 @@ int device_state(DeviceState** out) {
 
 // Capacity of a stream's split-K workspace.  An automatically chosen split launch has at most one
 // unit per CU (pick_split), and the largest tile compiled with the split-K exchange is 128 x 256
-// fp32, so cus * 128 KiB of partials and one counter per unit cover every such launch.  A forced
-// configuration (FP8GEMM_FORCE_CONFIG) beyond it is refused.
-constexpr size_t kMaxSplitTileBytes = 128 * 256 * sizeof(float);
-size_t workspace_partial_bytes(int cus) { return (size_t)std::max(cus, 1) * kMaxSplitTileBytes; }
+// fp32 (128 KiB); a stream-K launch of 256 x 256 tiles (one workgroup per CU) keeps two partial
+// tiles per workgroup (512 KiB).  So cus * 512 KiB of partials and one counter per unit cover
+// every such launch.  A forced configuration (FP8GEMM_FORCE_CONFIG) beyond it is refused.
+constexpr int kStreamKMinBlocks = 24;
+constexpr size_t kMaxPartialBytesPerCu = 2 * 256 * 256 * sizeof(float);
+size_t workspace_partial_bytes(int cus) { return (size_t)std::max(cus, 1) * kMaxPartialBytesPerCu; }
 size_t workspace_counters(int cus) { return std::max<size_t>((size_t)cus, 4096); }
 
 // The split-K workspace of `stream`: allocated once, at full capacity, the first time the stream
@@ -322,6 +324,43 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream,
     a.err = d->err;
     a.ws = nullptr;
     a.counters = nullptr;
+    int64_t slots = (int64_t)cus * (jk ? jk->occupancy : d->occupancy[c.entry]);
+
+    // Stream-K for the tiles after the last full round of whole tiles (dense 256-row tiles, which
+    // take no K split): instead of a last, partly idle round, the leftover tiles' K blocks are
+    // shared out evenly over the grid (sk_start in fp8gemm_args.h), and tiles shared by several
+    // workgroups are summed by the exchange in the kernel.  Taken when it saves a workgroup at
+    // least kStreamKMinBlocks K blocks: on MI355X a partly empty round costs as much as a full one
+    // (4096 x N x 16384 with 384, 448 and 512 tiles on 256 CUs: 464, 477 and 496 us), while the
+    // exchange costs about a K block's time per partial tile written or read.
+    // FP8GEMM_STREAMK=0 turns it off, =1 on wherever leftover tiles exist.  Not for the run-time
+    // specialised kernels (compiled without the exchange) nor for the allocation-free entry point.
+    bool streamk = false;
+    if (layout == kDense && e.kind == kKindTiled && e.bm == 256 && a.splits == 1 && !noalloc && !jk) {
+        const int64_t P = slots, T = a.units;
+        const int64_t full = T / P, R = T % P;
+        const int64_t total = R * a.nkb, per = total / std::max<int64_t>(P, 1), extra = total % std::max<int64_t>(P, 1);
+        const int64_t saved = a.nkb - per - (extra > 0 ? 1 : 0);
+        const char* f = std::getenv("FP8GEMM_STREAMK");
+        const bool want = (f && *f) ? f[0] == '1' : saved >= kStreamKMinBlocks;
+        const size_t need = (size_t)(2 * P) * e.bm * e.bn * sizeof(float);
+        if (want && R > 0 && per >= 1 && need <= workspace_partial_bytes(d->cus)) {
+            // a stream with no workspace that is being captured keeps whole tiles (UNSUPPORTED
+            // from workspace: nothing may be allocated during capture)
+            Workspace* w = nullptr;
+            st = workspace(d, stream, need, (size_t)R, &w);
+            if (st != FP8GEMM_OK && st != FP8GEMM_ERR_UNSUPPORTED) return st;
+            if (st == FP8GEMM_OK) {
+                streamk = true;
+                a.units = (int32_t)(full * P);
+                a.sk_tiles = (int32_t)R;
+                a.sk_per = (int32_t)per;
+                a.sk_extra = (int32_t)extra;
+                a.ws = w->partials;
+                a.counters = w->counters;
+            }
+        }
+    }
     if (a.splits > 1) {
         const int64_t tiles = (int64_t)a.units / a.splits;
         const size_t partial_bytes = (size_t)a.units * e.bm * e.bn * sizeof(float);
@@ -338,8 +377,8 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream,
             a.counters = w->counters;
         }
     }
-    int64_t slots = (int64_t)cus * (jk ? jk->occupancy : d->occupancy[c.entry]);
-    int64_t grid = std::min<int64_t>(a.units, slots);
+    // a stream-K launch needs exactly `slots` workgroups (its schedule is cut for that many)
+    int64_t grid = streamk ? slots : std::min<int64_t>(a.units, slots);
     if (grid <= 0) return FP8GEMM_OK;
     const char* lname = layout == kDense ? "nt" : (layout == kContiguous ? "contiguous" : (fp4 ? "masked fp8xfp4" : "masked"));
     if (e.kind == kKindStream)
@@ -353,6 +392,11 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream,
                       "%s%s tile=%dx%d waves=%dx%d stages=%d split=%d kb_per_split=%d units=%lld grid=%lld",
                       lname, jk ? " specialized" : "", e.bm, e.bn, e.waves_m, e.waves_n, e.stages, a.splits,
                       a.kb_per_split, (long long)a.units, (long long)grid);
+    if (streamk) {
+        const size_t n = std::strlen(g_last_config);
+        std::snprintf(g_last_config + n, sizeof g_last_config - n, " streamk_tiles=%d blocks_per_wg=%d",
+                      a.sk_tiles, a.sk_per);
+    }
     if (std::getenv("FP8GEMM_LOG")) std::fprintf(stderr, "[fp8gemm] %s\n", g_last_config);
     if (jk) {
         // the argument block travels by value with its size stated: HIP copies the bytes into the

@@ -34,6 +34,20 @@ __host__ __device__ inline uint32_t fast_div(uint32_t n, const FastDiv& f) {
     return (hi + n) >> f.shift;
 }
 
+// Stream-K schedule of the tiles left over after the last full round of tiles (dense layout,
+// 256-row tiles).  The leftover tiles' K blocks form one sequence in (tile, K block) order;
+// workgroup w (logical id, 0 <= w < P) takes blocks [sk_start(w), sk_start(w + 1)), with
+// sk_start(w) = w * per + min(w, extra): the first `extra` workgroups take per + 1 blocks, the
+// others per.  A workgroup's range is shorter than a tile's K extent, so it touches at most two
+// tiles (its segments 0 and 1).
+__host__ __device__ inline int sk_start(int w, int per, int extra) { return w * per + (w < extra ? w : extra); }
+
+// The workgroup whose range holds block g of the sequence (per >= 1).
+__host__ __device__ inline int sk_owner(int g, int per, int extra) {
+    const int big = extra * (per + 1);
+    return g < big ? g / (per + 1) : extra + (g - big) / per;
+}
+
 // Everything one launch needs; passed by value as the kernel argument.
 struct KernelArgs {
     const uint8_t* A;           // [rows_total][K] E4M3 codes
@@ -61,6 +75,9 @@ struct KernelArgs {
     FastDiv div_band_units;     // group_m * tiles_n
     FastDiv div_band_h;         // group_m (height of a full band)
     FastDiv div_band_h_last;    // height of the last band, tiles_m - group_m * (bands - 1)
+    // stream-K (0 sk_tiles: none): the tiles after the first `units` take the schedule above,
+    // sk_per and sk_extra for the grid's P workgroups; partials in ws slots 2w + segment
+    int32_t sk_tiles, sk_per, sk_extra;
 };
 
 }  // namespace fp8gemm

@@ -89,6 +89,8 @@ struct Tile {
     static_assert(SPB == 1 || IN <= 2, "paired slices: decode tiles (at most two N sub-tiles per wave)");
     // split-K partial reduction is compiled for tiles small enough to need it (decode shapes)
     static constexpr bool SPLITK = BM * BN <= 128 * 256;
+    // the dense 256-row tiles take leftover tiles stream-K (after the last full round of tiles)
+    static constexpr bool STREAMK = LAYOUT == kDense && BM == 256;
     // Epilogue staging: each wave writes its WM x WN bf16 results row-major into a private LDS
     // region (after the K loop, over the ring), then stores whole 16-byte chunks of rows.  The
     // row pitch holds an odd number of 16-byte units, so the 8-byte writes of 32 lanes in the
@@ -137,12 +139,31 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
     int logical = blockIdx.x;
     if ((P & 7) == 0) logical = (blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3);
 
-    for (int unit = logical; unit < args.units; unit += P) {
+    // Units [0, units) are whole tiles (or K splits of them); with stream-K each workgroup then
+    // takes two more iterations, its segments 0 and 1 of the leftover tiles (either may be empty).
+    // The run-time specialised variants (N or K fixed) keep whole tiles: with N fixed the compiler
+    // keeps more values live and the exchange code would spill.
+    constexpr bool SK = T::STREAMK && NC == 0 && KC == 0;
+    const int sk_iters = (SK && args.sk_tiles > 0) ? 2 * P : 0;
+    for (int unit = logical; unit < args.units + sk_iters; unit += P) {
+        // ---- a stream-K segment: K blocks [sk_kb0, sk_kb0 + sk_nks) of leftover tile sk_tile --
+        const bool sk = SK && unit >= args.units;
+        const int sk_seg = sk ? (unit - args.units) / P : 0;
+        int sk_tile = 0, sk_kb0 = 0, sk_nks = 0;
+        if (sk) {
+            const int r0 = sk_start(logical, args.sk_per, args.sk_extra);
+            const int r1 = sk_start(logical + 1, args.sk_per, args.sk_extra);
+            const int g = sk_seg == 0 ? r0 : (r0 / nkb + 1) * nkb;      // segment 1: the next tile's start
+            if (g >= r1) continue;                                       // uniform: no such segment
+            sk_tile = g / nkb;
+            sk_kb0 = g - sk_tile * nkb;
+            sk_nks = min(nkb - sk_kb0, r1 - g);
+        }
         // ---- decode the unit: split s fastest, then M tile, N tile, group -------------------
         // (uniform integer work on the scalar unit: multiply-shift divisions by launch constants)
         uint32_t u = (uint32_t)unit;
-        const uint32_t tile_id = fast_div(u, args.div_splits);   // unit / splits
-        const int split = (int)(u - tile_id * (uint32_t)args.splits);
+        const uint32_t tile_id = sk ? (uint32_t)(args.units + sk_tile) : fast_div(u, args.div_splits);
+        const int split = sk ? 0 : (int)(u - tile_id * (uint32_t)args.splits);
         u = tile_id;
         int tm, tn;
         if (args.group_m > 1) {
@@ -169,8 +190,8 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
         const int gidx = (int)u;                       // group (masked layout), else 0
         const int m0 = tm * BM;                        // first row of the tile (within group)
         const int n0 = tn * BN;
-        const int kb0 = split * args.kb_per_split;
-        const int kb1 = min(nkb, kb0 + args.kb_per_split);
+        const int kb0 = sk ? sk_kb0 : split * args.kb_per_split;
+        const int kb1 = sk ? sk_kb0 + sk_nks : min(nkb, kb0 + args.kb_per_split);
         const int nks = kb1 - kb0;
 
         // ---- rows of A, group of B ---------------------------------------------------------
@@ -523,6 +544,88 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
 #pragma unroll
                                 for (int j = 0; j < T::JM; ++j)
                                     acc[i2][j] = (s0 + c == 0) ? x[c][i2][j] : acc[i2][j] + x[c][i2][j];
+                        }
+                    }
+                }
+            }
+        }
+        if constexpr (SK) {
+            if (sk) {
+                // Stream-K exchange between the workgroups that share a leftover tile (segments
+                // from consecutive workgroups w_a..w_b, in K order).  As the split-K exchange
+                // above: partials are written and read with agent-coherent (sc1) accesses, each
+                // into its writer's slot 2w + segment, and an agent-scope counter finds the last
+                // to arrive, which sums the partials in K order.  The tile's first segment comes
+                // first in that order, so when it is the last to arrive it adds the others to its
+                // own accumulators and writes nothing; it checks the counter before writing, and it
+                // is usually last (its workgroup reaches it at the end of its range, the other
+                // segments at the start of theirs).  Any other last arrival re-reads every partial,
+                // its own included, in K order.
+                const int g0 = sk_tile * nkb;
+                const int w_a = sk_owner(g0, args.sk_per, args.sk_extra);
+                const int w_b = sk_owner(g0 + nkb - 1, args.sk_per, args.sk_extra);
+                const bool head = logical == w_a;
+                const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                    uniform_ptr(args.ws), 0, 2 * P * BM * BN * 4, kBufferFlags);
+                const int lane_off = (wave * (T::WM * T::WN) + lane * 4) * 4;
+                auto slot_of = [&](int w2) {
+                    const int seg2 = (sk_start(w2, args.sk_per, args.sk_extra) / nkb == sk_tile) ? 0 : 1;
+                    return (2 * w2 + seg2) * (BM * BN * 4) + lane_off;
+                };
+                bool last = false;
+                if (head) {
+                    if (tid == 0)
+                        s_flag = __hip_atomic_load(args.counters + sk_tile, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT) == w_b - w_a;
+                    __syncthreads();
+                    last = s_flag != 0;
+                    __syncthreads();          // every wave has read s_flag before it is written again
+                }
+                if (!last) {
+                    const int own = slot_of(logical);
+#pragma unroll
+                    for (int i2 = 0; i2 < T::IN; ++i2)
+#pragma unroll
+                        for (int j = 0; j < T::JM; ++j)
+                            __builtin_amdgcn_raw_buffer_store_b128(acc[i2][j], ws_rsrc, own + (i2 * T::JM + j) * 1024, 0,
+                                                                   kSc1);
+                    wait_vmcnt<0>();
+                    __syncthreads();
+                    if (tid == 0) {
+                        const int old = __hip_atomic_fetch_add(args.counters + sk_tile, 1, __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT);
+                        s_flag = (old == w_b - w_a);
+                    }
+                    __syncthreads();
+                    last = s_flag != 0;
+                }
+                if (last && tid == 0)   // ready for the next launch
+                    __hip_atomic_store(args.counters + sk_tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                store_direct = last;
+                if (last) {
+                    constexpr int NSUB = T::IN * T::JM;
+                    constexpr int CH = NSUB < 8 ? NSUB : 8;      // sub-tiles of one read batch
+                    if (!head) {
+                        const int off_a = slot_of(w_a);
+#pragma unroll
+                        for (int i2 = 0; i2 < T::IN; ++i2)
+#pragma unroll
+                            for (int j = 0; j < T::JM; ++j)
+                                acc[i2][j] = __builtin_amdgcn_raw_buffer_load_b128(ws_rsrc, off_a + (i2 * T::JM + j) * 1024,
+                                                                                   0, kSc1);
+                    }
+                    for (int w2 = w_a + 1; w2 <= w_b; ++w2) {
+                        const int off2 = slot_of(w2);
+#pragma unroll
+                        for (int c0 = 0; c0 < NSUB; c0 += CH) {
+                            v4f x[CH];
+#pragma unroll
+                            for (int c = 0; c < CH; ++c)
+                                if (c0 + c < NSUB)
+                                    x[c] = __builtin_amdgcn_raw_buffer_load_b128(ws_rsrc, off2 + (c0 + c) * 1024, 0, kSc1);
+#pragma unroll
+                            for (int c = 0; c < CH; ++c)
+                                if (c0 + c < NSUB) acc[(c0 + c) / T::JM][(c0 + c) % T::JM] += x[c];
                         }
                     }
                 }

@@ -33,12 +33,16 @@
  *   - Results are deterministic: the same inputs give the same bits, whatever the launch
  *     configuration's timing (split-K partials are summed in a fixed order).
  *   - Split-K workspace: each stream has its own library-owned workspace (fp32 partial tiles
- *     and arrival counters, CUs x 128 KiB + 16 KiB on the stream's device).  It is allocated
- *     once, at full size, by fp8gemm_prepare_stream or by the first call on the stream whose
- *     launch splits K (one hipMalloc pair and one blocking hipMemset), and it is never freed,
+ *     and arrival counters, CUs x 512 KiB + 16 KiB on the stream's device).  It serves the
+ *     K splits of decode-sized launches and the stream-K schedule of large dense launches (the
+ *     256 x 256 tiles left over after the last full round of tiles, shared out over every CU
+ *     by K block).  It is allocated once, at full size, by fp8gemm_prepare_stream or by the
+ *     first call on the stream whose launch needs it (one hipMalloc pair and one blocking
+ *     hipMemset), and it is never freed,
  *     moved or regrown, so a HIP graph captured on the stream stays valid for the life of the
  *     process.  Nothing is allocated while the stream is capturing: a split-K call on a stream
- *     that has no workspace yet, made during capture, returns FP8GEMM_ERR_UNSUPPORTED; call
+ *     that has no workspace yet, made during capture, returns FP8GEMM_ERR_UNSUPPORTED (a
+ *     stream-K launch keeps whole tiles instead); call
  *     fp8gemm_prepare_stream before capturing (and before any capture starts in the process,
  *     since the blocking hipMemset must not run while another thread captures).  A graph uses
  *     the workspace of the stream it was captured on: its replays must not overlap each other

@@ -6,6 +6,7 @@ replays the outputs are zeroed again by ordinary eager work and the device is sy
 Every replay must reproduce the eager result bit for bit.  The cases include split-K launches
 (whose arrival counters the kernels reset themselves, with no memset node in the graph), the
 masked decode kernel, E2M1 weights, the quantisers and the whole expert layer."""
+import os
 import sys
 
 import numpy as np
@@ -205,3 +206,78 @@ def test_split_k_capture_on_unprepared_stream_is_refused():
         assert hip.hipStreamSynchronize(s) == 0
         assert hip.hipStreamDestroy(s) == 0
     say("unprepared capture refused, prepared capture accepted")
+
+
+def test_stream_k_graph_replays():
+    """A stream-K launch (leftover 256 x 256 tiles spread over 7 workgroups each, forced on a
+    7-CU cap) captured after an eager call on the same stream: every replay gives the eager bits,
+    so the arrival counters are back at zero after each launch."""
+    d = W.dense(1100, 700, 1280, seed=504)
+    ops = (dev(d.A), dev_sa(d.sa), dev(d.B), dev(d.sb))
+    D = torch.zeros((1100, 700), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    os.environ["FP8GEMM_STREAMK"] = "1"
+    os.environ["FP8GEMM_FORCE_CONFIG"] = "256x256:4x2:2:1"
+    fg.set_num_cus(7)
+    try:
+        replay_matches_eager("stream-K 1100x700x1280", lambda s: fg.gemm_nt(*ops, out=D, stream=s), [D])
+        cfg = fg.last_config()
+    finally:
+        fg.set_num_cus(0)
+        os.environ.pop("FP8GEMM_FORCE_CONFIG", None)
+        os.environ.pop("FP8GEMM_STREAMK", None)
+    assert "streamk_tiles=" in cfg, cfg
+
+
+def test_stream_k_capture_on_unprepared_stream_keeps_whole_tiles():
+    """Stream-K needs the stream's workspace, which is never allocated during capture: on a
+    stream with none, the captured launch keeps whole tiles (no error) and its graph computes the
+    product; once the stream is prepared, the same capture takes stream-K."""
+    import ctypes
+
+    import oracle
+    from parity import assert_close, gpu_bits
+
+    hip = ctypes.CDLL("libamdhip64.so")
+    lib = fg.lib()
+    M, N, K = 1100, 700, 1280
+    d = W.dense(M, N, K, seed=505)
+    ops = (dev(d.A), dev_sa(d.sa), dev(d.B), dev(d.sb))
+    D = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    ref = oracle.gemm_nt(d.A, d.sa, d.B, d.sb)
+    torch.cuda.synchronize()
+    s = ctypes.c_void_p()
+    assert hip.hipStreamCreate(ctypes.byref(s)) == 0
+    os.environ["FP8GEMM_STREAMK"] = "1"
+    os.environ["FP8GEMM_FORCE_CONFIG"] = "256x256:4x2:2:1"
+    fg.set_num_cus(7)
+    try:
+        def capture_and_run():
+            graph, exe = ctypes.c_void_p(), ctypes.c_void_p()
+            assert hip.hipStreamBeginCapture(s, 2) == 0          # relaxed mode
+            rc = lib.fp8gemm_nt(*[t.data_ptr() for t in ops], D.data_ptr(), M, N, K, s)
+            assert hip.hipStreamEndCapture(s, ctypes.byref(graph)) == 0
+            cfg = fg.last_config()
+            if rc == 0:
+                assert hip.hipGraphInstantiate(ctypes.byref(exe), graph, None, None, 0) == 0
+                assert hip.hipGraphLaunch(exe, s) == 0
+                assert hip.hipStreamSynchronize(s) == 0
+                assert hip.hipGraphExecDestroy(exe) == 0
+            assert hip.hipGraphDestroy(graph) == 0
+            return rc, cfg
+        rc, cfg = capture_and_run()
+        assert rc == 0 and "streamk" not in cfg, (rc, cfg)
+        assert_close(gpu_bits(D), ref, what=cfg)
+        assert lib.fp8gemm_prepare_stream(s) == 0
+        D.zero_()
+        torch.cuda.synchronize()
+        rc, cfg = capture_and_run()
+        assert rc == 0 and "streamk_tiles=" in cfg, (rc, cfg)
+        assert_close(gpu_bits(D), ref, what=cfg)
+    finally:
+        fg.set_num_cus(0)
+        os.environ.pop("FP8GEMM_FORCE_CONFIG", None)
+        os.environ.pop("FP8GEMM_STREAMK", None)
+        assert hip.hipStreamSynchronize(s) == 0
+        assert hip.hipStreamDestroy(s) == 0
+    say("unprepared capture keeps whole tiles, prepared capture takes stream-K")

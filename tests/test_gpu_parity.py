@@ -211,6 +211,76 @@ def test_cu_cap_and_side_stream():
     assert np.array_equal(gpu_bits(D2), ref)
 
 
+class streamk_on:
+    """Stream-K wherever leftover tiles exist, inside the block (FP8GEMM_STREAMK=1)."""
+
+    def __enter__(self):
+        os.environ["FP8GEMM_STREAMK"] = "1"
+
+    def __exit__(self, *exc):
+        os.environ.pop("FP8GEMM_STREAMK", None)
+
+
+def streamk_cus(tiles, nkb, at_least):
+    """The smallest CU cap >= at_least that leaves leftover tiles with at least one K block per
+    workgroup."""
+    P = at_least
+    while tiles % P == 0 or (tiles % P) * nkb < P:
+        P += 1
+    return P
+
+
+@pytest.mark.parametrize("bn", [256, 160])
+@pytest.mark.parametrize("M,N,K,cus", [(1100, 700, 1280, 4), (1100, 700, 1280, 7), (600, 1030, 3840, 4),
+                                       (777, 1500, 7168, 5), (300, 300, 1024, 2)])
+def test_stream_k_leftover_tiles(bn, M, N, K, cus):
+    """Tiles past the last full round taken stream-K (forced on, small CU caps): each leftover
+    tile's K blocks are spread over 2 to 7 workgroups whose partials the last to arrive sums in K
+    order; ragged M and N tails.  Parity with the oracle, identical bits on a second call, and
+    exact results for integer inputs with power-of-two scales."""
+    tiles = -(-M // 256) * -(-N // bn)
+    P = streamk_cus(tiles, K // 128, cus)
+    d = W.dense(M, N, K, seed=M + N + K + bn)
+    ref = oracle.gemm_nt(d.A, d.sa, d.B, d.sb)
+    rng = np.random.default_rng(M + bn)
+    A, B = int_codes(rng, (M, K)), int_codes(rng, (N, K))
+    sa = (2.0 ** rng.integers(-1, 2, size=(M, K // 128))).astype(np.float32)
+    sb = (2.0 ** rng.integers(-1, 2, size=((N + 127) // 128, K // 128))).astype(np.float32)
+    ref2 = oracle.gemm_nt(A, sa, B, sb)
+    fg.set_num_cus(P)
+    try:
+        with forced(256, bn, 4, 2, 2, 1), streamk_on():
+            D = run_dense(d)
+            cfg = fg.last_config()
+            again = gpu_bits(run_dense(d)).copy()
+            D2 = run_dense(W.Dense(A, sa, B, sb))
+    finally:
+        fg.set_num_cus(0)
+    assert "streamk_tiles=" in cfg and "grid=%d " % P in cfg, cfg
+    rep = assert_close(gpu_bits(D), ref, what=cfg)
+    assert np.array_equal(again, gpu_bits(D)), cfg
+    assert_bit_exact(gpu_bits(D2), ref2, what=cfg)
+    say("stream-K", M, N, K, "cus", P, cfg, rep["bit_equal"])
+
+
+def test_stream_k_off_matches_oracle_too():
+    """The same leftover tiles as whole tiles (FP8GEMM_STREAMK=0): the schedule is a choice, both
+    within tolerance of the oracle."""
+    d = W.dense(1100, 700, 1280, seed=5)
+    ref = oracle.gemm_nt(d.A, d.sa, d.B, d.sb)
+    fg.set_num_cus(7)
+    os.environ["FP8GEMM_STREAMK"] = "0"
+    try:
+        with forced(256, 256, 4, 2, 2, 1):
+            D = run_dense(d)
+            cfg = fg.last_config()
+    finally:
+        os.environ.pop("FP8GEMM_STREAMK", None)
+        fg.set_num_cus(0)
+    assert "streamk" not in cfg, cfg
+    assert_close(gpu_bits(D), ref, what=cfg)
+
+
 # ------------------------------------------------------------------------------------------
 # grouped: contiguous
 # ------------------------------------------------------------------------------------------

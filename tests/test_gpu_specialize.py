@@ -1,7 +1,9 @@
 """GPU: the run-time specialised dense kernel (N and K compiled in) against the ahead-of-time kernel
-and the CPU oracle.  The two kernels share their body and arithmetic order, so their outputs must
-be identical bit for bit on every shape; the oracle comparison uses the GEMM tolerance
+and the CPU oracle.  The two kernels share their body and arithmetic order, so with the same
+schedule (whole tiles: the specialised kernels take no stream-K) their outputs must be identical
+bit for bit on every shape; the oracle comparison uses the GEMM tolerance
 |gpu - ref| <= 2^-7 |ref| + 1e-3 rms(ref)."""
+import os
 import sys
 
 import numpy as np
@@ -37,10 +39,17 @@ def operands(M, N, K, seed):
 
 
 def run_both(Aq, sa, Bq, sb):
+    """The table kernel and the specialised one on the same operands.  The specialised kernels
+    keep whole tiles, so the table kernel runs with stream-K off here (with it, its leftover
+    tiles sum their K blocks in another order)."""
     A, S, B, SB = dev(Aq), dev(np.ascontiguousarray(sa.T)), dev(Bq), dev(sb)
-    d0 = fg.gemm_nt(A, S, B, SB)
-    torch.cuda.synchronize()
-    c0 = fg.last_config()
+    os.environ["FP8GEMM_STREAMK"] = "0"
+    try:
+        d0 = fg.gemm_nt(A, S, B, SB)
+        torch.cuda.synchronize()
+        c0 = fg.last_config()
+    finally:
+        os.environ.pop("FP8GEMM_STREAMK", None)
     d1 = fg.gemm_nt_specialized(A, S, B, SB)
     torch.cuda.synchronize()
     c1 = fg.last_config()
