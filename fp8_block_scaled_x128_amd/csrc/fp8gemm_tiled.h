@@ -140,15 +140,19 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
     if ((P & 7) == 0) logical = (blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3);
 
     // Units [0, units) are whole tiles (or K splits of them); with stream-K each workgroup then
-    // takes two more iterations, its segments 0 and 1 of the leftover tiles (either may be empty).
-    // The run-time specialised variants (N or K fixed) keep whole tiles: with N fixed the compiler
-    // keeps more values live and the exchange code would spill.
+    // takes two more iterations over its segments of the leftover tiles, segment 1 first (either
+    // may be empty).  Segment 1 starts at a tile's first K block and segment 0, when the range
+    // crosses a tile boundary, ends at a tile's last one, so in this order every workgroup of
+    // such a schedule reads K block j or j + (K blocks per tile - blocks per workgroup) at step j:
+    // two K phases, which the workgroups of an XCD share through L2 (in range order they would
+    // run at up to four).  The run-time specialised variants (N or K fixed) keep whole tiles:
+    // with N fixed the compiler keeps more values live and the exchange code would spill.
     constexpr bool SK = T::STREAMK && NC == 0 && KC == 0;
     const int sk_iters = (SK && args.sk_tiles > 0) ? 2 * P : 0;
     for (int unit = logical; unit < args.units + sk_iters; unit += P) {
         // ---- a stream-K segment: K blocks [sk_kb0, sk_kb0 + sk_nks) of leftover tile sk_tile --
         const bool sk = SK && unit >= args.units;
-        const int sk_seg = sk ? (unit - args.units) / P : 0;
+        const int sk_seg = sk ? 1 - (unit - args.units) / P : 0;
         int sk_tile = 0, sk_kb0 = 0, sk_nks = 0;
         if (sk) {
             const int r0 = sk_start(logical, args.sk_per, args.sk_extra);
@@ -555,16 +559,17 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
                 // from consecutive workgroups w_a..w_b, in K order).  As the split-K exchange
                 // above: partials are written and read with agent-coherent (sc1) accesses, each
                 // into its writer's slot 2w + segment, and an agent-scope counter finds the last
-                // to arrive, which sums the partials in K order.  The tile's first segment comes
-                // first in that order, so when it is the last to arrive it adds the others to its
-                // own accumulators and writes nothing; it checks the counter before writing, and it
-                // is usually last (its workgroup reaches it at the end of its range, the other
-                // segments at the start of theirs).  Any other last arrival re-reads every partial,
-                // its own included, in K order.
+                // to arrive, which sums the partials in K order.  A tile's last segment is usually
+                // the last to arrive (its workgroup reaches it at the end of its range, the other
+                // segments at the start of theirs); when the tile has just one other segment, the
+                // last segment checks the counter before writing and, if the other is in, adds it
+                // to its own accumulators and writes nothing (two terms: IEEE addition commutes,
+                // so that is the K-order sum).  Any other last arrival re-reads every partial, its
+                // own included, in K order.
                 const int g0 = sk_tile * nkb;
                 const int w_a = sk_owner(g0, args.sk_per, args.sk_extra);
                 const int w_b = sk_owner(g0 + nkb - 1, args.sk_per, args.sk_extra);
-                const bool head = logical == w_a;
+                const bool fold = logical == w_b && w_b == w_a + 1;
                 const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(
                     uniform_ptr(args.ws), 0, 2 * P * BM * BN * 4, kBufferFlags);
                 const int lane_off = (wave * (T::WM * T::WN) + lane * 4) * 4;
@@ -573,10 +578,10 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
                     return (2 * w2 + seg2) * (BM * BN * 4) + lane_off;
                 };
                 bool last = false;
-                if (head) {
+                if (fold) {
                     if (tid == 0)
                         s_flag = __hip_atomic_load(args.counters + sk_tile, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT) == w_b - w_a;
+                                                   __HIP_MEMORY_SCOPE_AGENT) == 1;
                     __syncthreads();
                     last = s_flag != 0;
                     __syncthreads();          // every wave has read s_flag before it is written again
@@ -605,7 +610,8 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
                 if (last) {
                     constexpr int NSUB = T::IN * T::JM;
                     constexpr int CH = NSUB < 8 ? NSUB : 8;      // sub-tiles of one read batch
-                    if (!head) {
+                    // folding: acc += the other segment's partial; otherwise every partial in K order
+                    if (!fold) {
                         const int off_a = slot_of(w_a);
 #pragma unroll
                         for (int i2 = 0; i2 < T::IN; ++i2)
@@ -614,7 +620,8 @@ __global__ __launch_bounds__(WMW * WNW * 64) void fp8gemm_kernel(const KernelArg
                                 acc[i2][j] = __builtin_amdgcn_raw_buffer_load_b128(ws_rsrc, off_a + (i2 * T::JM + j) * 1024,
                                                                                    0, kSc1);
                     }
-                    for (int w2 = w_a + 1; w2 <= w_b; ++w2) {
+                    const int w_first = fold ? w_a : w_a + 1, w_last = fold ? w_a : w_b;
+                    for (int w2 = w_first; w2 <= w_last; ++w2) {
                         const int off2 = slot_of(w2);
 #pragma unroll
                         for (int c0 = 0; c0 < NSUB; c0 += CH) {

@@ -232,11 +232,12 @@ def streamk_cus(tiles, nkb, at_least):
 
 @pytest.mark.parametrize("bn", [256, 160])
 @pytest.mark.parametrize("M,N,K,cus", [(1100, 700, 1280, 4), (1100, 700, 1280, 7), (600, 1030, 3840, 4),
-                                       (777, 1500, 7168, 5), (300, 300, 1024, 2)])
+                                       (777, 1500, 7168, 5), (300, 300, 1024, 2), (300, 256, 256, 3)])
 def test_stream_k_leftover_tiles(bn, M, N, K, cus):
     """Tiles past the last full round taken stream-K (forced on, small CU caps): each leftover
-    tile's K blocks are spread over 2 to 7 workgroups whose partials the last to arrive sums in K
-    order; ragged M and N tails.  Parity with the oracle, identical bits on a second call, and
+    tile's K blocks are spread over 1 to 7 workgroups whose partials the last to arrive sums in K
+    order (with two, the later segment folds the earlier one into its own accumulators; with one,
+    the tile is whole in one range); ragged M and N tails.  Parity with the oracle, identical bits on a second call, and
     exact results for integer inputs with power-of-two scales."""
     tiles = -(-M // 256) * -(-N // bn)
     P = streamk_cus(tiles, K // 128, cus)

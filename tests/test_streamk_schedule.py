@@ -2,8 +2,10 @@
 checked for the invariants the kernel relies on: the leftover tiles' K blocks are covered exactly
 once, in order; a workgroup's range touches at most two tiles (segments 0 and 1, partial slots
 2w and 2w + 1); a tile's segments come from consecutive workgroups, so the last to arrive can find
-every partial (the owner of its first and last K block bound them); and the host's choice takes
-stream-K only where it saves enough K blocks.  No GPU is needed."""
+every partial (the owner of its first and last K block bound them); run segment 1 first, the
+segments read K block j or j + (blocks per tile - blocks of the range) at step j whenever no tile
+has more than two segments; and the host's choice takes stream-K only where it saves enough K
+blocks.  No GPU is needed."""
 import itertools
 
 import pytest
@@ -86,3 +88,45 @@ def test_the_leftover_of_the_largest_sweep_shape_takes_stream_k():
     # and the short-K shapes of the same tile count keep whole tiles
     full, R, per, extra, _ = schedule(16 * 28, 256, 16)
     assert 16 - per - (1 if extra else 0) < 24
+
+
+def steps(segs_w, nkb):
+    """(step, K block) pairs of one workgroup, its segment 1 first as the kernel runs them."""
+    out, j = [], 0
+    for t, kb0, nks, seg in sorted(segs_w, key=lambda x: -x[3]):
+        for k in range(kb0, kb0 + nks):
+            out.append((j, k))
+            j += 1
+    return out
+
+
+@pytest.mark.parametrize("T,P,nkb", CASES)
+def test_two_k_phases_when_tiles_have_at_most_two_segments(T, P, nkb):
+    full, R, per, extra, segs = schedule(T, P, nkb)
+    if R == 0 or per < 1:
+        return
+    owners = {}
+    for w in range(P):
+        for t, _, _, _ in segs[w]:
+            owners.setdefault(t, []).append(w)
+    if max(len(o) for o in owners.values()) > 2:
+        return
+    for w in range(P):
+        length = sk_start(w + 1, per, extra) - sk_start(w, per, extra)
+        for j, k in steps(segs[w], nkb):
+            assert k in (j, j + nkb - length), (w, j, k)
+    # a tile then has two segments from consecutive workgroups (the later one folds the other in),
+    # or one, when a range of per + 1 blocks is exactly a tile
+    for t, o in owners.items():
+        w_a, w_b = sk_owner(t * nkb, per, extra), sk_owner(t * nkb + nkb - 1, per, extra)
+        assert o == sorted({w_a, w_b}) and w_b - w_a == len(o) - 1
+
+
+def test_the_largest_sweep_shape_runs_in_two_phases():
+    # 4096 x 7168 x 16384: 192 leftover tiles of 128 K blocks on 256 workgroups of 96 blocks each
+    full, R, per, extra, segs = schedule(16 * 28, 256, 128)
+    phases = set()
+    for w in range(256):
+        for j, k in steps(segs[w], 128):
+            phases.add(k - j)
+    assert phases == {0, 32}
