@@ -98,8 +98,9 @@ int device_state(DeviceState** out) {
 // fp32 (128 KiB); a stream-K launch of 256 x 256 tiles (one workgroup per CU) keeps two partial
 // tiles per workgroup (512 KiB).  So cus * 512 KiB of partials and one counter per unit cover
 // every such launch.  A forced configuration (FP8GEMM_FORCE_CONFIG) beyond it is refused.
-constexpr int kStreamKMinBlocks = 24;
 constexpr size_t kMaxPartialBytesPerCu = 2 * 256 * 256 * sizeof(float);
+// Fewest K blocks per workgroup that stream-K must save over whole tiles (see launch()).
+int stream_k_min_blocks(int bn) { return bn >= 256 ? 12 : 6; }
 size_t workspace_partial_bytes(int cus) { return (size_t)std::max(cus, 1) * kMaxPartialBytesPerCu; }
 size_t workspace_counters(int cus) { return std::max<size_t>((size_t)cus, 4096); }
 
@@ -329,10 +330,20 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream,
     // Stream-K for the tiles after the last full round of whole tiles (dense 256-row tiles, which
     // take no K split): instead of a last, partly idle round, the leftover tiles' K blocks are
     // shared out evenly over the grid (sk_start in fp8gemm_args.h), and tiles shared by several
-    // workgroups are summed by the exchange in the kernel.  Taken when it saves a workgroup at
-    // least kStreamKMinBlocks K blocks: on MI355X a partly empty round costs as much as a full one
-    // (4096 x N x 16384 with 384, 448 and 512 tiles on 256 CUs: 464, 477 and 496 us), while the
-    // exchange costs about a K block's time per partial tile written or read.
+    // workgroups are summed by the exchange in the kernel.  On MI355X a partly empty round costs
+    // as much as a full one (4096 x N x 16384 with 384, 448 and 512 tiles on 256 CUs: 464, 477
+    // and 496 us), while the exchange and the stream-K phase's weaker L2 sharing cost several K
+    // blocks' time.  So it is taken when it saves a workgroup at least stream_k_min_blocks K
+    // blocks against whole tiles; measured (whole tiles -> stream-K, us, blocks saved):
+    //   256 x 256: 4096x7168x2048 79.5 -> 87.0 (4), 2048x7168x7168 104.7 -> 111.1 (7),
+    //     6144x2112x7168 104.4 -> 112.0 (8), 4096x7168x4096 130.0 -> 131.0 (8),
+    //     4096x3072x7168 101.1 -> 99.6 (14), 4096x7168x7168 212.4 -> 202.5 (14),
+    //     8192x7168x7168 411.3 -> 385.1 (28), 4096x7168x16384 465.1 -> 423.3 (32);
+    //   256 x 160: 4096x2112x4096 57.7 -> 61.4 (4), 4096x2112x7168 95.5 -> 92.6 (7),
+    //     4096x2112x16384 183.6 -> 171.1 (16), 3072x2112x7168 85.3 -> 78.8 (19).
+    // Every gain measured had a workgroup take at least 0.43 of a tile's K blocks (at most three
+    // segments per tile); a range shorter than a third of a tile keeps whole tiles, since each
+    // further segment adds a partial that the last arrival reads.
     // FP8GEMM_STREAMK=0 turns it off, =1 on wherever leftover tiles exist.  Not for the run-time
     // specialised kernels (compiled without the exchange) nor for the allocation-free entry point.
     bool streamk = false;
@@ -342,7 +353,7 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream,
         const int64_t total = R * a.nkb, per = total / std::max<int64_t>(P, 1), extra = total % std::max<int64_t>(P, 1);
         const int64_t saved = a.nkb - per - (extra > 0 ? 1 : 0);
         const char* f = std::getenv("FP8GEMM_STREAMK");
-        const bool want = (f && *f) ? f[0] == '1' : saved >= kStreamKMinBlocks;
+        const bool want = (f && *f) ? f[0] == '1' : saved >= stream_k_min_blocks(e.bn) && 3 * per >= a.nkb;
         const size_t need = (size_t)(2 * P) * e.bm * e.bn * sizeof(float);
         if (want && R > 0 && per >= 1 && need <= workspace_partial_bytes(d->cus)) {
             // a stream with no workspace that is being captured keeps whole tiles (UNSUPPORTED

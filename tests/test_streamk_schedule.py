@@ -84,10 +84,17 @@ def test_the_leftover_of_the_largest_sweep_shape_takes_stream_k():
     full, R, per, extra, _ = schedule(16 * 28, 256, 128)
     assert (full, R, per, extra) == (1, 192, 96, 0)
     saved = 128 - per - (1 if extra else 0)
-    assert saved >= 24                              # the host's threshold (kStreamKMinBlocks)
+    assert saved >= 12                              # the host's threshold for 256 x 256 tiles
     # and the short-K shapes of the same tile count keep whole tiles
     full, R, per, extra, _ = schedule(16 * 28, 256, 16)
-    assert 16 - per - (1 if extra else 0) < 24
+    assert 16 - per - (1 if extra else 0) < 12
+    # 4096 x 2112 x 7168 in 256 x 160 tiles: 224 tiles, no full round, 7 blocks saved (threshold 6)
+    full, R, per, extra, _ = schedule(16 * 14, 256, 56)
+    assert (full, R) == (0, 224) and 56 - per - (1 if extra else 0) == 7 and 3 * per >= 56
+    # 1024 x 2048 x 1024 in 256 x 160 tiles: 52 tiles of 8 K blocks, 1-2 blocks per workgroup --
+    # 6 blocks saved, but a range is under a third of a tile: whole tiles
+    full, R, per, extra, _ = schedule(4 * 13, 256, 8)
+    assert 8 - per - (1 if extra else 0) >= 6 and 3 * per < 8
 
 
 def steps(segs_w, nkb):
