@@ -264,6 +264,41 @@ def test_stream_k_leftover_tiles(bn, M, N, K, cus):
     say("stream-K", M, N, K, "cus", P, cfg, rep["bit_equal"])
 
 
+@pytest.mark.parametrize("bn", [256, 160])
+@pytest.mark.parametrize("M,N,K,cus", [(1100, 1500, 1024, 4), (1024, 2048, 128, 3), (777, 1000, 512, 2),
+                                       (513, 1001, 384, 2), (2048, 2048, 256, 5)])
+def test_several_whole_tiles_per_workgroup(bn, M, N, K, cus):
+    """Dense 256-row tiles, several whole tiles per workgroup (small CU caps, stream-K off): each
+    workgroup runs tile after tile through the same ring and staging area, whole tiles followed by
+    ragged ones and the reverse, one-slice tiles (K = 128), and N not a multiple of 8.  Parity with
+    the oracle, identical bits on a second call, and exact results for integer inputs with
+    power-of-two scales."""
+    d = W.dense(M, N, K, seed=M + 3 * N + K + bn)
+    ref = oracle.gemm_nt(d.A, d.sa, d.B, d.sb)
+    rng = np.random.default_rng(M + 7 * bn)
+    A, B = int_codes(rng, (M, K)), int_codes(rng, (N, K))
+    sa = (2.0 ** rng.integers(-1, 2, size=(M, K // 128))).astype(np.float32)
+    sb = (2.0 ** rng.integers(-1, 2, size=((N + 127) // 128, K // 128))).astype(np.float32)
+    ref2 = oracle.gemm_nt(A, sa, B, sb)
+    fg.set_num_cus(cus)
+    os.environ["FP8GEMM_STREAMK"] = "0"
+    try:
+        with forced(256, bn, 4, 2, 2, 1):
+            D = run_dense(d)
+            cfg = fg.last_config()
+            again = gpu_bits(run_dense(d)).copy()
+            D2 = run_dense(W.Dense(A, sa, B, sb))
+    finally:
+        os.environ.pop("FP8GEMM_STREAMK", None)
+        fg.set_num_cus(0)
+    units = int(cfg.split("units=")[1].split()[0])
+    assert "streamk" not in cfg and units >= 2 * cus, cfg
+    rep = assert_close(gpu_bits(D), ref, what=cfg)
+    assert np.array_equal(again, gpu_bits(D)), cfg
+    assert_bit_exact(gpu_bits(D2), ref2, what=cfg)
+    say("tiles per workgroup", M, N, K, "cus", cus, cfg, rep["bit_equal"])
+
+
 def test_stream_k_off_matches_oracle_too():
     """The same leftover tiles as whole tiles (FP8GEMM_STREAMK=0): the schedule is a choice, both
     within tolerance of the oracle."""
