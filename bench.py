@@ -33,6 +33,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -109,6 +110,42 @@ def read_traffic():
         return int(vals["traffic_bytes_per_launch"].split()[0])
     except (KeyError, ValueError):
         return None
+
+
+COUNTER_FILES = ("counters_dense_prefill.txt", "counters_dense_decode.txt", "counters_grouped.txt",
+                 "counters_quantize.txt")
+
+
+def leg_key(label):
+    """The key a counter summary's leg label and a benchmark leg share: 'dense 64x2112x7168',
+    'contiguous cfg2', 'masked cfg4', 'masked fp8xfp4 cfg4', 'quantize_1x128 32768x7168'."""
+    words = label.split()
+    if words[0] == "dense" or words[0].startswith("quantize"):
+        return " ".join(words[:2])
+    return " ".join(w for w in words[:3] if not re.match(r"^\d+x\d+$", w))
+
+
+def read_leg_traffic():
+    """Measured HBM bytes per call of every leg in the committed counter summaries (calibrated
+    FETCH_SIZE + WRITE_SIZE), keyed by leg_key; a summary taken on other kernel sources is
+    skipped."""
+    out = {}
+    h = kernel_source_hash()
+    for fname in COUNTER_FILES:
+        path = os.path.join(ROOT, "profiles", fname)
+        if not os.path.exists(path):
+            continue
+        lines = open(path).read().splitlines()
+        if not any(l.startswith("kernel_source_sha256_16:") and l.split(":", 1)[1].strip() == h for l in lines):
+            continue
+        label = None
+        for line in lines:
+            if line and not line.startswith(" ") and "[" in line:
+                label = line.split("[")[0].strip()
+            m = re.search(r"hbm_MB ([0-9.]+)", line)
+            if label and line.startswith("    derived:") and m:
+                out[leg_key(label)] = int(float(m.group(1)) * 1e6)
+    return out
 
 
 def main():
@@ -299,6 +336,16 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cases, eager, args.cpu_seconds)
 
+    # measured HBM bytes per call of each leg, from the committed counter summaries of the same
+    # kernel sources (None where there is none)
+    leg_traffic = read_leg_traffic()
+    for q in per:
+        q["traffic"] = leg_traffic.get("dense %dx%dx%d" % (q["M"], q["N"], q["K"]))
+    for name, g in grouped.items():
+        g["traffic"] = leg_traffic.get(name.replace("_", " "))
+    if "dense_32768x7168" in quantize:
+        quantize["dense_32768x7168"]["roofline"]["traffic"] = leg_traffic.get("quantize_1x128 32768x7168")
+
     line = {
         "metric": "FP8 TFLOPS and HBM GB/s per shape (dense, contiguous, masked) on 1 MI355X",
         "value": round(value, 2),
@@ -328,6 +375,8 @@ def main():
         "read_floor": read_floor,
         "library_reference": library,
         "gpu_state": gpu_state,
+        "traffic_note": "traffic: HBM bytes per call (calibrated FETCH_SIZE + WRITE_SIZE) from profiles/counters_*.txt "
+                        "taken on the same kernel sources; null where none match",
     }
     print(json.dumps(line), flush=True)
 

@@ -143,3 +143,33 @@ def test_gpu_state_sample_never_fails(monkeypatch):
 
     monkeypatch.setattr(subprocess, "run", boom)
     assert "unavailable" in bench.sample_gpu_state()
+
+
+@pytest.mark.parametrize("label,key", [
+    ("dense 64x2112x7168", "dense 64x2112x7168"),
+    ("contiguous cfg2 4x8192 N=4096 K=7168", "contiguous cfg2"),
+    ("masked cfg4 16x256 N=4096 K=7168", "masked cfg4"),
+    ("masked fp8xfp4 cfg4 16x256 N=4096 K=7168", "masked fp8xfp4 cfg4"),
+    ("quantize_1x128 32768x7168", "quantize_1x128 32768x7168"),
+])
+def test_counter_labels_map_to_bench_legs(label, key):
+    assert bench.leg_key(label) == key
+
+
+def test_leg_traffic_only_from_summaries_of_the_current_sources(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    body = ("title\ncommand\nsummary\nkernel_source_sha256_16: %s\n"
+            "dense 64x2112x7168  [fp8gemm_kernel<64, 64, 1, 4, 4, 0, 0, 0>]\n"
+            "    derived: hbm_MB 26.897  alg_MB 15.886  hbm/alg 1.693\n"
+            "    raw: FETCH_SIZE 1\n"
+            "masked fp8xfp4 cfg4 16x256 N=4096 K=7168  [fp8gemm_masked_decode_kernel<128, 4, 2, 2, 8, true>]\n"
+            "    derived: hbm_MB 273.519  alg_MB 265.426\n")
+    (prof / "counters_dense_decode.txt").write_text(body % "0123456789abcdef")
+    # a summary of other kernel sources: its numbers must not be used
+    (prof / "counters_grouped.txt").write_text((body % "fedcba9876543210").replace("273.519", "999.0")
+                                                .replace("dense 64x2112x7168", "dense 128x2112x7168"))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0123456789abcdef")
+    t = bench.read_leg_traffic()
+    assert t == {"dense 64x2112x7168": 26897000, "masked fp8xfp4 cfg4": 273519000}
