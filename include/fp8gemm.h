@@ -31,11 +31,14 @@
  *     they validate on the host (no device access, no synchronisation), enqueue the kernel and
  *     return.  An argument error is reported before anything is enqueued.
  *   - Results are deterministic: the same inputs give the same bits, whatever the launch
- *     configuration's timing (split-K partials are summed in a fixed order).
+ *     configuration's timing (split-K and stream-K partials are summed in a fixed K order).
+ *     The launch configuration itself depends on the shape, the device's CU count and the CU
+ *     cap, so a different cap (or stream-K turned off) may sum the same products in another
+ *     order, within the same tolerance.
  *   - Split-K workspace: each stream has its own library-owned workspace (fp32 partial tiles
  *     and arrival counters, CUs x 512 KiB + 16 KiB on the stream's device).  It serves the
  *     K splits of decode-sized launches and the stream-K schedule of large dense launches (the
- *     256 x 256 tiles left over after the last full round of tiles, shared out over every CU
+ *     256-row tiles left over after the last full round of tiles, shared out over every CU
  *     by K block).  It is allocated once, at full size, by fp8gemm_prepare_stream or by the
  *     first call on the stream whose launch needs it (one hipMalloc pair and one blocking
  *     hipMemset), and it is never freed,
@@ -50,6 +53,12 @@
  *   - Thread safety: calls may come from any host thread.  Calls on different streams may run
  *     concurrently.  fp8gemm_set_num_cus is a global knob, not synchronised with calls in
  *     flight.
+ *   - Environment (read at each call; for experiments and tests, not needed in normal use):
+ *     FP8GEMM_FORCE_CONFIG forces a table entry (BMxBN:WMxWN:STAGES:SPLIT for the tiled kernel,
+ *     stream:MT:W:JN:KP:PF:SPLIT for the masked decode kernel), FP8GEMM_STREAMK=0 or 1 turns
+ *     stream-K off, or on wherever dense 256-row tiles leave a partial round, and FP8GEMM_LOG
+ *     prints each launch configuration to stderr.  FP8GEMM_HIPRTC names the hipRTC library for
+ *     the run-time specialised kernels (default $ROCM_PATH/lib/libhiprtc.so.7).
  *
  * Return value of every int function: a fp8gemm_status code.
  */
