@@ -4,7 +4,9 @@ The split-K workspace and its arrival counters are kept per stream, the dispatch
 is built once under a lock, and the last-configuration string is kept per thread.  So calls made
 concurrently must give the same bits, and report the same launch configuration, as the same calls
 made one at a time.  The cases are chosen so that each one splits K across workgroups: dense decode
-shapes and a masked call whose groups times N tiles leave most CUs idle."""
+shapes, a masked call whose groups times N tiles leave most CUs idle, and a dense 256-row-tile
+shape that takes stream-K (2048 x 4096 x 7168: 208 tiles of 256 x 160, 45 K blocks per workgroup
+on 256 CUs)."""
 import sys
 import threading
 
@@ -42,7 +44,8 @@ def dev_sa(sa):
 def make_cases():
     """(name, call(stream, out), output shape) for each case; every call splits K."""
     cases = []
-    for M, N, K, seed in ((64, 2112, 7168, 81), (64, 4096, 7168, 82), (128, 2112, 7168, 83), (100, 700, 1024, 84)):
+    for M, N, K, seed in ((64, 2112, 7168, 81), (64, 4096, 7168, 82), (128, 2112, 7168, 83), (100, 700, 1024, 84),
+                          (2048, 4096, 7168, 86)):
         d = W.dense(M, N, K, seed=seed)
         ops = (dev(d.A), dev_sa(d.sa), dev(d.B), dev(d.sb))
         cases.append(("dense %dx%dx%d" % (M, N, K),
@@ -63,7 +66,9 @@ def test_threads_on_their_own_streams_match_sequential_calls():
         torch.cuda.synchronize()
         ref.append(gpu_bits(out).copy())
         ref_cfg.append(fg.last_config())
-        assert "split=1 " not in ref_cfg[-1], (name, ref_cfg[-1])
+        assert "split=1 " not in ref_cfg[-1] or "streamk_tiles=" in ref_cfg[-1], (name, ref_cfg[-1])
+        if name == "dense 2048x4096x7168":
+            assert "streamk_tiles=" in ref_cfg[-1], ref_cfg[-1]
         say(name, ref_cfg[-1])
 
     results, errors = {}, []
