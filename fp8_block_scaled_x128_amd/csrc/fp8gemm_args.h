@@ -38,8 +38,8 @@ __host__ __device__ inline uint32_t fast_div(uint32_t n, const FastDiv& f) {
 // 256-row tiles).  The leftover tiles' K blocks form one sequence in (tile, K block) order;
 // workgroup w (logical id, 0 <= w < P) takes blocks [sk_start(w), sk_start(w + 1)), with
 // sk_start(w) = w * per + min(w, extra): the first `extra` workgroups take per + 1 blocks, the
-// others per.  A workgroup's range is shorter than a tile's K extent, so it touches at most two
-// tiles (its segments 0 and 1).
+// others per.  A range is no longer than a tile's K extent (per < blocks per tile), so it
+// touches at most two tiles (its segments 0 and 1).
 __host__ __device__ inline int sk_start(int w, int per, int extra) { return w * per + (w < extra ? w : extra); }
 
 // The workgroup whose range holds block g of the sequence (per >= 1).
