@@ -157,7 +157,7 @@ def main():
         trace_summary(*args.trace_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)"
+        print("bench.py measures one GPU: the library has no multi-GPU path (--gpus %d requested)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 
