@@ -100,7 +100,24 @@ int device_state(DeviceState** out) {
 // every such launch.  A forced configuration (FP8GEMM_FORCE_CONFIG) beyond it is refused.
 constexpr size_t kMaxPartialBytesPerCu = 2 * 256 * 256 * sizeof(float);
 // Fewest K blocks per workgroup that stream-K must save over whole tiles (see launch()).
-int stream_k_min_blocks(int bn) { return bn >= 256 ? 12 : 6; }
+int stream_k_min_blocks(int bn) { return bn >= 256 ? 12 : (bn >= 192 ? 9 : 6); }
+
+// The stream-K plan of a dense launch of `tiles` 256-row tiles of width bn on P workgroups: the
+// whole-tile rounds, then the leftover tiles' K blocks shared out, `per` to each workgroup and
+// one more to the first `extra`.  Returns whether stream-K is taken (the thresholds of launch(),
+// or FP8GEMM_STREAMK=0/1) and sets the K blocks of the busiest workgroup either way.
+bool stream_k_plan(int64_t tiles, int64_t P, int nkb, int bn, int64_t* per, int64_t* extra, int64_t* blocks) {
+    P = std::max<int64_t>(P, 1);
+    const int64_t full = tiles / P, R = tiles % P;
+    *per = R * nkb / P;
+    *extra = R * nkb % P;
+    const int64_t saved = nkb - *per - (*extra > 0 ? 1 : 0);
+    const char* f = std::getenv("FP8GEMM_STREAMK");
+    const bool want = (f && *f) ? f[0] == '1' : saved >= stream_k_min_blocks(bn) && 3 * *per >= nkb;
+    const bool take = want && R > 0 && *per >= 1;
+    *blocks = take ? full * nkb + *per + (*extra > 0 ? 1 : 0) : (tiles + P - 1) / P * nkb;
+    return take;
+}
 size_t workspace_partial_bytes(int cus) { return (size_t)std::max(cus, 1) * kMaxPartialBytesPerCu; }
 size_t workspace_counters(int cus) { return std::max<size_t>((size_t)cus, 4096); }
 
@@ -251,17 +268,27 @@ Choice choose(int layout, int64_t rows, int64_t N, int nkb, int64_t expected_row
         if (N >= 16384 || K >= 8192) c.entry = find_entry(layout, 128, 128, 2, 4, 3);
         else c.entry = find_entry(layout, 64, 64, 1, 4, 4);
     } else if (m >= 1024 && N >= 256 && layout == kDense) {
-        // N tile width: fewest rounds of CUs times the time of one tile (a 256x160 tile takes
-        // about 0.86 of a 256x256 one on MI355X: the A operand and the per-slice fixed work do not
-        // shrink with the width)
-        struct Width { int bn; int64_t tile_time; } widths[] = {{256, 100}, {160, 86}};
+        // N tile width: the least estimated time of the busiest workgroup, i.e. its K blocks under
+        // the schedule launch() will run (whole tiles, or stream-K for the leftover tiles), times
+        // the time of one K block of that width, plus stream-K's exchange where it is taken: about
+        // 0.07 K-block times per column of the tile for each segment a tile has beyond its first
+        // (each adds a partial tile written and read).  Measured on MI355X: one round of 256 whole
+        // tiles at K = 7168 takes 121.9, 110.6 and 101.0 us for widths 256, 192 and 160 (block
+        // costs 1, 0.91, 0.83); 4096 x 1536 x 7168 with stream-K takes 82.2 us in 256 x 256 tiles
+        // (21 K blocks per workgroup, three segments per tile), 68.0 in 256 x 192 (28, two) and
+        // 77.1 in 256 x 160 (35, two).  Against the choice by whole rounds this picks 256 x 192 with
+        // stream-K there and for 4096 x 2112 x 7168 (91.3 against 91.8 us); ties keep the wider tile.
+        struct Width { int bn; int64_t block_cost; } widths[] = {{256, 100}, {192, 91}, {160, 83}};
         int64_t best = -1;
         const int64_t tiles_m = (m + 255) / 256;
         for (const Width& w : widths) {
             const int e = find_entry(layout, 256, w.bn, 4, 2, 2);
             if (e < 0) continue;
             const int64_t tiles = tiles_m * ((N + w.bn - 1) / w.bn);
-            const int64_t cost = ((tiles + cus - 1) / cus) * w.tile_time;
+            int64_t per = 0, extra = 0, blocks = 0;
+            const bool sk = stream_k_plan(tiles, cus, nkb, w.bn, &per, &extra, &blocks);
+            const int64_t segments = sk ? (nkb + per - 1) / per : 1;     // per tile, about
+            const int64_t cost = blocks * w.block_cost + 7 * w.bn * (segments - 1);
             if (best < 0 || cost < best) {
                 best = cost;
                 c.entry = e;
@@ -339,6 +366,8 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream,
     //     6144x2112x7168 104.4 -> 112.0 (8), 4096x7168x4096 130.0 -> 131.0 (8),
     //     4096x3072x7168 101.1 -> 99.6 (14), 4096x7168x7168 212.4 -> 202.5 (14),
     //     8192x7168x7168 411.3 -> 385.1 (28), 4096x7168x16384 465.1 -> 423.3 (32);
+    //   256 x 192: 4096x2112x7168 94.6 -> 91.3 (17), 4096x1536x7168 90.7 -> 68.0 (28),
+    //     4096x2112x16384 190.5 -> 165.3 (39); threshold 9, between its neighbours';
     //   256 x 160: 4096x2112x4096 57.7 -> 61.4 (4), 4096x2112x7168 95.5 -> 92.6 (7),
     //     4096x2112x16384 183.6 -> 171.1 (16), 3072x2112x7168 85.3 -> 78.8 (19).
     // Every gain measured had a workgroup take at least 0.43 of a tile's K blocks (at most three
@@ -350,12 +379,10 @@ int launch(int layout, KernelArgs& a, int64_t expected_rows, hipStream_t stream,
     if (layout == kDense && e.kind == kKindTiled && e.bm == 256 && a.splits == 1 && !noalloc && !jk) {
         const int64_t P = slots, T = a.units;
         const int64_t full = T / P, R = T % P;
-        const int64_t total = R * a.nkb, per = total / std::max<int64_t>(P, 1), extra = total % std::max<int64_t>(P, 1);
-        const int64_t saved = a.nkb - per - (extra > 0 ? 1 : 0);
-        const char* f = std::getenv("FP8GEMM_STREAMK");
-        const bool want = (f && *f) ? f[0] == '1' : saved >= stream_k_min_blocks(e.bn) && 3 * per >= a.nkb;
+        int64_t per = 0, extra = 0, blocks = 0;
+        const bool want = stream_k_plan(T, P, a.nkb, e.bn, &per, &extra, &blocks);
         const size_t need = (size_t)(2 * P) * e.bm * e.bn * sizeof(float);
-        if (want && R > 0 && per >= 1 && need <= workspace_partial_bytes(d->cus)) {
+        if (want && need <= workspace_partial_bytes(d->cus)) {
             // a stream with no workspace that is being captured keeps whole tiles (UNSUPPORTED
             // from workspace: nothing may be allocated during capture)
             Workspace* w = nullptr;

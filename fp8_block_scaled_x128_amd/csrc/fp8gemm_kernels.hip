@@ -56,9 +56,11 @@ const KernelEntry* kernel_table(int* count) {
         // dense, prefill: 256x256 tiles, 8 waves (4 along M x 2 along N), 2-slice ring (matrix
         // cores busy 0.26-0.47 of the time on the five M = 4096 shapes it runs)
         FP8GEMM_ENTRY(256, 256, 4, 2, 2, kDense),
-        // dense, prefill, narrower N tiles for widths whose 256-wide tile count leaves CUs idle
-        // (N = 2112: 224 tiles in one round)
+        // dense, prefill, narrower N tiles for widths whose 256-wide tiles leave CUs idle or
+        // split into many stream-K segments (chosen by the estimated time of the busiest
+        // workgroup: N = 1536 and 2112 take 256 x 192 with stream-K, N = 2112 at short K 256 x 160)
         FP8GEMM_ENTRY(256, 160, 4, 2, 2, kDense),
+        FP8GEMM_ENTRY(256, 192, 4, 2, 2, kDense),
         // dense, medium
         FP8GEMM_ENTRY(128, 128, 2, 2, 4, kDense),
         FP8GEMM_ENTRY(128, 256, 2, 4, 2, kDense),

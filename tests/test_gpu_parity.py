@@ -230,7 +230,7 @@ def streamk_cus(tiles, nkb, at_least):
     return P
 
 
-@pytest.mark.parametrize("bn", [256, 160])
+@pytest.mark.parametrize("bn", [256, 192, 160])
 @pytest.mark.parametrize("M,N,K,cus", [(1100, 700, 1280, 4), (1100, 700, 1280, 7), (600, 1030, 3840, 4),
                                        (777, 1500, 7168, 5), (300, 300, 1024, 2), (300, 256, 256, 3)])
 def test_stream_k_leftover_tiles(bn, M, N, K, cus):
@@ -264,7 +264,7 @@ def test_stream_k_leftover_tiles(bn, M, N, K, cus):
     say("stream-K", M, N, K, "cus", P, cfg, rep["bit_equal"])
 
 
-@pytest.mark.parametrize("bn", [256, 160])
+@pytest.mark.parametrize("bn", [256, 192, 160])
 @pytest.mark.parametrize("M,N,K,cus", [(1100, 1500, 1024, 4), (1024, 2048, 128, 3), (777, 1000, 512, 2),
                                        (513, 1001, 384, 2), (2048, 2048, 256, 5)])
 def test_several_whole_tiles_per_workgroup(bn, M, N, K, cus):
@@ -297,6 +297,23 @@ def test_several_whole_tiles_per_workgroup(bn, M, N, K, cus):
     assert np.array_equal(again, gpu_bits(D)), cfg
     assert_bit_exact(gpu_bits(D2), ref2, what=cfg)
     say("tiles per workgroup", M, N, K, "cus", cus, cfg, rep["bit_equal"])
+
+
+@pytest.mark.parametrize("M,N,K,tile,streamk", [(4096, 1536, 7168, "256x192", True),
+                                                  (4096, 2112, 7168, "256x192", True),
+                                                  (4096, 4096, 7168, "256x256", False),
+                                                  (4096, 2112, 1024, "256x160", False)])
+def test_prefill_tile_width_choice(M, N, K, tile, streamk):
+    """The N tile width of large dense launches: the least estimated time of the busiest
+    workgroup under the schedule the launch runs (whole tiles or stream-K), so 256 x 192 with
+    stream-K where 1536 or 2112 columns leave 256 x 256 tiles a partial round at long K, and the
+    narrower whole tiles at short K.  Parity with the oracle on the full output."""
+    d = W.dense(M, N, K, seed=M + N + K + 7)
+    D = run_dense(d)
+    cfg = fg.last_config()
+    assert ("tile=%s " % tile) in cfg and (("streamk_tiles=" in cfg) == streamk), cfg
+    rep = assert_close(gpu_bits(D), oracle.gemm_nt(d.A, d.sa, d.B, d.sb), what=cfg)
+    say("width", M, N, K, cfg, rep["bit_equal"])
 
 
 def test_stream_k_off_matches_oracle_too():
