@@ -229,6 +229,20 @@ def test_stream_k_graph_replays():
     assert "streamk_tiles=" in cfg, cfg
 
 
+def test_default_stream_k_graph_replays():
+    """A launch that takes stream-K by the library's own choice (2048 x 4096 x 7168 on the whole
+    device: 256-row tiles in less than one round), captured and replayed several times with eager
+    work between the replays: every replay gives the eager bits."""
+    M, N, K = 2048, 4096, 7168
+    d = W.dense(M, N, K, seed=506)
+    ops = (dev(d.A), dev_sa(d.sa), dev(d.B), dev(d.sb))
+    D = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    replay_matches_eager("default stream-K %dx%dx%d" % (M, N, K), lambda s: fg.gemm_nt(*ops, out=D, stream=s), [D])
+    cfg = fg.last_config()
+    assert "streamk_tiles=" in cfg, cfg
+
+
 def test_stream_k_capture_on_unprepared_stream_keeps_whole_tiles():
     """Stream-K needs the stream's workspace, which is never allocated during capture: on a
     stream with none, the captured launch keeps whole tiles (no error) and its graph computes the
