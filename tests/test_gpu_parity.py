@@ -316,6 +316,27 @@ def test_prefill_tile_width_choice(M, N, K, tile, streamk):
     say("width", M, N, K, cfg, rep["bit_equal"])
 
 
+@pytest.mark.parametrize("cus", [96, 200, 250])
+@pytest.mark.parametrize("M,N,K", [(2048, 1536, 4096), (1280, 2112, 3584)])
+def test_prefill_widths_under_a_cu_cap(M, N, K, cus):
+    """The width choice and the stream-K plan work from the capped CU count (caps that are not a
+    multiple of 8 also switch the XCD remap off): the launch stays within the cap and matches the
+    oracle, and a second call gives the same bits."""
+    d = W.dense(M, N, K, seed=M + N + K + cus)
+    ref = oracle.gemm_nt(d.A, d.sa, d.B, d.sb)
+    fg.set_num_cus(cus)
+    try:
+        D = run_dense(d)
+        cfg = fg.last_config()
+        again = gpu_bits(run_dense(d)).copy()
+    finally:
+        fg.set_num_cus(0)
+    assert "tile=256x" in cfg and int(cfg.split("grid=")[1].split()[0]) <= cus, cfg
+    rep = assert_close(gpu_bits(D), ref, what=cfg)
+    assert np.array_equal(again, gpu_bits(D)), cfg
+    say("capped widths", M, N, K, cus, cfg, rep["bit_equal"])
+
+
 def test_stream_k_off_matches_oracle_too():
     """The same leftover tiles as whole tiles (FP8GEMM_STREAMK=0): the schedule is a choice, both
     within tolerance of the oracle."""
